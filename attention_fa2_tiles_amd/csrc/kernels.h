@@ -1,0 +1,88 @@
+// Host-side launch interface between the C ABI (api.cpp) and the kernels.
+// Arguments here are already validated; every launcher returns hipError_t.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+enum Variant : int { PLAIN = 0, JVP = 1, PW = 2 };
+
+struct FwdArgs {
+  int dtype;               // fa_dtype code
+  int variant;             // PLAIN, JVP or PW
+  const void* q;           // q   (PW: q1)
+  const void* k;           // k   (PW: k1)
+  const void* v;
+  const void* q2;          // PW only
+  const void* k2;          // PW only
+  const void* tq;          // JVP only
+  const void* tk;          // JVP only
+  const void* tv;          // JVP only
+  void* o;
+  float* lse;
+  void* to;                // JVP only
+  int B, H, M, N, D;
+  int causal;
+  float sm_scale;          // resolved (> 0)
+  int w;                   // PW only
+};
+
+struct BwdArgs {
+  int dtype;
+  int variant;             // PLAIN or PW
+  const void* q;           // (PW: q1)
+  const void* k;           // (PW: k1)
+  const void* v;
+  const void* q2;          // PW only
+  const void* k2;          // PW only
+  const void* dout;
+  const float* lse;
+  const float* delta;
+  void* dq;                // (PW: dq1)
+  void* dk;                // (PW: dk1)
+  void* dv;
+  void* dq2;               // PW only
+  void* dk2;               // PW only
+  int B, H, M, N, D;
+  int causal;
+  float sm_scale;
+  int w;
+};
+
+struct MergeArgs {
+  int dtype;
+  const void* x;
+  const void* q;
+  const void* y0;
+  const float* l0;
+  void* y;                 // fwd
+  float* lse;              // fwd
+  const void* gy;          // bwd
+  const float* gl;         // bwd (may be null)
+  void* gx;                // bwd
+  float* gq;               // bwd
+  void* gy0;               // bwd
+  float* gl0;              // bwd
+  float* partial;          // bwd workspace
+  int rows, D;
+  float eps;
+};
+
+hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t s);
+hipError_t launch_attn_delta(int dtype, const void* o, const void* dout, float* delta,
+                             int64_t rows, int D, hipStream_t s);
+hipError_t launch_attn_dkdv(const BwdArgs& a, hipStream_t s);
+hipError_t launch_attn_dq(const BwdArgs& a, hipStream_t s);
+
+// fp32 (no MFMA) versions of the same operations.
+hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t s);
+hipError_t launch_attn_dkdv_f32(const BwdArgs& a, hipStream_t s);
+hipError_t launch_attn_dq_f32(const BwdArgs& a, hipStream_t s);
+
+hipError_t launch_merge_fwd(const MergeArgs& a, hipStream_t s);
+int merge_bwd_partial_rows(int rows, int D);   // number of gq partial vectors
+hipError_t launch_merge_bwd(const MergeArgs& a, hipStream_t s);
+
+}  // namespace fa

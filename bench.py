@@ -1,0 +1,406 @@
+#!/usr/bin/env python3
+"""Benchmark of the tiled-attention hot path on one MI355X.
+
+One step = fa_fwd + fa_bwd (Delta, dK/dV and dQ launches) on the causal bf16
+workload B=4, H=16, M=N=2048, D=128 with inputs already resident in HBM.
+``value`` is that step's throughput in TFLOP/s under the Triton tutorial's
+flop convention (forward 4*B*H*M*N*D, halved for causal; backward 2.5x the
+forward).  The same JSON line carries:
+
+* ``roofline`` for the dominant kernel of the step (its average launch time
+  from HIP events recorded on the launch stream over a timed loop), against
+  MI355X's dense bf16 MFMA peak of 2.5 PFLOP/s;
+* ``components``: per-kernel times of the step and the other workloads of
+  the hot path -- non-causal bf16 B1 H32 8192 D128, the fused JVP (fp16 B4 H16
+  1024 D64, causal and not), piecewise attention (fp16 B2 H16 4096 D64, w =
+  1024) and the residual merge (bf16 32768 x 4096, in HBM GB/s against 8 TB/s);
+* ``cpu_baseline``: the fp64 numpy oracle timed on the host on a bounded
+  sample of the same workload (a few whole heads).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+HEADLINE = "causal_bf16_b4h16_s2048_d128"
+METRIC = "attention fwd/bwd TFLOP/s + % bf16 MFMA peak; residual-merge HBM GB/s"
+
+
+def progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Timer:
+    """Average duration of repeated launches, from HIP events recorded on the
+    stream the library launches on (torch's current stream)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def avg_ms(self, fn, iters, warmup=2):
+        torch = self.torch
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(iters):
+            fn()
+        end.record()
+        end.synchronize()
+        return start.elapsed_time(end) / iters
+
+
+def attn_setup(torch, wl, names):
+    from attention_fa2_tiles_amd.inputs import attn_inputs
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_util import dev
+    t = attn_inputs(wl, names)
+    return t, {n: dev(t[n]) for n in names}
+
+
+def attn_buffers(torch, wl, d, bwd=True):
+    from attention_fa2_tiles_amd import lib
+    from gpu_util import empty, empty_f32
+    B, H, M, N, D = wl.B, wl.H, wl.M, wl.N, wl.D
+    buf = {"o": empty((B, H, M, D), wl.dtype), "lse": empty_f32((B, H, M)), "delta": empty_f32((B, H, M))}
+    if bwd:
+        for n in ("dq", "dk", "dv"):
+            buf[n] = empty((B, H, M if n == "dq" else N, D), wl.dtype)
+        nb = lib.fa_bwd_workspace_size(B, H, M, N, D, wl.dtype)
+        buf["ws"] = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        buf["ws_bytes"] = nb
+    return buf
+
+
+def attn_calls(wl, d, b):
+    from attention_fa2_tiles_amd import lib
+    B, H, M, N, D, c, s = wl.B, wl.H, wl.M, wl.N, wl.D, wl.causal, wl.sm_scale
+    q, k, v, do = d["q"], d["k"], d["v"], d["do"]
+    return {
+        "fwd": lambda: lib.fa_fwd(wl.dtype, q, k, v, b["o"], b["lse"], B, H, M, N, D, c, s),
+        "bwd": lambda: lib.fa_bwd(wl.dtype, q, k, v, b["o"], do, b["lse"], b["dq"], b["dk"], b["dv"],
+                                  b["ws"], b["ws_bytes"], B, H, M, N, D, c, s),
+        "delta": lambda: lib.fa_bwd_delta(wl.dtype, b["o"], do, b["delta"], B, H, M, D),
+        "dkdv": lambda: lib.fa_bwd_dkdv(wl.dtype, q, k, v, do, b["lse"], b["delta"], b["dk"], b["dv"],
+                                        B, H, M, N, D, c, s),
+        "dq": lambda: lib.fa_bwd_dq(wl.dtype, q, k, v, do, b["lse"], b["delta"], b["dq"], B, H, M, N, D, c, s),
+    }
+
+
+def kernel_work(wl):
+    """Algorithmic work per launch of each kernel of one step.
+
+    GEMM-equivalents of 2*M*N*D flops per head (halved when causal): the
+    forward does two (S, PV); the backward's five (S recomputed, dP, dV, dK,
+    dQ -- the 2.5x of the flop convention) are split as four for the dK/dV
+    kernel and one (dQ) for the dQ kernel, which also recomputes S and dP.
+    Delta is bandwidth-bound: it reads O and dO and writes one fp32 per row."""
+    g = 2.0 * wl.B * wl.H * wl.M * wl.N * wl.D * (0.5 if wl.causal else 1.0)
+    es = 4 if wl.dtype == 0 else 2
+    return {
+        "fwd": ("mfma", 2 * g),
+        "dkdv": ("mfma", 4 * g),
+        "dq": ("mfma", 1 * g),
+        "delta": ("hbm", 2.0 * wl.B * wl.H * wl.M * wl.D * es + 4.0 * wl.B * wl.H * wl.M),
+    }
+
+
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "fwd": ["attention_fa2_tiles_amd/csrc/attn_fwd.hip", "attention_fa2_tiles_amd/csrc/common.h"],
+    "dkdv": ["attention_fa2_tiles_amd/csrc/attn_bwd.hip", "attention_fa2_tiles_amd/csrc/common.h"],
+    "dq": ["attention_fa2_tiles_amd/csrc/attn_bwd.hip", "attention_fa2_tiles_amd/csrc/common.h"],
+    "delta": ["attention_fa2_tiles_amd/csrc/attn_bwd.hip"],
+}
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel's source changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get(HEADLINE, {}).get(kernel)
+    if not rec or rec.get("source_digest") != source_digest(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def bench_headline(torch, args, timer):
+    from attention_fa2_tiles_amd.inputs import WORKLOADS
+    wl = WORKLOADS[HEADLINE]
+    progress(f"inputs for {wl.name}")
+    _, d = attn_setup(torch, wl, ("q", "k", "v", "do"))
+    b = attn_buffers(torch, wl, d)
+    calls = attn_calls(wl, d, b)
+
+    def step():
+        calls["fwd"]()
+        calls["bwd"]()
+
+    progress(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    progress(f"timing {args.steps} steps")
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / args.steps
+    flops = wl.fwd_flops() + wl.bwd_flops()
+    tflops = flops / (ms_step * 1e-3) / 1e12
+
+    progress("per-kernel timing")
+    iters = max(args.steps, 10)
+    per = {k: timer.avg_ms(calls[k], iters) for k in ("fwd", "delta", "dkdv", "dq")}
+    work = kernel_work(wl)
+    kernels = {}
+    for k, ms in per.items():
+        bound, amount = work[k]
+        if bound == "mfma":
+            ach = amount / (ms * 1e-3) / 1e12
+            kernels[k] = {"ms": round(ms, 5), "TFLOP/s": round(ach, 2),
+                          "frac_bf16_peak": round(ach / PEAK_BF16_TFLOPS, 4)}
+        else:
+            ach = amount / (ms * 1e-3) / 1e9
+            kernels[k] = {"ms": round(ms, 5), "GB/s": round(ach, 1), "frac_hbm_peak": round(ach / PEAK_HBM_GBPS, 4)}
+    dominant = max(("fwd", "dkdv", "dq"), key=lambda k: per[k])
+    bound, amount = work[dominant]
+    achieved = amount / (per[dominant] * 1e-3) / 1e12
+    roofline = {
+        "kernel": dominant,
+        "bound": "mfma",
+        "achieved": round(achieved, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": measured_traffic(dominant),
+        "avg_launch_ms": round(per[dominant], 5),
+        "algorithmic_flops_per_launch": amount,
+    }
+    fwd_tf = wl.fwd_flops() / (per["fwd"] * 1e-3) / 1e12
+    bwd_ms = timer.avg_ms(calls["bwd"], iters)
+    bwd_tf = wl.bwd_flops() / (bwd_ms * 1e-3) / 1e12
+    summary = {
+        "fwd_TFLOP/s": round(fwd_tf, 2), "fwd_frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
+        "bwd_TFLOP/s": round(bwd_tf, 2), "bwd_frac_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+        "bwd_ms": round(bwd_ms, 5), "kernels": kernels,
+    }
+    return wl, ms_step, tflops, wall, roofline, summary
+
+
+def bench_attention_other(torch, timer, name, iters):
+    from attention_fa2_tiles_amd.inputs import WORKLOADS
+    wl = WORKLOADS[name]
+    progress(f"component {name}")
+    _, d = attn_setup(torch, wl, ("q", "k", "v", "do"))
+    b = attn_buffers(torch, wl, d)
+    calls = attn_calls(wl, d, b)
+    calls["fwd"]()
+    f_ms = timer.avg_ms(calls["fwd"], iters)
+    b_ms = timer.avg_ms(calls["bwd"], iters)
+    f_tf = wl.fwd_flops() / (f_ms * 1e-3) / 1e12
+    b_tf = wl.bwd_flops() / (b_ms * 1e-3) / 1e12
+    del d, b
+    torch.cuda.empty_cache()
+    return {"fwd_ms": round(f_ms, 4), "fwd_TFLOP/s": round(f_tf, 2), "fwd_frac_peak": round(f_tf / PEAK_BF16_TFLOPS, 4),
+            "bwd_ms": round(b_ms, 4), "bwd_TFLOP/s": round(b_tf, 2), "bwd_frac_peak": round(b_tf / PEAK_BF16_TFLOPS, 4)}
+
+
+def bench_jvp(torch, timer, name, iters):
+    from attention_fa2_tiles_amd import lib
+    from attention_fa2_tiles_amd.inputs import WORKLOADS
+    from gpu_util import empty, empty_f32
+    wl = WORKLOADS[name]
+    progress(f"component {name}")
+    names = ("q", "k", "v", "tq", "tk", "tv")
+    _, d = attn_setup(torch, wl, names)
+    B, H, M, N, D = wl.B, wl.H, wl.M, wl.N, wl.D
+    o, to, lse = empty((B, H, M, D), wl.dtype), empty((B, H, M, D), wl.dtype), empty_f32((B, H, M))
+    ms = timer.avg_ms(lambda: lib.fa_fwd_jvp(wl.dtype, *[d[n] for n in names], o, lse, to,
+                                             B, H, M, N, D, wl.causal, wl.sm_scale), iters)
+    tf = 3 * wl.fwd_flops() / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "TFLOP/s": round(tf, 2), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "counted_flops": "3 x forward"}
+
+
+def bench_pw(torch, timer, iters):
+    from attention_fa2_tiles_amd import lib
+    from attention_fa2_tiles_amd.inputs import PIECEWISE_W, WORKLOADS
+    from gpu_util import empty, empty_f32
+    wl = WORKLOADS["piecewise_f16_b2h16_s4096_d64_w1024"]
+    progress(f"component {wl.name}")
+    names = ("q1", "k1", "q2", "k2", "v", "do")
+    _, d = attn_setup(torch, wl, names)
+    B, H, M, N, D = wl.B, wl.H, wl.M, wl.N, wl.D
+    o, lse = empty((B, H, M, D), wl.dtype), empty_f32((B, H, M))
+    g = [empty((B, H, M, D), wl.dtype) for _ in range(5)]
+    nb = lib.pw_bwd_workspace_size(B, H, M, N, D, wl.dtype)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    args = (B, H, M, N, D, wl.causal, wl.sm_scale, PIECEWISE_W)
+    fwd = lambda: lib.pw_fwd(wl.dtype, *[d[n] for n in names[:5]], o, lse, *args)
+    bwd = lambda: lib.pw_bwd(wl.dtype, *[d[n] for n in names[:5]], o, d["do"], lse, *g, ws, nb, *args)
+    fwd()
+    f_ms = timer.avg_ms(fwd, iters)
+    b_ms = timer.avg_ms(bwd, iters)
+    f_tf = wl.fwd_flops() / (f_ms * 1e-3) / 1e12
+    b_tf = wl.bwd_flops() / (b_ms * 1e-3) / 1e12
+    return {"fwd_ms": round(f_ms, 4), "fwd_TFLOP/s": round(f_tf, 2), "bwd_ms": round(b_ms, 4),
+            "bwd_TFLOP/s": round(b_tf, 2), "counted_flops": "one QK^T per score"}
+
+
+def bench_merge(torch, timer, iters):
+    from attention_fa2_tiles_amd import lib
+    from attention_fa2_tiles_amd.inputs import MERGE_WORKLOAD, merge_inputs
+    from gpu_util import dev, empty, empty_f32
+    wl = MERGE_WORKLOAD
+    progress(f"component {wl.name}")
+    t = merge_inputs(wl)
+    x, y0, q, l0, gy, gl = (dev(t[n]) for n in ("x", "y0", "q", "l0", "gy", "gl"))
+    del t
+    R, D = wl.rows, wl.D
+    y, lse = empty((R, D), wl.dtype), empty_f32((R,))
+    gx, gy0, gq, gl0 = empty((R, D), wl.dtype), empty((R, D), wl.dtype), empty_f32((D,)), empty_f32((R,))
+    nb = lib.resmerge_bwd_workspace_size(R, D)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    fwd = lambda: lib.resmerge_fwd(wl.dtype, x, q, y0, l0, y, lse, R, D, wl.eps)
+    bwd = lambda: lib.resmerge_bwd(wl.dtype, x, q, y0, l0, gy, gl, gx, gq, gy0, gl0, ws, nb, R, D, wl.eps)
+    f_ms = timer.avg_ms(fwd, iters)
+    b_ms = timer.avg_ms(bwd, iters)
+    f_gb = wl.fwd_bytes() / (f_ms * 1e-3) / 1e9
+    b_gb = wl.bwd_bytes() / (b_ms * 1e-3) / 1e9
+    return {"fwd_ms": round(f_ms, 4), "fwd_GB/s": round(f_gb, 1), "fwd_frac_hbm": round(f_gb / PEAK_HBM_GBPS, 4),
+            "bwd_ms": round(b_ms, 4), "bwd_GB/s": round(b_gb, 1), "bwd_frac_hbm": round(b_gb / PEAK_HBM_GBPS, 4),
+            "fwd_bytes": wl.fwd_bytes(), "bwd_bytes": wl.bwd_bytes()}
+
+
+def cpu_baseline(target_s):
+    """The fp64 oracle, as it stands, on whole heads of the headline workload."""
+    import numpy as np
+    import oracle
+    from attention_fa2_tiles_amd.inputs import WORKLOADS, AttnWorkload, attn_inputs
+    wl = WORKLOADS[HEADLINE]
+    progress("cpu baseline (fp64 oracle)")
+    one = AttnWorkload("sample", wl.dtype, 1, 1, wl.M, wl.N, wl.D, wl.causal, wl.seed)
+    per_head = one.fwd_flops() + one.bwd_flops()
+
+    def run(nheads):
+        w = AttnWorkload("sample", wl.dtype, 1, nheads, wl.M, wl.N, wl.D, wl.causal, wl.seed)
+        t = attn_inputs(w)
+        f = {n: t[n].f64 for n in ("q", "k", "v", "do")}
+        t0 = time.perf_counter()
+        oracle.attn_fwd(f["q"], f["k"], f["v"], wl.causal, wl.scale())
+        oracle.attn_bwd(f["q"], f["k"], f["v"], f["do"], wl.causal, wl.scale())
+        return time.perf_counter() - t0
+
+    t1 = run(1)
+    n = int(max(1, min(wl.B * wl.H, round(target_s / max(t1, 1e-3)))))
+    tn = run(n) if n > 1 else t1
+    threads = os.cpu_count()
+    try:
+        from threadpoolctl import threadpool_info
+        info = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if info:
+            threads = max(p.get("num_threads", 1) for p in info)
+    except Exception:
+        pass
+    del np
+    return {"value": round(n * per_head / tn / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"fa_fwd + fa_bwd fp64 numpy oracle on {n} of {wl.B * wl.H} heads of {wl.name} "
+                      f"(B=1, H={n}); {tn:.1f} s wall",
+            "seconds": round(tn, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-components", action="store_true", help="time only the headline step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(attention heads and merge rows would shard across GPUs with no exchange; "
+              "see the design notes).", file=sys.stderr)
+        sys.exit(2)
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: WORLD_SIZE > 1 is not supported (single-GPU build)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from attention_fa2_tiles_amd import lib
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    lib.load()
+    torch.cuda.set_device(0)
+    timer = Timer(torch)
+
+    wl, ms_step, tflops, wall, roofline, summary = bench_headline(torch, args, timer)
+    components = {HEADLINE: summary}
+    if not args.no_components:
+        iters = max(5, min(args.steps, 20))
+        components["noncausal_bf16_b1h32_s8192_d128"] = bench_attention_other(
+            torch, timer, "noncausal_bf16_b1h32_s8192_d128", max(3, iters // 2))
+        components["jvp_f16_b4h16_s1024_d64_causal"] = bench_jvp(torch, timer, "jvp_f16_b4h16_s1024_d64_causal", iters)
+        components["jvp_f16_b4h16_s1024_d64"] = bench_jvp(torch, timer, "jvp_f16_b4h16_s1024_d64", iters)
+        components["piecewise_f16_b2h16_s4096_d64_w1024"] = bench_pw(torch, timer, iters)
+        components["merge_bf16_rows32768_d4096"] = bench_merge(torch, timer, iters)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "M": wl.M, "N": wl.N, "D": wl.D,
+                   "causal": wl.causal, "sm_scale": float(wl.scale()), "step": "fa_fwd + fa_bwd",
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "components": components,
+        "timed_wall_s": round(wall, 4),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

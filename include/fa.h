@@ -1,0 +1,186 @@
+/*
+ * fa.h -- C ABI of libfa2tiles.so: FlashAttention-2-style tiled attention,
+ * its backward, its fused forward-mode JVP, piecewise attention, and the
+ * block-residual online-softmax merge, as hand-written HIP kernels for
+ * AMD MI355X (gfx950).
+ *
+ * Common conventions (every entry point)
+ * --------------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *   never allocates, frees or keeps a pointer after a call returns.  Outputs
+ *   are overwritten, never accumulated into.
+ * - Attention tensors are contiguous [B, H, S, D] (D fastest): q-like tensors
+ *   have S = M rows (queries), k-like tensors S = N rows (keys).  LSE and the
+ *   backward's Delta are contiguous fp32 [B, H, M].
+ * - dtype selects the element type of every attention tensor (and of the
+ *   merge's D-length row tensors): FA_F32, FA_F16 or FA_BF16.  Matrix
+ *   products of fp16/bf16 inputs run on MFMA with fp32 accumulation; the
+ *   probabilities P (and dS) are rounded to the input dtype before the
+ *   products that consume them, as the FlagAttention kernels do.  FA_F32
+ *   inputs are computed entirely in fp32 arithmetic.
+ * - LSE is the natural-log log-sum-exp of the scaled scores of each query
+ *   row (FlagAttention piecewise.py stores it this way; the Triton tutorial
+ *   stores log2 -- same information, different unit).  A query row with no
+ *   visible key gets O = 0 and LSE = -inf.
+ * - causal is 0 or 1.  Causal masking is aligned bottom-right: query i sees
+ *   key j iff j <= i + (N - M) (the P_SEQ offset of FlagAttention).
+ * - sm_scale == 0 selects the default 1/sqrt(D) (the pages' "None"); any
+ *   other value must be finite and > 0.
+ * - stream is a hipStream_t passed as void*; NULL is the default stream.
+ *   Launches are asynchronous; the caller synchronises.
+ * - Every argument is validated on the host BEFORE any HIP call; if a check
+ *   fails nothing is launched and the matching negative fa_status is
+ *   returned.  A failed launch returns FA_ERR_HIP.  No C++ exception crosses
+ *   this boundary.
+ * - Pointers must be 16-byte aligned (FA_ERR_ALIGN).
+ * - Supported attention shapes: B, H >= 1; M, N multiples of 64; D in
+ *   {64, 128} (FA_ERR_UNSUPPORTED otherwise).
+ *
+ * Citations name the page and the function or passage whose computation the
+ * entry point performs:
+ *   [tutorial]  Birch-san's gist _06_fused_attention_blockptr_jvp.py (Triton
+ *               fused-attention tutorial with JVP) and its comment thread;
+ *   [piecewise] FlagAttention src/flag_attn/piecewise.py;
+ *   [merge]     flash_attn_res 0.1.11, slop/backward_phase_2.txt.
+ */
+#ifndef FA2TILES_FA_H
+#define FA2TILES_FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,        /* a required pointer is NULL                    */
+  FA_ERR_SHAPE = -2,       /* a size is <= 0 or the sizes overflow         */
+  FA_ERR_DTYPE = -3,       /* unknown dtype code                            */
+  FA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned             */
+  FA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required    */
+  FA_ERR_UNSUPPORTED = -6, /* valid but unsupported (D, M/N granularity...)  */
+  FA_ERR_HIP = -7          /* a HIP launch or runtime call failed           */
+} fa_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* fa_strerror(int status);
+
+/* Library ABI version (major*100 + minor). */
+int fa_version(void);
+
+/*
+ * Attention forward [tutorial: _attn_fwd / _attn_fwd_inner; piecewise:
+ * _fwd_kernel without the piecewise score selection].
+ *   O   = softmax(sm_scale * Q K^T  (causally masked))  V      [B,H,M,D]
+ *   lse = log sum_j exp(sm_scale * q_i . k_j)  over visible j  [B,H,M] fp32
+ * One kernel; online softmax over K/V blocks; causal blocks beyond the
+ * diagonal are skipped.
+ */
+int fa_fwd(int dtype, const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int M, int N, int D, int causal, float sm_scale, void* stream);
+
+/*
+ * Attention backward [tutorial: _attn_bwd_preprocess, _attn_bwd_dkdv,
+ * _attn_bwd_dq, with the non-causal block range from the comment thread;
+ * piecewise: _bwd_preprocess, _bwd_kv_kernel, _bwd_q_kernel].
+ * Gradients of <dout, O> with O = fa_fwd(q, k, v); o and lse must be the
+ * outputs of fa_fwd on the same inputs.  Three launches on `stream`:
+ *   Delta_i = sum_d o_id dout_id                    (fa_bwd_delta)
+ *   dK, dV  with K/V resident, looping over queries  (fa_bwd_dkdv)
+ *   dQ      with Q resident, looping over keys       (fa_bwd_dq)
+ * workspace: device buffer of at least fa_bwd_workspace_size() bytes (it
+ * holds Delta); it is scratch, its content on return is unspecified.
+ */
+size_t fa_bwd_workspace_size(int B, int H, int M, int N, int D, int dtype);
+int fa_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
+           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+           void* workspace, size_t workspace_bytes,
+           int B, int H, int M, int N, int D, int causal, float sm_scale, void* stream);
+
+/* The three steps of fa_bwd, exposed separately so each can be timed. */
+/* delta [B,H,M] fp32 <- rowsum(o * dout)  [tutorial: _attn_bwd_preprocess] */
+int fa_bwd_delta(int dtype, const void* o, const void* dout, float* delta,
+                 int B, int H, int M, int D, void* stream);
+/* dk, dv [B,H,N,D] from q, k, v, dout, lse and delta  [tutorial: _attn_bwd_dkdv] */
+int fa_bwd_dkdv(int dtype, const void* q, const void* k, const void* v, const void* dout,
+                const float* lse, const float* delta, void* dk, void* dv,
+                int B, int H, int M, int N, int D, int causal, float sm_scale, void* stream);
+/* dq [B,H,M,D] from q, k, v, dout, lse and delta  [tutorial: _attn_bwd_dq] */
+int fa_bwd_dq(int dtype, const void* q, const void* k, const void* v, const void* dout,
+              const float* lse, const float* delta, void* dq,
+              int B, int H, int M, int N, int D, int causal, float sm_scale, void* stream);
+
+/*
+ * Fused forward-mode JVP [tutorial: the ENABLE_JVP path of _attn_fwd_inner
+ * and the tangent epilogue of _attn_fwd; method of Lu & Song, arXiv
+ * 2410.11081].  Outputs o and lse exactly as fa_fwd, plus the tangent
+ *   to = d/dt O(q + t*tq, k + t*tk, v + t*tv) at t = 0          [B,H,M,D]
+ * computed in the same pass: with Sdot = sm_scale (tq K^T + Q tk^T),
+ *   to = (P*Sdot) V - rowsum(P*Sdot) O + P tv.
+ * tq is q-like, tk and tv are k-like.
+ */
+int fa_fwd_jvp(int dtype, const void* q, const void* k, const void* v,
+               const void* tq, const void* tk, const void* tv,
+               void* o, float* lse, void* to,
+               int B, int H, int M, int N, int D, int causal, float sm_scale, void* stream);
+
+/*
+ * Piecewise attention forward [piecewise: attention() and _fwd_kernel].
+ * Score of (i, j): sm_scale * q1_i . k1_j if |i + (N - M) - j| <= w, else
+ * sm_scale * q2_i . k2_j; then softmax, P V and lse as fa_fwd.  w may be
+ * negative (every pair then uses q2, k2).  Blocks entirely inside or outside
+ * the band compute one product; only blocks crossing it compute both.
+ */
+int pw_fwd(int dtype, const void* q1, const void* k1, const void* q2, const void* k2,
+           const void* v, void* o, float* lse,
+           int B, int H, int M, int N, int D, int causal, float sm_scale, int w, void* stream);
+
+/*
+ * Piecewise attention backward [piecewise: _bwd_preprocess, _bwd_kv_kernel,
+ * _bwd_q_kernel].  dS is split by the same distance rule: the near part
+ * yields dq1, dk1, the far part dq2, dk2; dv = P^T dout.  o and lse must come
+ * from pw_fwd on the same inputs.  workspace as for fa_bwd
+ * (pw_bwd_workspace_size() bytes, holds Delta).
+ */
+size_t pw_bwd_workspace_size(int B, int H, int M, int N, int D, int dtype);
+int pw_bwd(int dtype, const void* q1, const void* k1, const void* q2, const void* k2,
+           const void* v, const void* o, const void* dout, const float* lse,
+           void* dq1, void* dk1, void* dq2, void* dk2, void* dv,
+           void* workspace, size_t workspace_bytes,
+           int B, int H, int M, int N, int D, int causal, float sm_scale, int w, void* stream);
+
+/*
+ * Block-residual two-way online-softmax merge, forward [merge:
+ * reference_forward].  Per row r of x, y0 ([rows, D], dtype):
+ *   rho = (mean(x^2) + eps)^-1/2;  l1 = rho * (x . q);  m = max(l0, l1)
+ *   a = e^(l0-m) / Z, b = e^(l1-m) / Z, Z = e^(l0-m) + e^(l1-m)
+ *   y = a*y0 + b*x   ([rows, D], dtype);   lse = m + log Z   ([rows] fp32)
+ * q is the pseudo-query ([D], dtype); l0 is [rows] fp32 (may hold -inf).
+ * D must be a multiple of 8; eps must be finite and >= 0.
+ */
+int resmerge_fwd(int dtype, const void* x, const void* q, const void* y0, const float* l0,
+                 void* y, float* lse, int rows, int D, float eps, void* stream);
+
+/*
+ * Merge backward [merge: the phase-2 merge backward kernel and its
+ * launcher].  VJP of resmerge_fwd for <gy, y> + <gl, lse>; gl == NULL means
+ * zeros.  Outputs (all overwritten): gx, gy0 [rows, D] dtype; gl0 [rows]
+ * fp32; gq [D] fp32 = sum over rows, reduced in a fixed order (no float
+ * atomics, so repeated calls are bitwise identical).  workspace: at least
+ * resmerge_bwd_workspace_size(rows, D) bytes of device scratch (per-block
+ * partial sums of gq).
+ */
+size_t resmerge_bwd_workspace_size(int rows, int D);
+int resmerge_bwd(int dtype, const void* x, const void* q, const void* y0, const float* l0,
+                 const void* gy, const float* gl, void* gx, float* gq, void* gy0, float* gl0,
+                 void* workspace, size_t workspace_bytes, int rows, int D, float eps,
+                 void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA2TILES_FA_H */

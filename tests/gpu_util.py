@@ -1,0 +1,66 @@
+"""Helpers shared by the GPU tests: device buffers and host round trips.
+
+Inputs come from attention_fa2_tiles_amd.inputs (seeded, rounded to the
+storage dtype); the same stored values, upcast to float64, go to the oracle.
+All device work goes through the C ABI (attention_fa2_tiles_amd.lib); torch is
+only used to allocate device memory and copy it to and from the host.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+
+from attention_fa2_tiles_amd import lib
+from attention_fa2_tiles_amd.inputs import BF16, F16, F32
+
+
+def need_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    lib.load()  # raises if the HIP library is missing: there is no fallback
+    return torch
+
+
+def torch_dtype(dtype):
+    import torch
+    return {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}[dtype]
+
+
+def dev(t):
+    """inputs.Tensor -> device tensor holding exactly the stored values."""
+    import torch
+    s = np.ascontiguousarray(t.storage)
+    if t.dtype == BF16:
+        return torch.from_numpy(s.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(s).cuda()
+
+
+def empty(shape, dtype):
+    import torch
+    return torch.empty(shape, dtype=torch_dtype(dtype), device="cuda")
+
+
+def empty_f32(shape):
+    import torch
+    return torch.empty(shape, dtype=torch.float32, device="cuda")
+
+
+def filled(shape, dtype, value=float("nan")):
+    """Output buffers start as NaN so that an element the kernel never
+    writes cannot pass a comparison by accident."""
+    t = empty(shape, dtype)
+    t.fill_(value)
+    return t
+
+
+def host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()

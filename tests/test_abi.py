@@ -1,0 +1,143 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point that
+include/fa.h declares, and rejects bad arguments on the host before any HIP
+call (no GPU is needed; every case below fails validation, so nothing is
+launched).  Requires the library to be built (``__graft_entry__.build()``)."""
+
+import os
+import re
+
+import pytest
+
+from attention_fa2_tiles_amd import lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+if not os.path.exists(lib.LIB_PATH):
+    pytest.skip("libfa2tiles.so not built; run python -m attention_fa2_tiles_amd.build", allow_module_level=True)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_\w+|pw_\w+|resmerge_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = lib.load()
+    names = declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in fa.h but not exported"
+    # the binding covers exactly the declared surface
+    assert sorted(lib.EXPORTS) == names
+
+
+def test_version_and_strerror():
+    assert lib.fa_version() >= 100
+    for code, name in lib.STATUS.items():
+        assert lib.fa_strerror(code).startswith(name)
+    assert "unknown" in lib.fa_strerror(12345)
+
+
+def test_workspace_sizes():
+    assert lib.fa_bwd_workspace_size(2, 3, 128, 256, 64, 2) == 2 * 3 * 128 * 4
+    assert lib.pw_bwd_workspace_size(1, 1, 64, 64, 64, 1) == 64 * 4
+    assert lib.fa_bwd_workspace_size(0, 3, 128, 256, 64, 2) == 0
+    n = lib.resmerge_bwd_workspace_size(32768, 4096)
+    assert n > 0 and n % (4096 * 4) == 0
+    assert lib.resmerge_bwd_workspace_size(-1, 8) == 0
+
+
+# Fake, 16-byte-aligned device addresses: never dereferenced, because each
+# case below is rejected by host-side validation first.
+A = 0x100000
+P = [A + 0x1000 * i for i in range(20)]
+
+
+def status(fn, *args):
+    with pytest.raises(lib.FAError) as e:
+        fn(*args)
+    return e.value.status
+
+
+def fwd_args(**kw):
+    a = dict(dtype=2, q=P[0], k=P[1], v=P[2], o=P[3], lse=P[4], B=1, H=2, M=128, N=128, D=64,
+             causal=1, sm_scale=0.0, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), -1),
+    (dict(lse=None), -1),
+    (dict(dtype=7), -3),
+    (dict(v=P[2] + 8), -4),
+    (dict(lse=P[4] + 2), -4),
+    (dict(B=0), -2),
+    (dict(M=-64), -2),
+    (dict(D=96), -6),
+    (dict(D=32), -6),
+    (dict(M=100), -6),
+    (dict(N=130), -6),
+    (dict(causal=2), -6),
+    (dict(sm_scale=-1.0), -6),
+    (dict(sm_scale=float("nan")), -6),
+    (dict(sm_scale=float("inf")), -6),
+    (dict(B=1 << 20, H=1 << 20), -2),
+])
+def test_fa_fwd_rejects(kw, code):
+    assert status(lib.fa_fwd, *fwd_args(**kw)) == code
+
+
+def test_bwd_rejects_small_workspace():
+    args = [2, P[0], P[1], P[2], P[3], P[5], P[4], P[6], P[7], P[8], P[9], 2 * 128 * 4 - 4,
+            1, 2, 128, 128, 64, 1, 0.0, None]
+    assert status(lib.fa_bwd, *args) == -5
+    args[10] = None
+    args[11] = 1 << 20
+    assert status(lib.fa_bwd, *args) == -5
+    args = [2, P[0], P[1], P[2], P[3], P[5], P[4], None, P[7], P[8], P[9], 1 << 20,
+            1, 2, 128, 128, 64, 1, 0.0, None]
+    assert status(lib.fa_bwd, *args) == -1
+
+
+def test_step_entry_points_reject():
+    assert status(lib.fa_bwd_delta, 1, P[0], P[1], None, 1, 1, 64, 64) == -1
+    assert status(lib.fa_bwd_delta, 1, P[0], P[1], P[2], 1, 1, 64, 48) == -6
+    assert status(lib.fa_bwd_dkdv, 2, P[0], P[1], P[2], P[3], P[4], P[5], P[6], None,
+                  1, 1, 64, 64, 64, 0, 0.0) == -1
+    assert status(lib.fa_bwd_dq, 2, P[0], P[1], P[2], P[3], P[4], P[5], P[6],
+                  1, 1, 64, 64, 64, 3, 0.0) == -6
+
+
+def test_jvp_and_pw_reject():
+    assert status(lib.fa_fwd_jvp, 1, P[0], P[1], P[2], None, P[4], P[5], P[6], P[7], P[8],
+                  1, 1, 64, 64, 64, 0, 0.0) == -1
+    assert status(lib.pw_fwd, 1, P[0], P[1], P[2], P[3], P[4], P[5], P[6],
+                  1, 1, 64, 64, 256, 1, 0.0, 10) == -6
+    assert status(lib.pw_bwd, 1, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], P[9], P[10],
+                  P[11], P[12], P[13], 0, 1, 1, 64, 64, 64, 1, 0.0, 10) == -5
+
+
+def test_merge_rejects():
+    f = lib.resmerge_fwd
+    ok = [2, P[0], P[1], P[2], P[3], P[4], P[5], 8, 64]
+    assert status(f, *ok[:7], 8, 60, 1e-6) == -6          # D not a multiple of 8
+    assert status(f, *ok[:7], 0, 64, 1e-6) == -2
+    assert status(f, *ok, -1.0) == -6
+    assert status(f, *ok, float("nan")) == -6
+    assert status(f, 9, *ok[1:], 1e-6) == -3
+    assert status(f, 2, P[0] + 4, *ok[2:], 1e-6) == -4
+    b = lib.resmerge_bwd
+    need = lib.resmerge_bwd_workspace_size(8, 64)
+    args = [2, P[0], P[1], P[2], P[3], P[4], None, P[6], P[7], P[8], P[9], P[10], need - 4, 8, 64, 1e-6]
+    assert status(b, *args) == -5
+    args[12] = need
+    args[7] = None  # gx
+    assert status(b, *args) == -1
+
+
+def test_load_missing_library_raises():
+    with pytest.raises(lib.FAError):
+        lib.load("/nonexistent/libfa2tiles.so")

@@ -1,0 +1,147 @@
+"""GPU parity: fa_fwd / fa_bwd (and its three steps) against the fp64 oracle.
+
+Small shapes are compared element by element on every output; they span
+several tiles in both directions, a half-filled last query block, M != N
+(bottom-right causal alignment, including query rows that see no key), both
+head dims and all three dtypes.  The full-size workloads (causal bf16
+B4 H16 2048 D128 and non-causal bf16 B1 H32 8192 D128) run in the same launch
+configuration the benchmark times and are compared on whole sampled heads.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from attention_fa2_tiles_amd import lib
+from attention_fa2_tiles_amd.inputs import BF16, F16, F32, WORKLOADS, AttnWorkload, attn_inputs
+from gpu_util import dev, empty_f32, filled, host, log, need_gpu
+from tolerance import check_grad, check_lse, check_output
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fwd_bwd(wl, t, with_bwd=True, steps=False):
+    torch = need_gpu()
+    q, k, v, do = (dev(t[n]) for n in ("q", "k", "v", "do"))
+    B, H, M, N, D = wl.B, wl.H, wl.M, wl.N, wl.D
+    o = filled((B, H, M, D), wl.dtype)
+    lse = empty_f32((B, H, M))
+    lib.fa_fwd(wl.dtype, q, k, v, o, lse, B, H, M, N, D, wl.causal, wl.sm_scale)
+    out = {"o": o, "lse": lse}
+    if with_bwd:
+        dq, dk, dv = (filled(x.shape, wl.dtype) for x in (q, k, v))
+        if steps:
+            delta = empty_f32((B, H, M))
+            lib.fa_bwd_delta(wl.dtype, o, do, delta, B, H, M, D)
+            lib.fa_bwd_dkdv(wl.dtype, q, k, v, do, lse, delta, dk, dv, B, H, M, N, D, wl.causal, wl.sm_scale)
+            lib.fa_bwd_dq(wl.dtype, q, k, v, do, lse, delta, dq, B, H, M, N, D, wl.causal, wl.sm_scale)
+        else:
+            ws_bytes = lib.fa_bwd_workspace_size(B, H, M, N, D, wl.dtype)
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+            lib.fa_bwd(wl.dtype, q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, H, M, N, D,
+                       wl.causal, wl.sm_scale)
+        out.update(dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    return {kk: host(vv) for kk, vv in out.items()}
+
+
+def compare(wl, t, got, heads=None, with_bwd=True):
+    sel = (slice(None), slice(None)) if heads is None else None
+    c = wl.scale()
+    pairs = [(b, h) for b in range(wl.B) for h in range(wl.H)] if heads is None else heads
+    for (b, h) in pairs:
+        f = {n: t[n].f64[b:b + 1, h:h + 1] for n in ("q", "k", "v", "do")}
+        o, lse = oracle.attn_fwd(f["q"], f["k"], f["v"], wl.causal, c)
+        tag = f"{wl.name}[b={b},h={h}]"
+        check_output(f"{tag}.o", got["o"][b, h], o[0, 0], wl.dtype)
+        check_lse(f"{tag}.lse", got["lse"][b, h], lse[0, 0], wl.dtype)
+        if with_bwd:
+            dq, dk, dv = oracle.attn_bwd(f["q"], f["k"], f["v"], f["do"], wl.causal, c)
+            check_grad(f"{tag}.dq", got["dq"][b, h], dq[0, 0], wl.dtype)
+            check_grad(f"{tag}.dk", got["dk"][b, h], dk[0, 0], wl.dtype)
+            check_grad(f"{tag}.dv", got["dv"][b, h], dv[0, 0], wl.dtype)
+    del sel
+
+
+SMALL = [
+    # dtype, B, H, M, N, D, causal
+    (BF16, 2, 3, 192, 192, 128, True),
+    (BF16, 2, 3, 192, 192, 128, False),
+    (F16, 1, 2, 256, 256, 64, True),
+    (F16, 1, 2, 256, 256, 64, False),
+    (BF16, 1, 2, 64, 64, 64, True),
+    (BF16, 1, 2, 128, 320, 128, True),    # M < N: rows see a longer prefix
+    (F16, 1, 2, 320, 128, 64, True),      # M > N: the first 192 rows see no key
+    (F16, 1, 2, 128, 320, 128, False),
+    (F32, 1, 2, 128, 128, 64, False),
+    (F32, 1, 2, 192, 128, 128, True),
+    (F32, 1, 1, 64, 192, 64, True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "-".join(map(str, c)))
+def test_small_parity(case):
+    dtype, B, H, M, N, D, causal = case
+    wl = AttnWorkload("small", dtype, B, H, M, N, D, causal, seed=11 + M + N + D)
+    log(f"fa small parity {case}")
+    t = attn_inputs(wl)
+    got = run_fwd_bwd(wl, t)
+    compare(wl, t, got)
+
+
+def test_steps_equal_fused_bwd():
+    """fa_bwd == fa_bwd_delta + fa_bwd_dkdv + fa_bwd_dq, bit for bit."""
+    wl = AttnWorkload("steps", BF16, 1, 2, 256, 256, 128, True, seed=5)
+    t = attn_inputs(wl)
+    a = run_fwd_bwd(wl, t, steps=False)
+    b = run_fwd_bwd(wl, t, steps=True)
+    for n in ("dq", "dk", "dv"):
+        assert np.array_equal(a[n], b[n]), n
+
+
+def test_deterministic():
+    wl = AttnWorkload("det", F16, 1, 4, 256, 256, 64, False, seed=6)
+    t = attn_inputs(wl)
+    a = run_fwd_bwd(wl, t)
+    b = run_fwd_bwd(wl, t)
+    for n in a:
+        assert np.array_equal(a[n], b[n]), n
+
+
+def test_noncausal_bwd_sees_all_queries():
+    """A backward that walks only the causal band (the defect discussed in the
+    tutorial's comment thread) would give the same dK for causal and
+    non-causal inputs on the first key block; the oracle says they differ and
+    the kernel must follow the oracle."""
+    wl = AttnWorkload("nc", BF16, 1, 2, 256, 256, 64, False, seed=8)
+    t = attn_inputs(wl)
+    got = run_fwd_bwd(wl, t)
+    compare(wl, t, got)
+    wlc = AttnWorkload("c", BF16, 1, 2, 256, 256, 64, True, seed=8)
+    gotc = run_fwd_bwd(wlc, t)
+    assert np.abs(got["dk"][:, :, :64] - gotc["dk"][:, :, :64]).max() > 0.1
+
+
+def test_large_scale_peaky_softmax():
+    """sm_scale 1.0 at D = 128 makes rows nearly one-hot (large logits)."""
+    wl = AttnWorkload("peaky", BF16, 1, 2, 256, 256, 128, True, seed=9, sm_scale=1.0)
+    t = attn_inputs(wl)
+    compare(wl, t, run_fwd_bwd(wl, t))
+
+
+@pytest.mark.parametrize("name,heads", [
+    ("causal_bf16_b4h16_s2048_d128", [(0, 0), (1, 9), (3, 15)]),
+    ("noncausal_bf16_b1h32_s8192_d128", [(0, 5)]),
+])
+def test_full_size_sampled_heads(name, heads):
+    wl = WORKLOADS[name]
+    log(f"fa full-size {name} heads {heads}")
+    t = attn_inputs(wl)
+    got = run_fwd_bwd(wl, t)
+    compare(wl, t, got, heads=heads)
+
+
+def test_full_size_tiny_f32():
+    wl = WORKLOADS["tiny_f32"]
+    t = attn_inputs(wl)
+    compare(wl, t, run_fwd_bwd(wl, t))
