@@ -339,6 +339,32 @@ def cpu_baseline(target_s):
             "seconds": round(tn, 2)}
 
 
+def profile_mode(torch):
+    """Launch each kernel of the headline step a few times, then copy 256 MiB
+    device-to-device; rocprofv3 --pmc runs wrap this to count HBM bytes per
+    dispatch, and the copy's counter value per byte is the calibration."""
+    from attention_fa2_tiles_amd.inputs import WORKLOADS
+    wl = WORKLOADS[HEADLINE]
+    _, d = attn_setup(torch, wl, ("q", "k", "v", "do"))
+    b = attn_buffers(torch, wl, d)
+    calls = attn_calls(wl, d, b)
+    calls["fwd"]()
+    for k in ("fwd", "delta", "dkdv", "dq"):
+        for _ in range(3):
+            calls[k]()
+        torch.cuda.synchronize()
+        progress(f"profiled {k}")
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    progress("profiled copy")
+
+
+COPY_BYTES = 256 << 20
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -347,6 +373,9 @@ def main():
     ap.add_argument("--no-components", action="store_true", help="time only the headline step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--profile", action="store_true",
+                    help="counter-collection mode: a few launches of each kernel of the step, then a plain "
+                         "device-to-device copy of 256 MiB (the byte-count calibration), no timing output")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -365,6 +394,10 @@ def main():
     lib.load()
     torch.cuda.set_device(0)
     timer = Timer(torch)
+
+    if args.profile:
+        profile_mode(torch)
+        return
 
     wl, ms_step, tflops, wall, roofline, summary = bench_headline(torch, args, timer)
     components = {HEADLINE: summary}
