@@ -38,6 +38,9 @@ def compile_flags():
         "-Wall",
         "-Wno-unused-function",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA results in VGPRs: keeps loop-carried accumulators from being
+        # copied between AGPRs and VGPRs on every iteration
+        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         f"-I{os.path.join(os.path.dirname(PKG), 'include')}",
     ]
 

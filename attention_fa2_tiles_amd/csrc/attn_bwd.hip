@@ -23,6 +23,8 @@
 //  * dQ pass: 4 waves x 32 queries per workgroup with Q and dO resident;
 //    64-key blocks of K, V (row-major) and K^t stream through LDS.  Each lane
 //    owns one query, so LSE and Delta are per-lane scalars.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -241,15 +243,12 @@ __global__ __launch_bounds__(kNT) void attn_dkdv_kernel(const BwdParams p) {
     issue(0);
     commit(smem[0]);
   }
+  __builtin_amdgcn_s_waitcnt(0);  // resident K/V loads and the first block
   __syncthreads();
 
-  for (int qb = 0; qb < nq; ++qb) {
-    St& cur = smem[qb & 1];
-    if (qb + 1 < nq) issue(qb + 1);
-    const int i0 = q_begin + qb * kQB;
-    const bool active = wave_valid && (!CAUSAL || i0 + kQB - 1 + pshift >= kw0);
-    if (active) {
-      const bool need_mask = CAUSAL && (i0 + pshift < kw0 + 31);
+  // One query block for this wave; MASK selects the causal-diagonal path.
+  auto block = [&](const St& cur, int i0, auto mask_tag) {
+      constexpr bool need_mask = decltype(mask_tag)::value;
       bool an = true, af = false;
       if constexpr (kPw) pw_classify(i0, i0 + kQB - 1, kw0, kw0 + 31, pshift, p.w, an, af);
       f32x16 s[ST], dp[ST], dsf[kPw ? ST : 1];
@@ -300,8 +299,8 @@ __global__ __launch_bounds__(kNT) void attn_dkdv_kernel(const BwdParams p) {
         for (int r = 0; r < 16; ++r) {
           const float l2 = lv[r >> 2][r & 3];
           const float dl = dv4[r >> 2][r & 3];
-          float pv = exp2_fast(s[st][r] * p.scale2 - l2);
-          if (need_mask) {
+          float pv = exp2_fast(fmaf(s[st][r], p.scale2, -l2));
+          if constexpr (need_mask) {
             const int qrow_i = i0 + 32 * st + perm_row(r, h);
             if (kj > qrow_i + pshift) pv = 0.f;
           }
@@ -352,6 +351,17 @@ __global__ __launch_bounds__(kNT) void attn_dkdv_kernel(const BwdParams p) {
           }
         }
       }
+  };
+
+  for (int qb = 0; qb < nq; ++qb) {
+    const St& cur = smem[qb & 1];
+    if (qb + 1 < nq) issue(qb + 1);
+    const int i0 = q_begin + qb * kQB;
+    if (wave_valid && (!CAUSAL || i0 + kQB - 1 + pshift >= kw0)) {
+      if (CAUSAL && (i0 + pshift < kw0 + 31))
+        block(cur, i0, std::true_type{});
+      else
+        block(cur, i0, std::false_type{});
     }
     if (qb + 1 < nq) commit(smem[(qb + 1) & 1]);
     __syncthreads();
@@ -488,15 +498,12 @@ __global__ __launch_bounds__(kNT) void attn_dq_kernel(const BwdParams p) {
     issue(0);
     commit(smem[0]);
   }
+  __builtin_amdgcn_s_waitcnt(0);  // resident Q/dO loads and the first block
   __syncthreads();
 
-  for (int jb = 0; jb < nkb; ++jb) {
-    St& cur = smem[jb & 1];
-    if (jb + 1 < nkb) issue(jb + 1);
-    const int n0 = jb * BN;
-    const bool active = wave_valid && (!CAUSAL || n0 <= row0 + 31 + pshift);
-    if (active) {
-      const bool need_mask = CAUSAL && (n0 + BN - 1 > row0 + pshift);
+  // One key block for this wave; MASK selects the causal-diagonal path.
+  auto block = [&](const St& cur, int n0, auto mask_tag) {
+      constexpr bool need_mask = decltype(mask_tag)::value;
       bool an = true, af = false;
       if constexpr (kPw) pw_classify(row0, row0 + 31, n0, n0 + BN - 1, pshift, p.w, an, af);
       f32x16 s[ST], dp[ST], dsf[kPw ? ST : 1];
@@ -539,8 +546,10 @@ __global__ __launch_bounds__(kNT) void attn_dq_kernel(const BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = n0 + 32 * st + perm_row(r, h);
-          float pv = exp2_fast(s[st][r] * p.scale2 - lse2);
-          if (need_mask && key > qi + pshift) pv = 0.f;
+          float pv = exp2_fast(fmaf(s[st][r], p.scale2, -lse2));
+          if constexpr (need_mask) {
+            if (key > qi + pshift) pv = 0.f;
+          }
           const float ds = pv * (dp[st][r] - dl);
           if constexpr (kPw) {
             if (an) {
@@ -581,6 +590,17 @@ __global__ __launch_bounds__(kNT) void attn_dq_kernel(const BwdParams p) {
           }
         }
       }
+  };
+
+  for (int jb = 0; jb < nkb; ++jb) {
+    const St& cur = smem[jb & 1];
+    if (jb + 1 < nkb) issue(jb + 1);
+    const int n0 = jb * BN;
+    if (wave_valid && (!CAUSAL || n0 <= row0 + 31 + pshift)) {
+      if (CAUSAL && (n0 + BN - 1 > row0 + pshift))
+        block(cur, n0, std::true_type{});
+      else
+        block(cur, n0, std::false_type{});
     }
     if (jb + 1 < nkb) commit(smem[(jb + 1) & 1]);
     __syncthreads();

@@ -10,14 +10,17 @@
 // (q2, k2) by query-key distance (FlagAttention piecewise.py, _fwd_kernel).
 //
 // How it maps to CDNA4: 4 waves per workgroup, 32 query rows per wave
-// (BM = 128), K/V blocks of 64 keys staged in LDS, double-buffered, loaded
-// with 16-byte global loads.  Scores are formed transposed, S^t = K Q^t, so
-// that each lane owns one query row: row max and row sum are in-lane
-// reductions plus one exchange with the other half-wave, and the rescale of
-// the output accumulator is lane-local because that accumulator is also kept
-// transposed (O^t = V^t P^t).  K sits in LDS row-major (swap23 rows) and V
-// transposed, so both products read 16-byte MFMA operands straight from LDS
-// and the scores feed the second product without leaving registers.
+// (BM = 128), K/V blocks of 64 keys double-buffered in LDS and filled by
+// direct global -> LDS loads (no staging registers).  Scores are formed
+// transposed, S^t = K Q^t, so that each lane owns one query row: row max and
+// row sum are in-lane reductions plus one exchange with the other half-wave,
+// and the rescale of the output accumulator is lane-local because that
+// accumulator is also kept transposed (O^t = V^t P^t).  K is read with
+// 16-byte row reads, V^t with transposing LDS reads of the same row-major
+// tile layout, and the scores feed the second product without leaving
+// registers (swap23 row order).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -28,6 +31,7 @@ constexpr int kWaves = 4;
 constexpr int kNT = 64 * kWaves;
 constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per K/V block
+constexpr float kRescaleSlack = 8.0f;  // log2 units: P may reach 2^8 before a rescale
 
 struct FwdParams {
   const void* q;
@@ -49,20 +53,28 @@ struct FwdParams {
 
 template <typename T, int D, int VAR>
 struct alignas(16) FwdStage {
-  using RT = RowTile<T, kBN, D, kNT>;
-  using TT = TransTile<T, kBN, D, kNT>;
-  static constexpr int NRM = (VAR == PLAIN) ? 1 : 2;  // K (+ tK or K2)
-  static constexpr int NTR = (VAR == JVP) ? 2 : 1;    // V^t (+ tV^t)
-  T rm[NRM][RT::ELEMS];
-  T tr[NTR][TT::ELEMS];
+  using Tile = DTile<T, kBN, D, kWaves>;
+  static constexpr int NK = (VAR == PLAIN) ? 1 : 2;  // K (+ tK or K2)
+  static constexpr int NV = (VAR == JVP) ? 2 : 1;    // V (+ tV)
+  T k[NK][Tile::ELEMS];
+  T v[NV][Tile::ELEMS];
 };
 
+// Two waves per SIMD (two workgroups per CU) when the variant fits in 256
+// registers per lane and two stages of LDS per workgroup fit twice in the
+// CU's 160 KiB; the JVP variant (second accumulator, tangent query) and the
+// D = 128 piecewise variant (two K tiles) run one wave per SIMD.
+template <int VAR, int D>
+constexpr int fwd_waves_per_eu() {
+  return (VAR == PLAIN || (VAR == PW && D == 64)) ? 2 : 1;
+}
+
 template <typename T, int D, int VAR, bool CAUSAL>
-__global__ __launch_bounds__(kNT) void attn_fwd_kernel(const FwdParams p) {
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(fwd_waves_per_eu<VAR, D>(), fwd_waves_per_eu<VAR, D>())))
+void attn_fwd_kernel(const FwdParams p) {
   using V8 = typename Vec8<T>::type;
   using St = FwdStage<T, D, VAR>;
-  using RT = typename St::RT;
-  using TT = typename St::TT;
+  using Tile = typename St::Tile;
   constexpr int KK = D / 16;     // 16-wide k steps over the head dim
   constexpr int DT = D / 32;     // 32-wide tiles of the output's head dim
   constexpr int ST = kBN / 32;   // 32-key score tiles per block
@@ -91,11 +103,14 @@ __global__ __launch_bounds__(kNT) void attn_fwd_kernel(const FwdParams p) {
   const int64_t qbase = (int64_t)bh * p.M * D;
   const int64_t kbase = (int64_t)bh * p.N * D;
 
-  const T* Kp = (const T*)p.k + kbase;
-  const T* Vp = (const T*)p.v + kbase;
-  const T* K2p = kPw ? (const T*)p.k2 + kbase : nullptr;
-  const T* TKp = kJvp ? (const T*)p.tk + kbase : nullptr;
-  const T* TVp = kJvp ? (const T*)p.tv + kbase : nullptr;
+  // Direct loads of this head's K/V (and tK/tV or K2): uniform block base
+  // pointer plus in-tile lane offsets computed once.
+  const T* gk = (const T*)p.k + kbase;
+  const T* gv = (const T*)p.v + kbase;
+  const T* gk2 = kPw ? (const T*)p.k2 + kbase : kJvp ? (const T*)p.tk + kbase : gk;
+  const T* gv2 = kJvp ? (const T*)p.tv + kbase : gv;
+  DmaTile<T, kBN, D, kWaves> dma;
+  dma.lane_offsets(wave, lane);
 
   int n_end = p.N;
   const int wg_last_row = min(p.M, m0 + kBM) - 1;
@@ -128,12 +143,27 @@ __global__ __launch_bounds__(kNT) void attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) accg[dt] = zero16();
   }
-  float m_i = kNegInf;  // running max, log2 units
+  float m_i = kNegInf;  // running max (possibly stale, see block()), log2 units
   float l_i = 0.f;      // running sum, this half-wave's keys
   float mu_i = 0.f;     // JVP: running sum of P * Sdot, this half-wave's keys
 
-  RT ldk, ldk2;
-  TT ldv, ldtv;
+  // Loop-invariant LDS byte offsets inside a tile.  K row reads: row li,
+  // chunk 2 kk + h (the 32-row sub-tile adds a constant).  V^t transposing
+  // reads: (d-tile dt, half s) for key group 0 (key groups add constants).
+  uint32_t kofs[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) kofs[kk] = (uint32_t)((li * D + (((2 * kk + h) ^ swz<D>(li)) * 8)) * 2);
+  const TrLane tl(lane);
+  uint32_t vofs[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int m = swap23(8 * tl.hh + 4 * s2 + tl.r);
+      const int d = 32 * dt + tl.dcol;
+      vofs[dt][s2] = (uint32_t)((m * D + (((d >> 3) ^ swz<D>(m)) * 8) + (d & 7)) * 2);
+    }
+  }
 
   // Piecewise: which score pairs a block needs, for a row range.
   auto pw_class = [&](int r_lo, int r_hi, int n0, bool& all_near, bool& all_far) {
@@ -143,136 +173,112 @@ __global__ __launch_bounds__(kNT) void attn_fwd_kernel(const FwdParams p) {
     all_far = (p.w < 0) || (dmin > p.w) || (dmax < -p.w);
   };
 
-  bool ld_k1 = true, ld_k2 = true;  // piecewise: tiles staged for the next block
-  auto issue = [&](int jb) {
+  // Issue the direct loads of K/V block jb into stage st (completion: vmcnt).
+  auto issue = [&](St& st, int jb) {
     const int64_t off = (int64_t)jb * kBN * D;
     if constexpr (kPw) {
       bool an, af;
       pw_class(m0, wg_last_row, jb * kBN, an, af);
-      ld_k1 = !af;
-      ld_k2 = !an;
-      if (ld_k1) ldk.load(Kp + off, tid);
-      if (ld_k2) ldk2.load(K2p + off, tid);
+      if (!af) dma.load(gk + off, st.k[0], wave);
+      if (!an) dma.load(gk2 + off, st.k[1], wave);
     } else {
-      ldk.load(Kp + off, tid);
-      if constexpr (kJvp) ldk2.load(TKp + off, tid);
+      dma.load(gk + off, st.k[0], wave);
+      if constexpr (kJvp) dma.load(gk2 + off, st.k[1], wave);
     }
-    ldv.load(Vp + off, tid);
-    if constexpr (kJvp) ldtv.load(TVp + off, tid);
-  };
-  auto commit = [&](St& s) {
-    if constexpr (kPw) {
-      if (ld_k1) ldk.store(s.rm[0], tid);
-      if (ld_k2) ldk2.store(s.rm[1], tid);
-    } else {
-      ldk.store(s.rm[0], tid);
-      if constexpr (kJvp) ldk2.store(s.rm[1], tid);
-    }
-    ldv.store(s.tr[0], tid);
-    if constexpr (kJvp) ldtv.store(s.tr[1], tid);
+    dma.load(gv + off, st.v[0], wave);
+    if constexpr (kJvp) dma.load(gv2 + off, st.v[1], wave);
   };
 
-  if (nblk > 0) {
-    issue(0);
-    commit(smem[0]);
-  }
+  if (nblk > 0) issue(smem[0], 0);
+  // The query operands and the first block have landed before the loop.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int jb = 0; jb < nblk; ++jb) {
-    St& cur = smem[jb & 1];
-    if (jb + 1 < nblk) issue(jb + 1);
-    const int n0 = jb * kBN;
-    const bool active = wave_valid && (!CAUSAL || n0 <= row0 + 31 + pshift);
-    if (active) {
-      const bool need_mask = CAUSAL && (n0 + kBN - 1 > row0 + pshift);
-      f32x16 s[ST];
-      f32x16 sd[kJvp ? ST : 1];
-      // ---- scores S^t = K Q^t (and tangents) ------------------------------
-      if constexpr (kPw) {
-        bool an, af;
-        pw_class(row0, row0 + 31, n0, an, af);
-#pragma unroll
-        for (int st = 0; st < ST; ++st) {
-          f32x16 s1 = zero16(), s2 = zero16();
-          const T* k1row = cur.rm[0] + (32 * st + li) * RT::PITCH + 8 * h;
-          const T* k2row = cur.rm[1] + (32 * st + li) * RT::PITCH + 8 * h;
-          if (!af) {
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) s1 = mfma32x32x16(lds_read8(k1row + 16 * kk), qf[kk], s1);
-          }
-          if (!an) {
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) s2 = mfma32x32x16(lds_read8(k2row + 16 * kk), q2f[kk], s2);
-          }
-          if (an) {
-            s[st] = s1;
-          } else if (af) {
-            s[st] = s2;
-          } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = n0 + 32 * st + perm_row(r, h);
-              const int dist = qi + pshift - key;
-              s[st][r] = (dist <= p.w && dist >= -p.w) ? s1[r] : s2[r];
-            }
-          }
-        }
-      } else {
-#pragma unroll
-        for (int st = 0; st < ST; ++st) {
-          s[st] = zero16();
-          if constexpr (kJvp) sd[st] = zero16();
-          const T* krow = cur.rm[0] + (32 * st + li) * RT::PITCH + 8 * h;
-#pragma unroll
-          for (int kk = 0; kk < KK; ++kk) {
-            const V8 a = lds_read8(krow + 16 * kk);
-            s[st] = mfma32x32x16(a, qf[kk], s[st]);
-            if constexpr (kJvp) sd[st] = mfma32x32x16(a, tqf[kk], sd[st]);
-          }
-          if constexpr (kJvp) {
-            const T* tkrow = cur.rm[1] + (32 * st + li) * RT::PITCH + 8 * h;
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) sd[st] = mfma32x32x16(lds_read8(tkrow + 16 * kk), qf[kk], sd[st]);
-          }
-        }
-      }
-      // ---- online softmax (log2 units) ------------------------------------
-      float mloc = kNegInf;
+  auto krow8 = [&](const T* tile, int st, int kk) -> V8 {
+    return *reinterpret_cast<const V8*>(reinterpret_cast<const char*>(tile) + kofs[kk] + st * 32 * D * 2);
+  };
+
+  // One K/V block for this wave.  Scores are raw Q.K in the loop; the scale
+  // (sm_scale * log2 e) is folded into the exponent's FMA.  The running max
+  // m_i is in log2 units and is only raised when a row's block max exceeds
+  // it by more than kRescaleSlack: otherwise P = exp2(s - m_i) <= 2^slack is
+  // accumulated against the stale max, which leaves O = acc / l and
+  // LSE = m_i + log2 l exact and skips the rescale of the accumulators.
+  auto block = [&](const St& cur, int n0, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    f32x16 s[ST];
+    f32x16 sd[kJvp ? ST : 1];
+    // ---- scores S^t = K Q^t (and tangents) ------------------------------
+    if constexpr (kPw) {
+      bool an, af;
+      pw_class(row0, row0 + 31, n0, an, af);
 #pragma unroll
       for (int st = 0; st < ST; ++st) {
+        f32x16 s1 = zero16(), s2 = zero16();
+        if (!af) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[st][r] * p.scale2;
-          if (need_mask) {
+          for (int kk = 0; kk < KK; ++kk) s1 = mfma32x32x16(krow8(cur.k[0], st, kk), qf[kk], s1);
+        }
+        if (!an) {
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) s2 = mfma32x32x16(krow8(cur.k[1], st, kk), q2f[kk], s2);
+        }
+        if (an) {
+          s[st] = s1;
+        } else if (af) {
+          s[st] = s2;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
             const int key = n0 + 32 * st + perm_row(r, h);
-            if (key > qi + pshift) x = kNegInf;
+            const int dist = qi + pshift - key;
+            s[st][r] = (dist <= p.w && dist >= -p.w) ? s1[r] : s2[r];
           }
-          s[st][r] = x;
-          mloc = fmaxf(mloc, x);
         }
       }
-      mloc = fmaxf(mloc, xor32(mloc));
-      const float m_new = fmaxf(m_i, mloc);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = exp2_fast(m_i - m_use);
-      float lsum = 0.f, musum = 0.f;
+    } else {
+#pragma unroll
+      for (int st = 0; st < ST; ++st) {
+        s[st] = zero16();
+        if constexpr (kJvp) sd[st] = zero16();
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const V8 a = krow8(cur.k[0], st, kk);
+          s[st] = mfma32x32x16(a, qf[kk], s[st]);
+          if constexpr (kJvp) sd[st] = mfma32x32x16(a, tqf[kk], sd[st]);
+        }
+        if constexpr (kJvp) {
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) sd[st] = mfma32x32x16(krow8(cur.k[1], st, kk), qf[kk], sd[st]);
+        }
+      }
+    }
+    // ---- online softmax ---------------------------------------------------
+    if constexpr (MASK) {
 #pragma unroll
       for (int st = 0; st < ST; ++st) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pv = exp2_fast(s[st][r] - m_use);
-          s[st][r] = pv;
-          lsum += pv;
-          if constexpr (kJvp) {
-            const float ps = pv * sd[st][r] * p.sm_scale;
-            sd[st][r] = ps;
-            musum += ps;
-          }
+          const int key = n0 + 32 * st + perm_row(r, h);
+          if (key > qi + pshift) s[st][r] = kNegInf;
         }
       }
-      l_i = alpha * l_i + lsum;
-      m_i = m_new;
-      if constexpr (kJvp) mu_i = alpha * mu_i + musum;
+    }
+    // row max over this lane's 16 * ST scores: four independent chains
+    float mx[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) mx[c] = kNegInf;
+#pragma unroll
+    for (int st = 0; st < ST; ++st) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx[(r >> 1) & 3] = fmaxf(mx[(r >> 1) & 3], s[st][r]);
+    }
+    const float mloc = halves_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))) * p.scale2;
+    if (__ballot(mloc > m_i + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_i, mloc);
+      const float alpha = exp2_fast(m_i - m_new);  // m_i = -inf -> 0
+      l_i *= alpha;
+      if constexpr (kJvp) mu_i *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -282,37 +288,93 @@ __global__ __launch_bounds__(kNT) void attn_fwd_kernel(const FwdParams p) {
           for (int r = 0; r < 16; ++r) accg[dt][r] *= alpha;
         }
       }
-      // ---- O^t += V^t P^t (and the tangent accumulator) --------------------
-      V8 pb[PT];
-      V8 psb[kJvp ? PT : 1];
+      m_i = m_new;
+    }
+    const float neg_m = (m_i == kNegInf) ? 0.f : -m_i;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f}, mus[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < PT; ++t) {
-        pb[t] = pack8<T>(s[t >> 1], 8 * (t & 1));
-        if constexpr (kJvp) psb[t] = pack8<T>(sd[t >> 1], 8 * (t & 1));
-      }
+    for (int st = 0; st < ST; ++st) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const T* vrow = cur.tr[0] + (32 * dt + li) * TT::PITCH + 8 * h;
-#pragma unroll
-        for (int t = 0; t < PT; ++t) {
-          const V8 a = lds_read8(vrow + 16 * t);
-          acc[dt] = mfma32x32x16(a, pb[t], acc[dt]);
-          if constexpr (kJvp) accg[dt] = mfma32x32x16(a, psb[t], accg[dt]);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const float pv = exp2_fast(fmaf(s[st][r], p.scale2, neg_m));
+        s[st][r] = pv;
+        ls[r & 3] += pv;
         if constexpr (kJvp) {
-          const T* tvrow = cur.tr[1] + (32 * dt + li) * TT::PITCH + 8 * h;
-#pragma unroll
-          for (int t = 0; t < PT; ++t) accg[dt] = mfma32x32x16(lds_read8(tvrow + 16 * t), pb[t], accg[dt]);
+          const float ps = pv * sd[st][r] * p.sm_scale;
+          sd[st][r] = ps;
+          mus[r & 3] += ps;
         }
       }
     }
-    if (jb + 1 < nblk) commit(smem[(jb + 1) & 1]);
+    l_i += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    if constexpr (kJvp) mu_i += (mus[0] + mus[1]) + (mus[2] + mus[3]);
+    // ---- O^t += V^t P^t (and the tangent accumulator) ----------------------
+    V8 pb[PT];
+    V8 psb[kJvp ? PT : 1];
+#pragma unroll
+    for (int t = 0; t < PT; ++t) {
+      pb[t] = pack8<T>(s[t >> 1], 8 * (t & 1));
+      if constexpr (kJvp) psb[t] = pack8<T>(sd[t >> 1], 8 * (t & 1));
+    }
+    // V^t operands come from transposing LDS reads issued as inline asm
+    // (see TrOps): the reads of d-tile dt + 1 are in flight while the
+    // products of d-tile dt run.
+    const uint32_t vbase = lds_addr(cur.v[0]);
+    const uint32_t vbase2 = kJvp ? lds_addr(cur.v[kJvp ? 1 : 0]) : 0u;
+    TrOps<T, PT> va, vb;
+    TrOps<T, kJvp ? PT : 1> ta, tb;
+    va.template issue_at<D>(vbase, vofs[0]);
+    if constexpr (kJvp) ta.template issue_at<D>(vbase2, vofs[0]);
+    va.wait();
+    if constexpr (kJvp) ta.wait();
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      TrOps<T, PT>& cv = (dt & 1) ? vb : va;
+      TrOps<T, PT>& nv = (dt & 1) ? va : vb;
+      TrOps<T, kJvp ? PT : 1>& ct = (dt & 1) ? tb : ta;
+      TrOps<T, kJvp ? PT : 1>& nt = (dt & 1) ? ta : tb;
+      if (dt + 1 < DT) {
+        nv.template issue_at<D>(vbase, vofs[dt + 1]);
+        if constexpr (kJvp) nt.template issue_at<D>(vbase2, vofs[dt + 1]);
+      }
+#pragma unroll
+      for (int t = 0; t < PT; ++t) {
+        acc[dt] = mfma32x32x16(cv.op[t], pb[t], acc[dt]);
+        if constexpr (kJvp) accg[dt] = mfma32x32x16(cv.op[t], psb[t], accg[dt]);
+      }
+      if constexpr (kJvp) {
+#pragma unroll
+        for (int t = 0; t < PT; ++t) accg[dt] = mfma32x32x16(ct.op[t], pb[t], accg[dt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (dt + 1 < DT) {
+        nv.wait();
+        if constexpr (kJvp) nt.wait();
+      }
+    }
+  };
+
+  // One step: prefetch block jb + 1 into `next` while block jb is computed
+  // from `cur`; then wait for this wave's loads and synchronise.
+  auto step = [&](const St& cur, St& next, int jb) {
+    if (jb + 1 < nblk) issue(next, jb + 1);
+    const int n0 = jb * kBN;
+    const bool active = wave_valid && (!CAUSAL || n0 <= row0 + 31 + pshift);
+    if (active) {
+      if (CAUSAL && (n0 + kBN - 1 > row0 + pshift))
+        block(cur, n0, std::true_type{});
+      else
+        block(cur, n0, std::false_type{});
+    }
+    wait_vmcnt0();
     __syncthreads();
-  }
+  };
+  for (int jb = 0; jb < nblk; ++jb) step(smem[jb & 1], smem[(jb + 1) & 1], jb);
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----------------------
+  // Waves whose rows lie beyond M (last query block of a head) store nothing.
   if (!wave_valid) return;
-  const float l = l_i + xor32(l_i);
+  const float l = halves_sum(l_i);
   const bool has = l > 0.f;
   const float inv = has ? 1.f / l : 0.f;
   T* orow = (T*)p.o + qbase + (int64_t)qi * D;
@@ -320,7 +382,7 @@ __global__ __launch_bounds__(kNT) void attn_fwd_kernel(const FwdParams p) {
   for (int dt = 0; dt < DT; ++dt) store_acc_t<T>(orow, acc[dt], 32 * dt, h, inv);
   if (h == 0) p.lse[(int64_t)bh * p.M + qi] = has ? (m_i + log2f(l)) * kLn2 : kNegInf;
   if constexpr (kJvp) {
-    const float mu = mu_i + xor32(mu_i);
+    const float mu = halves_sum(mu_i);
     const float c = mu * inv;  // mu / l
     T* torow = (T*)p.to + qbase + (int64_t)qi * D;
 #pragma unroll

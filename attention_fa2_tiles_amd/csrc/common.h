@@ -62,6 +62,9 @@ __device__ __forceinline__ typename Vec8<T>::type pack8(const f32x16& v, int bas
   return r;
 }
 
+// s_waitcnt vmcnt(0) with the LDS and export counters left alone.
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
@@ -169,6 +172,192 @@ struct TransTile {
           }
         }
       }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// LDS tiles filled by direct global -> LDS loads (gfx950 global_load_lds of
+// 16 bytes: lane l's 16 bytes land at the instruction's LDS base + 16 * l).
+//
+// A tile holds R rows of D 2-byte elements, row-major with no padding.  LDS
+// row m holds global row swap23(m) of the tile, and 16-byte chunk c of LDS
+// row m sits at chunk slot c ^ swz<D>(m).  The XOR pattern makes both ways
+// the kernels read a tile free of bank conflicts:
+//  * row reads (ds_read_b128): 16 lanes read one chunk of 16 consecutive
+//    rows -> 16 distinct 16-byte slots of the 256-byte bank window;
+//  * transposing reads (ds_read_b64_tr_b16): 32 lanes read a 4-row x
+//    4-chunk block -> 16 distinct slots.
+// ---------------------------------------------------------------------------
+
+template <int D>
+__device__ __forceinline__ int swz(int m) {
+  static_assert(D == 64 || D == 128, "head dim");
+  if constexpr (D == 128) return ((m & 3) << 2) | ((m >> 2) & 3);
+  else return (((m >> 1) & 1) << 2) | ((m >> 2) & 3);
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+template <typename T, int R, int D, int NW>
+struct DTile {
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  static constexpr int ROWS_PER_INSTR = 64 / CPR;   // rows per wave instruction
+  static constexpr int INSTR = R / ROWS_PER_INSTR;  // wave instructions per tile
+  static constexpr int PER_WAVE = INSTR / NW;
+  static constexpr int ELEMS = R * D;
+  static_assert(INSTR % NW == 0, "tile must split evenly over the waves");
+
+  // Issue this wave's share of the direct loads of the R x D tile at g
+  // (row stride D elements) into lds.  Completion is tracked by vmcnt.
+  __device__ static __forceinline__ void load(T* lds, const T* g, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int ins = wave * PER_WAVE + j;
+      const int p = ins * 64 + lane;
+      const int m = p / CPR, slot = p % CPR;
+      const T* src = g + swap23(m) * D + ((slot ^ swz<D>(m)) * 8);
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)src,
+          (void __attribute__((address_space(3)))*)(lds + ins * 512), 16, 0, 0);
+    }
+  }
+
+  // 8 consecutive elements (chunk c) of LDS row m: one ds_read_b128.
+  __device__ static __forceinline__ typename Vec8<T>::type row8(const T* lds, int m, int c) {
+    return *reinterpret_cast<const typename Vec8<T>::type*>(lds + m * D + ((c ^ swz<D>(m)) * 8));
+  }
+};
+
+// Direct loads of an R x D tile with loop-invariant per-lane byte offsets
+// inside the tile (computed once by lane_offsets): a tile is issued from a
+// uniform base pointer plus those 32-bit offsets, which the compiler can
+// encode with a scalar base register, so issuing costs no vector arithmetic.
+template <typename T, int R, int D, int NW>
+struct DmaTile {
+  using Tile = DTile<T, R, D, NW>;
+  static constexpr int PER_WAVE = Tile::PER_WAVE;
+  uint32_t voff[PER_WAVE];
+
+  __device__ __forceinline__ void lane_offsets(int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int ins = wave * PER_WAVE + j;
+      const int p = ins * 64 + lane;
+      const int m = p / Tile::CPR, slot = p % Tile::CPR;
+      voff[j] = (uint32_t)((swap23(m) * D + ((slot ^ swz<D>(m)) * 8)) * 2);
+    }
+  }
+  // Load the tile whose first row is at g (row stride D) into lds.
+  __device__ __forceinline__ void load(const T* g, T* lds, int wave) const {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int ins = wave * PER_WAVE + j;
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(reinterpret_cast<const char*>(g) + voff[j]),
+          (void __attribute__((address_space(3)))*)(lds + ins * 512), 16, 0, 0);
+    }
+  }
+};
+
+// Combine the two half-wave partial values of a row (lanes l and l ^ 32).
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x), false, false);
+  return fmaxf(__builtin_bit_cast(float, (int)r[0]), __builtin_bit_cast(float, (int)r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x), false, false);
+  return __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+}
+
+// Per-lane part of a transposing operand read.  The operand is the 32 x 16
+// block X^t[d][j] of a tile X[j][d] (j = tile row: key or query, natural
+// order), d in [32 dt, 32 dt + 32), j in [j0, j0 + 16): lane l receives
+// X[j0 + 8 (l/32) + e][32 dt + l%32] for e = 0..7, i.e. exactly the MFMA
+// operand "row = l%32, 8 consecutive k from 8 (l/32)".  Built from two
+// ds_read_b64_tr_b16: inside each 16-lane group, lane 4r + c supplies row
+// j_r, columns d0 + 4c .. d0 + 4c + 3, and lane i receives column d0 + i of
+// the four rows.
+struct TrLane {
+  int r;      // row within the 4-row group this lane addresses
+  int dcol;   // column offset (within a 32-wide d tile) this lane addresses
+  int hh;     // operand k-group (l / 32)
+  __device__ __forceinline__ explicit TrLane(int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    r = i >> 2;
+    dcol = 16 * (g & 1) + 4 * (i & 3);
+    hh = g >> 1;
+  }
+};
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Column offset of d-tile dt (for TrOps::issue).
+__device__ __forceinline__ constexpr int dt_base(int dt) { return 32 * dt; }
+
+// NOPS transposing operand reads X^t[d0 + (0..31)][16 t + (0..15)], t = 0..
+// NOPS-1, of an R x D tile X (see DTile / TrLane).  Each operand is two
+// ds_read_b64_tr_b16 issued as inline asm: the compiler's wait-count pass
+// cannot tell these reads apart from the direct loads of the next stage
+// that are in flight (it has no alias scope for them) and would otherwise
+// wait for all of those loads before every such read.  The results are only
+// valid after wait(), which waits for all outstanding LDS reads and ties the
+// result registers to that wait.
+template <typename T, int NOPS>
+struct TrOps {
+  typename Vec8<T>::type op[NOPS];
+
+  template <int D>
+  __device__ __forceinline__ void issue(const T* lds, const TrLane& tl, int d0) {
+    const int d = d0 + tl.dcol;
+#pragma unroll
+    for (int t = 0; t < NOPS; ++t) {
+      u32x2 part[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int m = swap23(16 * t + 8 * tl.hh + 4 * s + tl.r);
+        const uint32_t a = lds_addr(lds + m * D + (((d >> 3) ^ swz<D>(m)) * 8) + (d & 7));
+        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(part[s]) : "v"(a));
+      }
+      u32x4 w;
+      w[0] = part[0][0];
+      w[1] = part[0][1];
+      w[2] = part[1][0];
+      w[3] = part[1][1];
+      op[t] = __builtin_bit_cast(typename Vec8<T>::type, w);
+    }
+  }
+  // Same reads from precomputed per-lane offsets: ofs[s] is the byte offset
+  // (inside the tile) of this lane's half-s read for key group 0; key group
+  // t adds t * 16 rows, folded into the instruction's immediate offset.
+  template <int D>
+  __device__ __forceinline__ void issue_at(uint32_t base, const uint32_t (&ofs)[2]) {
+    const uint32_t a0 = base + ofs[0], a1 = base + ofs[1];
+#pragma unroll
+    for (int t = 0; t < NOPS; ++t) {
+      u32x2 part[2];
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(part[0]) : "v"(a0), "i"(t * 16 * D * 2));
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(part[1]) : "v"(a1), "i"(t * 16 * D * 2));
+      u32x4 w;
+      w[0] = part[0][0];
+      w[1] = part[0][1];
+      w[2] = part[1][0];
+      w[3] = part[1][1];
+      op[t] = __builtin_bit_cast(typename Vec8<T>::type, w);
+    }
+  }
+  __device__ __forceinline__ void wait() {
+    if constexpr (NOPS == 1) {
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(op[0]));
+    } else if constexpr (NOPS == 2) {
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(op[0]), "+v"(op[1]));
+    } else if constexpr (NOPS == 4) {
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(op[0]), "+v"(op[1]), "+v"(op[2]), "+v"(op[3]));
+    } else {
+      static_assert(NOPS == 1 || NOPS == 2 || NOPS == 4, "operand count");
     }
   }
 };

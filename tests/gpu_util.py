@@ -55,6 +55,44 @@ def filled(shape, dtype, value=float("nan")):
     return t
 
 
+GUARD_ELEMS = 4096
+_guards = []
+
+
+def guarded(shape, dtype, value=float("nan")):
+    """An output buffer placed between two guard regions of GUARD_ELEMS
+    elements filled with a sentinel; check_guards() verifies that no kernel
+    wrote outside the buffer."""
+    import torch
+    n = 1
+    for x in shape:
+        n *= x
+    flat = torch.empty(n + 2 * GUARD_ELEMS, dtype=torch_dtype(dtype), device="cuda")
+    flat.fill_(-12345.0 if dtype != F16 else -1234.0)
+    t = flat[GUARD_ELEMS:GUARD_ELEMS + n].view(shape)
+    t.fill_(value)
+    _guards.append(flat)
+    return t
+
+
+def guarded_f32(shape):
+    return guarded(shape, F32)
+
+
+def check_guards():
+    import torch
+    torch.cuda.synchronize()
+    bad = []
+    for flat in _guards:
+        head = flat[:GUARD_ELEMS].float()
+        tail = flat[-GUARD_ELEMS:].float()
+        sentinel = head[0].item()
+        if not (torch.all(head == sentinel) and torch.all(tail == sentinel)):
+            bad.append(flat.numel())
+    _guards.clear()
+    assert not bad, f"a kernel wrote outside its output buffer ({len(bad)} buffers)"
+
+
 def host(t):
     import torch
     torch.cuda.synchronize()

@@ -14,24 +14,25 @@ import pytest
 import oracle
 from attention_fa2_tiles_amd import lib
 from attention_fa2_tiles_amd.inputs import BF16, F16, F32, WORKLOADS, AttnWorkload, attn_inputs
-from gpu_util import dev, empty_f32, filled, host, log, need_gpu
+from gpu_util import check_guards, dev, empty_f32, filled, guarded, guarded_f32, host, log, need_gpu
 from tolerance import check_fp32_abs, check_grad, check_lse, check_output
 
 pytestmark = pytest.mark.gpu
 
 
-def run_fwd_bwd(wl, t, with_bwd=True, steps=False):
+def run_fwd_bwd(wl, t, with_bwd=True, steps=False, guard=False):
     torch = need_gpu()
     q, k, v, do = (dev(t[n]) for n in ("q", "k", "v", "do"))
     B, H, M, N, D = wl.B, wl.H, wl.M, wl.N, wl.D
-    o = filled((B, H, M, D), wl.dtype)
-    lse = empty_f32((B, H, M))
+    alloc = guarded if guard else filled
+    o = alloc((B, H, M, D), wl.dtype)
+    lse = guarded_f32((B, H, M)) if guard else empty_f32((B, H, M))
     lib.fa_fwd(wl.dtype, q, k, v, o, lse, B, H, M, N, D, wl.causal, wl.sm_scale)
     out = {"o": o, "lse": lse}
     if with_bwd:
-        dq, dk, dv = (filled(x.shape, wl.dtype) for x in (q, k, v))
+        dq, dk, dv = (alloc(x.shape, wl.dtype) for x in (q, k, v))
         if steps:
-            delta = empty_f32((B, H, M))
+            delta = guarded_f32((B, H, M)) if guard else empty_f32((B, H, M))
             lib.fa_bwd_delta(wl.dtype, o, do, delta, B, H, M, D)
             lib.fa_bwd_dkdv(wl.dtype, q, k, v, do, lse, delta, dk, dv, B, H, M, N, D, wl.causal, wl.sm_scale)
             lib.fa_bwd_dq(wl.dtype, q, k, v, do, lse, delta, dq, B, H, M, N, D, wl.causal, wl.sm_scale)
@@ -42,7 +43,10 @@ def run_fwd_bwd(wl, t, with_bwd=True, steps=False):
                        wl.causal, wl.sm_scale)
         out.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
-    return {kk: host(vv) for kk, vv in out.items()}
+    res = {kk: host(vv) for kk, vv in out.items()}
+    if guard:
+        check_guards()
+    return res
 
 
 def compare(wl, t, got, heads=None, with_bwd=True):
@@ -85,7 +89,7 @@ def test_small_parity(case):
     wl = AttnWorkload("small", dtype, B, H, M, N, D, causal, seed=11 + M + N + D)
     log(f"fa small parity {case}")
     t = attn_inputs(wl)
-    got = run_fwd_bwd(wl, t)
+    got = run_fwd_bwd(wl, t, guard=True)
     compare(wl, t, got)
 
 

@@ -6,7 +6,7 @@ import pytest
 import oracle
 from attention_fa2_tiles_amd import lib
 from attention_fa2_tiles_amd.inputs import BF16, F16, F32, PIECEWISE_W, WORKLOADS, AttnWorkload, attn_inputs
-from gpu_util import dev, empty_f32, filled, host, log, need_gpu
+from gpu_util import check_guards, dev, empty_f32, filled, guarded, guarded_f32, host, log, need_gpu
 from tolerance import check_grad, check_lse, check_output
 
 pytestmark = pytest.mark.gpu
@@ -21,12 +21,14 @@ def run_jvp(wl, t):
     torch = need_gpu()
     q, k, v, tq, tk, tv = (dev(t[n]) for n in JVP_NAMES)
     B, H, M, N, D = wl.B, wl.H, wl.M, wl.N, wl.D
-    o = filled((B, H, M, D), wl.dtype)
-    to = filled((B, H, M, D), wl.dtype)
-    lse = empty_f32((B, H, M))
+    o = guarded((B, H, M, D), wl.dtype)
+    to = guarded((B, H, M, D), wl.dtype)
+    lse = guarded_f32((B, H, M))
     lib.fa_fwd_jvp(wl.dtype, q, k, v, tq, tk, tv, o, lse, to, B, H, M, N, D, wl.causal, wl.sm_scale)
     torch.cuda.synchronize()
-    return {"o": host(o), "lse": host(lse), "to": host(to)}
+    res = {"o": host(o), "lse": host(lse), "to": host(to)}
+    check_guards()
+    return res
 
 
 def compare_jvp(wl, t, got, heads=None):
@@ -88,12 +90,12 @@ def run_pw(wl, t, w, with_bwd=True):
     torch = need_gpu()
     q1, k1, q2, k2, v, do = (dev(t[n]) for n in PW_NAMES)
     B, H, M, N, D = wl.B, wl.H, wl.M, wl.N, wl.D
-    o = filled((B, H, M, D), wl.dtype)
-    lse = empty_f32((B, H, M))
+    o = guarded((B, H, M, D), wl.dtype)
+    lse = guarded_f32((B, H, M))
     lib.pw_fwd(wl.dtype, q1, k1, q2, k2, v, o, lse, B, H, M, N, D, wl.causal, wl.sm_scale, w)
     out = {"o": o, "lse": lse}
     if with_bwd:
-        grads = {n: filled(x.shape, wl.dtype) for n, x in
+        grads = {n: guarded(x.shape, wl.dtype) for n, x in
                  (("dq1", q1), ("dk1", k1), ("dq2", q2), ("dk2", k2), ("dv", v))}
         nb = lib.pw_bwd_workspace_size(B, H, M, N, D, wl.dtype)
         ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
@@ -101,7 +103,9 @@ def run_pw(wl, t, w, with_bwd=True):
                    grads["dk2"], grads["dv"], ws, nb, B, H, M, N, D, wl.causal, wl.sm_scale, w)
         out.update(grads)
     torch.cuda.synchronize()
-    return {kk: host(vv) for kk, vv in out.items()}
+    res = {kk: host(vv) for kk, vv in out.items()}
+    check_guards()
+    return res
 
 
 def compare_pw(wl, t, got, w, heads=None, with_bwd=True):

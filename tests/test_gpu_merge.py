@@ -6,7 +6,7 @@ import pytest
 import oracle
 from attention_fa2_tiles_amd import lib
 from attention_fa2_tiles_amd.inputs import BF16, F16, F32, MERGE_WORKLOAD, MergeWorkload, merge_inputs
-from gpu_util import dev, empty, empty_f32, filled, host, log, need_gpu
+from gpu_util import check_guards, dev, empty, empty_f32, filled, guarded, guarded_f32, host, log, need_gpu
 from tolerance import check_grad, check_lse, check_output
 
 pytestmark = pytest.mark.gpu
@@ -18,17 +18,19 @@ def run_merge(wl, t, with_gl=True, l0=None):
     l0d = dev(t["l0"]) if l0 is None else torch.from_numpy(l0.astype(np.float32)).cuda()
     gl = dev(t["gl"]) if with_gl else None
     R, D = wl.rows, wl.D
-    y = filled((R, D), wl.dtype)
-    lse = empty_f32((R,))
+    y = guarded((R, D), wl.dtype)
+    lse = guarded_f32((R,))
     lib.resmerge_fwd(wl.dtype, x, q, y0, l0d, y, lse, R, D, wl.eps)
-    gx, gy0 = filled((R, D), wl.dtype), filled((R, D), wl.dtype)
-    gq, gl0 = empty_f32((D,)), empty_f32((R,))
+    gx, gy0 = guarded((R, D), wl.dtype), guarded((R, D), wl.dtype)
+    gq, gl0 = guarded_f32((D,)), guarded_f32((R,))
     nb = lib.resmerge_bwd_workspace_size(R, D)
     ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
     lib.resmerge_bwd(wl.dtype, x, q, y0, l0d, gy, gl, gx, gq, gy0, gl0, ws, nb, R, D, wl.eps)
     torch.cuda.synchronize()
-    return {n: host(v) for n, v in (("y", y), ("lse", lse), ("gx", gx), ("gq", gq), ("gy0", gy0),
-                                    ("gl0", gl0))}
+    res = {n: host(v) for n, v in (("y", y), ("lse", lse), ("gx", gx), ("gq", gq), ("gy0", gy0),
+                                   ("gl0", gl0))}
+    check_guards()
+    return res
 
 
 def compare(wl, t, got, with_gl=True, l0=None):
