@@ -27,11 +27,20 @@
 namespace fa {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kNT = 64 * kWaves;
-constexpr int kBM = 32 * kWaves;  // query rows per workgroup
 constexpr int kBN = 64;           // keys per K/V block
 constexpr float kRescaleSlack = 8.0f;  // log2 units: P may reach 2^8 before a rescale
+constexpr int kLdsBytes = 160 * 1024;
+
+// Launch shape per variant.  Variants whose per-lane state fits in 256
+// registers run 8 waves (256 query rows) per workgroup, i.e. two waves per
+// SIMD sharing each K/V block; the others (JVP with D = 128) run 4 waves.
+// Each wave owns 32 query rows.
+template <int VAR, int D>
+struct FwdShape {
+  static constexpr int WAVES = (VAR == JVP && D == 128) ? 4 : 8;
+  static constexpr int NT = 64 * WAVES;
+  static constexpr int BM = 32 * WAVES;
+};
 
 struct FwdParams {
   const void* q;
@@ -53,25 +62,32 @@ struct FwdParams {
 
 template <typename T, int D, int VAR>
 struct alignas(16) FwdStage {
-  using Tile = DTile<T, kBN, D, kWaves>;
+  using Tile = DTile<T, kBN, D, FwdShape<VAR, D>::WAVES>;
   static constexpr int NK = (VAR == PLAIN) ? 1 : 2;  // K (+ tK or K2)
   static constexpr int NV = (VAR == JVP) ? 2 : 1;    // V (+ tV)
   T k[NK][Tile::ELEMS];
   T v[NV][Tile::ELEMS];
 };
 
-// Two waves per SIMD (two workgroups per CU) when the variant fits in 256
-// registers per lane and two stages of LDS per workgroup fit twice in the
-// CU's 160 KiB; the JVP variant (second accumulator, tangent query) and the
-// D = 128 piecewise variant (two K tiles) run one wave per SIMD.
+// K/V stages in the LDS ring: three (prefetch two blocks ahead) when they fit
+// in the CU's LDS, else two.
+template <typename T, int D, int VAR>
+constexpr int fwd_stages() {
+  return 3 * (int)sizeof(FwdStage<T, D, VAR>) <= kLdsBytes ? 3 : 2;
+}
+
 template <int VAR, int D>
 constexpr int fwd_waves_per_eu() {
-  return (VAR == PLAIN || (VAR == PW && D == 64)) ? 2 : 1;
+  return FwdShape<VAR, D>::WAVES / 4;
 }
 
 template <typename T, int D, int VAR, bool CAUSAL>
-__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(fwd_waves_per_eu<VAR, D>(), fwd_waves_per_eu<VAR, D>())))
+__global__ __launch_bounds__((FwdShape<VAR, D>::NT))
+__attribute__((amdgpu_waves_per_eu(fwd_waves_per_eu<VAR, D>(), fwd_waves_per_eu<VAR, D>())))
 void attn_fwd_kernel(const FwdParams p) {
+  constexpr int kWaves = FwdShape<VAR, D>::WAVES;
+  constexpr int kBM = FwdShape<VAR, D>::BM;
+  constexpr int NS = fwd_stages<T, D, VAR>();
   using V8 = typename Vec8<T>::type;
   using St = FwdStage<T, D, VAR>;
   using Tile = typename St::Tile;
@@ -82,7 +98,7 @@ void attn_fwd_kernel(const FwdParams p) {
   constexpr bool kJvp = VAR == JVP;
   constexpr bool kPw = VAR == PW;
 
-  __shared__ St smem[2];
+  __shared__ St smem[NS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -189,10 +205,18 @@ void attn_fwd_kernel(const FwdParams p) {
     if constexpr (kJvp) dma.load(gv2 + off, st.v[1], wave);
   };
 
-  if (nblk > 0) issue(smem[0], 0);
-  // The query operands and the first block have landed before the loop.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // Prologue: the query operands have landed; blocks 0 .. NS-2 are in
+  // flight and block 0 has landed (loads complete in issue order).
+  constexpr int kLoadsPerBlock = DmaTile<T, kBN, D, kWaves>::PER_WAVE * (St::NK + St::NV);
+  wait_vmcnt0();
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < nblk) issue(smem[j], j);
+  if (NS == 3 && nblk > 1)
+    wait_vmcnt<kLoadsPerBlock>();
+  else
+    wait_vmcnt0();
+  lds_barrier();
 
   auto krow8 = [&](const T* tile, int st, int kk) -> V8 {
     return *reinterpret_cast<const V8*>(reinterpret_cast<const char*>(tile) + kofs[kk] + st * 32 * D * 2);
@@ -354,22 +378,32 @@ void attn_fwd_kernel(const FwdParams p) {
     }
   };
 
-  // One step: prefetch block jb + 1 into `next` while block jb is computed
-  // from `cur`; then wait for this wave's loads and synchronise.
-  auto step = [&](const St& cur, St& next, int jb) {
-    if (jb + 1 < nblk) issue(next, jb + 1);
+  // Block jb is computed from stage jb % NS while block jb + NS - 1 is being
+  // loaded into the stage freed by block jb - 1.  Before the barrier each
+  // wave waits until its loads of block jb + 1 have landed, leaving those of
+  // the newest block in flight (loads complete in issue order).
+  int cur_stage = 0;
+  for (int jb = 0; jb < nblk; ++jb) {
+    const int ahead = jb + NS - 1;
+    int ld_stage = cur_stage + NS - 1;
+    if (ld_stage >= NS) ld_stage -= NS;
+    const bool issued = ahead < nblk;
+    if (issued) issue(smem[ld_stage], ahead);
     const int n0 = jb * kBN;
     const bool active = wave_valid && (!CAUSAL || n0 <= row0 + 31 + pshift);
     if (active) {
       if (CAUSAL && (n0 + kBN - 1 > row0 + pshift))
-        block(cur, n0, std::true_type{});
+        block(smem[cur_stage], n0, std::true_type{});
       else
-        block(cur, n0, std::false_type{});
+        block(smem[cur_stage], n0, std::false_type{});
     }
-    wait_vmcnt0();
-    __syncthreads();
-  };
-  for (int jb = 0; jb < nblk; ++jb) step(smem[jb & 1], smem[(jb + 1) & 1], jb);
+    if (NS == 3 && issued)
+      wait_vmcnt<kLoadsPerBlock>();
+    else
+      wait_vmcnt0();
+    lds_barrier();
+    cur_stage = (cur_stage + 1 == NS) ? 0 : cur_stage + 1;
+  }
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----------------------
   // Waves whose rows lie beyond M (last query block of a head) store nothing.
@@ -412,11 +446,12 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
   p.BH = a.B * a.H;
   p.M = a.M;
   p.N = a.N;
+  constexpr int kBM = FwdShape<VAR, D>::BM;
   p.nmb = (a.M + kBM - 1) / kBM;
   p.scale2 = a.sm_scale * kLog2e;
   p.sm_scale = a.sm_scale;
   p.w = a.w;
-  dim3 grid(p.nmb * p.BH), block(kNT);
+  dim3 grid(p.nmb * p.BH), block(FwdShape<VAR, D>::NT);
   if (a.causal)
     hipLaunchKernelGGL((attn_fwd_kernel<T, D, VAR, true>), grid, block, 0, s, p);
   else

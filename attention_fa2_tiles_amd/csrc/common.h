@@ -62,8 +62,26 @@ __device__ __forceinline__ typename Vec8<T>::type pack8(const f32x16& v, int bas
   return r;
 }
 
-// s_waitcnt vmcnt(0) with the LDS and export counters left alone.
-__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N) with the LDS and export counters left alone (gfx9
+// encoding: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+__device__ __forceinline__ void wait_vmcnt0() { wait_vmcnt<0>(); }
+
+// Workgroup barrier without the release/acquire fences of __syncthreads():
+// those make the compiler wait for every outstanding load (including the
+// direct LDS loads of stages still being prefetched) before the barrier.
+// Callers make LDS data visible themselves (wait_vmcnt for direct loads,
+// lgkmcnt for LDS stores); the empty asm statements keep the compiler from
+// moving memory accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
