@@ -13,16 +13,20 @@
 // piecewise variant dS is split by the distance rule into the (q1, k1) and
 // (q2, k2) parts.
 //
-// Layout on CDNA4:
-//  * dK/dV pass: 4 waves x 32 keys per workgroup with K and V resident in
-//    registers; query blocks of 32 rows stream through LDS both row-major
-//    (swap23, for S = Q K^t and dP = dO V^t) and transposed (for the
-//    accumulations dV^t += dO^t P and dK^t += Q^t dS).  Each lane owns one
-//    key column, so P and dS leave the score product already laid out as the
-//    B operand of the accumulation products.
-//  * dQ pass: 4 waves x 32 queries per workgroup with Q and dO resident;
-//    64-key blocks of K, V (row-major) and K^t stream through LDS.  Each lane
-//    owns one query, so LSE and Delta are per-lane scalars.
+// Layout on CDNA4 (both passes stream tiles through a three-stage LDS ring
+// filled by direct global -> LDS loads, prefetching two blocks ahead):
+//  * dK/dV pass: 32 keys per wave, 8 waves (4 for piecewise) per workgroup.
+//    K stays in registers (B operand of S = Q K^t), each wave's 32 rows of V
+//    stay in LDS (B operand of dP = dO V^t).  Query blocks of Q, dO and their
+//    LSE / Delta rows stream through the ring.  Each lane owns one key, so P
+//    and dS leave the score products already laid out as the B operands of
+//    dV^t += dO^t P and dK^t += Q^t dS, whose A operands (dO^t, Q^t) are
+//    transposing LDS reads of the same row-major tiles.
+//  * dQ pass: 32 queries per wave, 8 waves (4 for piecewise) per workgroup,
+//    Q and dO resident in registers; 64-key blocks of K and V stream through
+//    the ring.  S^t = K Q^t and dP^t = V dO^t put one query per lane (LSE and
+//    Delta are per-lane scalars) and dQ^t += K^t dS^t reads K^t with
+//    transposing LDS reads of the K tile.
 #include <type_traits>
 
 #include "common.h"
@@ -31,8 +35,7 @@
 namespace fa {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kNT = 64 * kWaves;
+constexpr int kLdsBytes = 160 * 1024;
 
 // ------------------------------------------------------------------ Delta --
 template <typename T>
@@ -111,48 +114,114 @@ __device__ __forceinline__ void pw_classify(int r_lo, int r_hi, int c_lo, int c_
   all_far = (w < 0) || (dmin > w) || (dmax < -w);
 }
 
-// ------------------------------------------------------------- dK/dV pass --
-constexpr int kQB = 32;            // query rows per streamed block
-constexpr int kKB = 32 * kWaves;   // keys per workgroup
+// 16-byte row reads of a DTile: row m, chunk c, as a byte offset.
+template <int D>
+__device__ __forceinline__ uint32_t row_chunk_ofs(int m, int c) {
+  return (uint32_t)((m * D + ((c ^ swz<D>(m)) * 8)) * 2);
+}
+
+// Byte offsets of the transposing reads (TrOps::issue_at) of d-tile dt,
+// halves s = 0, 1, key/query group 0 of a swap23 DTile.
+template <int D>
+__device__ __forceinline__ void tr_offsets(const TrLane& tl, uint32_t (&ofs)[D / 32][2]) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int m = swap23(8 * tl.hh + 4 * s2 + tl.r);
+      const int d = 32 * dt + tl.dcol;
+      ofs[dt][s2] = (uint32_t)((m * D + (((d >> 3) ^ swz<D>(m)) * 8) + (d & 7)) * 2);
+    }
+  }
+}
+
+// acc[dt] += X^t B over the d-tiles of a DTile X in LDS (transposing reads,
+// the reads of d-tile dt + 1 in flight during the products of d-tile dt).
+template <typename T, int D, int NOPS>
+__device__ __forceinline__ void accum_tr(f32x16 (&acc)[D / 32], uint32_t base, const uint32_t (&ofs)[D / 32][2],
+                                         const typename Vec8<T>::type (&b)[NOPS]) {
+  constexpr int DT = D / 32;
+  TrOps<T, NOPS> xa, xb;
+  xa.template issue_at<D>(base, ofs[0]);
+  xa.wait();
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    TrOps<T, NOPS>& cx = (dt & 1) ? xb : xa;
+    TrOps<T, NOPS>& nx = (dt & 1) ? xa : xb;
+    if (dt + 1 < DT) nx.template issue_at<D>(base, ofs[dt + 1]);
+#pragma unroll
+    for (int t = 0; t < NOPS; ++t) acc[dt] = mfma32x32x16(cx.op[t], b[t], acc[dt]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (dt + 1 < DT) nx.wait();
+  }
+}
+
+// ============================================================ dK/dV pass ==
+template <int D, int VAR>
+struct DkdvShape {
+  static constexpr int WAVES = (VAR == PW) ? 4 : 8;
+  static constexpr int NT = 64 * WAVES;
+  static constexpr int KB = 32 * WAVES;           // keys per workgroup
+  static constexpr int QB = (D == 64) ? 64 : 32;  // query rows per streamed block
+  static constexpr int NS = 3;                    // ring stages
+};
 
 template <typename T, int D, int VAR>
 struct alignas(16) DkdvStage {
-  using RT = RowTile<T, kQB, D, kNT>;
-  using TT = TransTile<T, kQB, D, kNT>;
+  using Sh = DkdvShape<D, VAR>;
+  using Tile = DTile<T, Sh::QB, D, Sh::WAVES>;
   static constexpr int NQ = (VAR == PW) ? 2 : 1;
-  T qrm[NQ][RT::ELEMS];
-  T dorm[RT::ELEMS];
-  T qtr[NQ][TT::ELEMS];
-  T dotr[TT::ELEMS];
-  alignas(16) float lse2[kQB];
-  alignas(16) float delta[kQB];
+  T q[NQ][Tile::ELEMS];       // Q (piecewise: Q1, Q2)
+  T dout[Tile::ELEMS];
+  float stats[2 * Sh::QB];    // LSE of the block's rows, then their Delta
 };
 
-template <typename T, int D, int VAR, bool CAUSAL>
-__global__ __launch_bounds__(kNT) void attn_dkdv_kernel(const BwdParams p) {
-  using V8 = typename Vec8<T>::type;
-  using St = DkdvStage<T, D, VAR>;
-  using RT = typename St::RT;
-  using TT = typename St::TT;
-  constexpr int KK = D / 16;
-  constexpr int DT = D / 32;
-  constexpr int ST = kQB / 32;
-  constexpr int PT = kQB / 16;
-  constexpr bool kPw = VAR == PW;
-  constexpr int NQ = St::NQ;
+template <typename T, int D, int VAR>
+struct alignas(16) DkdvSmem {
+  using Sh = DkdvShape<D, VAR>;
+  using VTile = DTile<T, 32, D, 1, false>;  // natural key order
+  DkdvStage<T, D, VAR> st[Sh::NS];
+  T v[Sh::WAVES][VTile::ELEMS];
+};
 
-  __shared__ St smem[2];
+template <int D, int VAR>
+constexpr int dkdv_waves_per_eu() {
+  return DkdvShape<D, VAR>::WAVES / 4;
+}
+
+template <typename T, int D, int VAR, bool CAUSAL>
+__global__ __launch_bounds__((DkdvShape<D, VAR>::NT))
+__attribute__((amdgpu_waves_per_eu(dkdv_waves_per_eu<D, VAR>(), dkdv_waves_per_eu<D, VAR>())))
+void attn_dkdv_kernel(const BwdParams p) {
+  using Sh = DkdvShape<D, VAR>;
+  constexpr int kWaves = Sh::WAVES;
+  constexpr int QB = Sh::QB;
+  constexpr int KB = Sh::KB;
+  constexpr int NS = Sh::NS;
+  using V8 = typename Vec8<T>::type;
+  using Sm = DkdvSmem<T, D, VAR>;
+  using St = DkdvStage<T, D, VAR>;
+  using VTile = typename Sm::VTile;
+  using Dma = DmaTile<T, QB, D, kWaves>;
+  constexpr int KK = D / 16;   // 16-wide k steps over the head dim
+  constexpr int DT = D / 32;   // 32-wide d tiles of dK^t / dV^t
+  constexpr int ST = QB / 32;  // 32-query score tiles per block
+  constexpr int PT = QB / 16;  // 16-query operand slices per block
+  constexpr bool kPw = VAR == PW;
+  static_assert(sizeof(Sm) <= kLdsBytes, "LDS budget");
+
+  __shared__ Sm smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 31, h = lane >> 5;
 
   // Heads vary fastest (one head's Q/dO stay in one XCD's L2).  Causal: key
-  // block 0 is seen by every query, so natural order already runs the
-  // longest workgroups first.
+  // block 0 is seen by every query, so natural order runs the longest
+  // workgroups first.
   const int bh = blockIdx.x % p.BH;
   const int kb = blockIdx.x / p.BH;
-  const int n0 = kb * kKB;
+  const int n0 = kb * KB;
   const int kw0 = n0 + 32 * wave;
   const bool wave_valid = kw0 < p.N;
   const int kj = kw0 + li;  // this lane's key
@@ -161,18 +230,15 @@ __global__ __launch_bounds__(kNT) void attn_dkdv_kernel(const BwdParams p) {
   const int64_t kbase = (int64_t)bh * p.N * D;
   const int64_t lbase = (int64_t)bh * p.M;
 
-  const T* Qp = (const T*)p.q + qbase;
-  const T* Q2p = kPw ? (const T*)p.q2 + qbase : nullptr;
-  const T* DOp = (const T*)p.dout + qbase;
-
-  // K and V columns stay in registers: lane li feeds key kj as B operand.
-  V8 kf[KK], k2f[kPw ? KK : 1], vf[KK];
+  // Resident operands: this wave's 32 rows of V in LDS, K (K1, K2) columns
+  // in registers (lane li feeds key kj).
+  V8 kf[KK], k2f[kPw ? KK : 1];
   if (wave_valid) {
+    VTile::load(smem.v[wave], (const T*)p.v + kbase + (int64_t)kw0 * D, 0, lane);
     const int64_t off = kbase + (int64_t)kj * D + 8 * h;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       kf[kk] = *reinterpret_cast<const V8*>((const T*)p.k + off + 16 * kk);
-      vf[kk] = *reinterpret_cast<const V8*>((const T*)p.v + off + 16 * kk);
       if constexpr (kPw) k2f[kk] = *reinterpret_cast<const V8*>((const T*)p.k2 + off + 16 * kk);
     }
   }
@@ -187,184 +253,211 @@ __global__ __launch_bounds__(kNT) void attn_dkdv_kernel(const BwdParams p) {
 
   // Query blocks to visit.
   int q_begin = 0;
-  if (CAUSAL) q_begin = max(0, n0 - pshift) / kQB * kQB;
-  const int nq = p.M > q_begin ? (p.M - q_begin + kQB - 1) / kQB : 0;
-  const int wg_key_hi = min(p.N, n0 + kKB) - 1;
+  if (CAUSAL) q_begin = max(0, n0 - pshift) / QB * QB;
+  const int nq = p.M > q_begin ? (p.M - q_begin + QB - 1) / QB : 0;
+  const int wg_key_hi = min(p.N, n0 + KB) - 1;
 
-  RT ldq[NQ], lddo;
-  TT ldqt[NQ], lddot;
-  float ld_lse = 0.f, ld_delta = 0.f;
-  bool ld_q[2] = {true, true};
+  const T* gq = (const T*)p.q + qbase;
+  const T* gq2 = kPw ? (const T*)p.q2 + qbase : gq;
+  const T* gdo = (const T*)p.dout + qbase;
+  Dma dma;
+  dma.lane_offsets(wave, lane);
 
-  auto issue = [&](int qb) {
-    const int i0 = q_begin + qb * kQB;
+  // LSE / Delta rows of a block: 2 QB floats loaded with 4-byte direct loads,
+  // E of them per wave, so every wave issues exactly one such load.
+  constexpr int E = 2 * QB / kWaves;
+  static_assert(64 % E == 0, "row statistics split");
+  const int st_first = wave * E;
+  const int st_ins = st_first / 64;
+  const bool st_lane = lane >= st_first % 64 && lane < st_first % 64 + E;
+  const int st_elem = st_ins * 64 + lane;
+  const float* st_src = st_elem < QB ? p.lse + lbase + st_elem : p.delta + lbase + (st_elem - QB);
+
+  // Issue the direct loads of query block qb into stage st; returns the
+  // number of vector-memory instructions this wave issued.
+  auto issue = [&](St& st, int qb) -> int {
+    const int i0 = q_begin + qb * QB;
     const int64_t off = (int64_t)i0 * D;
+    int n = Dma::PER_WAVE + 1;
     if constexpr (kPw) {
       bool an, af;
-      pw_classify(i0, i0 + kQB - 1, n0, wg_key_hi, pshift, p.w, an, af);
-      ld_q[0] = !af;
-      ld_q[1] = !an;
-      if (ld_q[0]) {
-        ldq[0].load(Qp + off, tid);
-        ldqt[0].load(Qp + off, tid);
+      pw_classify(i0, i0 + QB - 1, n0, wg_key_hi, pshift, p.w, an, af);
+      if (!af) {
+        dma.load(gq + off, st.q[0], wave);
+        n += Dma::PER_WAVE;
       }
-      if (ld_q[1]) {
-        ldq[1].load(Q2p + off, tid);
-        ldqt[1].load(Q2p + off, tid);
+      if (!an) {
+        dma.load(gq2 + off, st.q[kPw ? 1 : 0], wave);
+        n += Dma::PER_WAVE;
       }
     } else {
-      ldq[0].load(Qp + off, tid);
-      ldqt[0].load(Qp + off, tid);
+      dma.load(gq + off, st.q[0], wave);
+      n += Dma::PER_WAVE;
     }
-    lddo.load(DOp + off, tid);
-    lddot.load(DOp + off, tid);
-    if (tid < kQB) {
-      ld_lse = lse_to_log2(p.lse[lbase + i0 + tid]);
-      ld_delta = p.delta[lbase + i0 + tid];
-    }
+    dma.load(gdo + off, st.dout, wave);
+    if (st_lane)
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(st_src + i0),
+                                       (void __attribute__((address_space(3)))*)(st.stats + st_ins * 64), 4, 0,
+                                       0);
+    return n;
   };
-  auto commit = [&](St& s) {
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      if (!kPw || ld_q[j]) {
-        ldq[j].store(s.qrm[j], tid);
-        ldqt[j].store(s.qtr[j], tid);
-      }
-    }
-    lddo.store(s.dorm, tid);
-    lddot.store(s.dotr, tid);
-    if (tid < kQB) {
-      s.lse2[tid] = ld_lse;
-      s.delta[tid] = ld_delta;
-    }
+  // Wait until the loads of every block but the newest (n instructions)
+  // have landed.
+  auto wait_all_but = [&](int n) {
+    if constexpr (kPw)
+      wait_vmcnt_any<3 * Dma::PER_WAVE + 1, 2 * Dma::PER_WAVE + 1>(n);
+    else
+      wait_vmcnt<2 * Dma::PER_WAVE + 1>();
   };
 
-  if (nq > 0) {
-    issue(0);
-    commit(smem[0]);
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // resident K/V loads and the first block
-  __syncthreads();
+  // Prologue: resident loads, blocks 0 .. NS-2 in flight, block 0 landed.
+  int n_new = 0;
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < nq) n_new = issue(smem.st[j], j);
+  if (nq > 1)
+    wait_all_but(n_new);
+  else
+    wait_vmcnt0();
+  lds_barrier();
+
+  // Loop-invariant LDS byte offsets.  Row reads: row li, chunk 2 kk + h of a
+  // Q/dO tile (swap23 rows) or of this wave's V tile (natural rows).
+  uint32_t rofs[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) rofs[kk] = row_chunk_ofs<D>(li, 2 * kk + h);
+  const TrLane tl(lane);
+  uint32_t tofs[DT][2];
+  tr_offsets<D>(tl, tofs);
+  auto rd8 = [&](const T* tile, int st, int kk) -> V8 {
+    return *reinterpret_cast<const V8*>(reinterpret_cast<const char*>(tile) + rofs[kk] + st * 32 * D * 2);
+  };
+  const T* vres = smem.v[wave];
 
   // One query block for this wave; MASK selects the causal-diagonal path.
+  // Rows with LSE = -inf (no visible key) only occur in causal blocks whose
+  // every pair is masked, where P is set to 0 after the exponent.
+  const float neg_inv_scale = -1.f / p.sm_scale;
   auto block = [&](const St& cur, int i0, auto mask_tag) {
-      constexpr bool need_mask = decltype(mask_tag)::value;
-      bool an = true, af = false;
-      if constexpr (kPw) pw_classify(i0, i0 + kQB - 1, kw0, kw0 + 31, pshift, p.w, an, af);
-      f32x16 s[ST], dp[ST], dsf[kPw ? ST : 1];
+    constexpr bool MASK = decltype(mask_tag)::value;
+    bool an = true, af = false;
+    if constexpr (kPw) pw_classify(i0, i0 + QB - 1, kw0, kw0 + 31, pshift, p.w, an, af);
+    f32x16 s[ST], dp[ST], dsf[kPw ? ST : 1];
 #pragma unroll
-      for (int st = 0; st < ST; ++st) {
-        const int roff = (32 * st + li);
-        // scores S = Q K^t (rows: queries, swap23 order; column: this key)
+    for (int st = 0; st < ST; ++st) {
+      // The score accumulator starts at -LSE / sm_scale and the dP one at
+      // -Delta (this lane's 16 rows), so that scale2 * S is the exponent of P
+      // and dP - Delta comes out of the product.
+      f32x16 sinit, dinit;
+      {
+        const f32x4* l4 = reinterpret_cast<const f32x4*>(cur.stats + 32 * st + 8 * h);
+        const f32x4* d4 = reinterpret_cast<const f32x4*>(cur.stats + QB + 32 * st + 8 * h);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 lv = l4[(g & 1) + 4 * (g >> 1)];
+          const f32x4 dv = d4[(g & 1) + 4 * (g >> 1)];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sinit[4 * g + e] = lv[e] * neg_inv_scale;
+            dinit[4 * g + e] = -dv[e];
+          }
+        }
+      }
+      // scores S = Q K^t (rows: queries in swap23 order; column: this key)
+      if constexpr (kPw) {
+        f32x16 s1 = sinit, s2 = sinit;
+        if (!af) {
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) s1 = mfma32x32x16(rd8(cur.q[0], st, kk), kf[kk], s1);
+        }
+        if (!an) {
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) s2 = mfma32x32x16(rd8(cur.q[kPw ? 1 : 0], st, kk), k2f[kk], s2);
+        }
+        if (an) {
+          s[st] = s1;
+        } else if (af) {
+          s[st] = s2;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = i0 + 32 * st + perm_row(r, h);
+            s[st][r] = pw_near(row + pshift - kj, p.w) ? s1[r] : s2[r];
+          }
+        }
+      } else {
+        s[st] = sinit;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) s[st] = mfma32x32x16(rd8(cur.q[0], st, kk), kf[kk], s[st]);
+      }
+      // dP - Delta = dO V^t - Delta
+      dp[st] = dinit;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) dp[st] = mfma32x32x16(rd8(cur.dout, st, kk), rd8(vres, 0, kk), dp[st]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pv = exp2_fast(s[st][r] * p.scale2);
+        if constexpr (MASK) {
+          const int row = i0 + 32 * st + perm_row(r, h);
+          if (kj > row + pshift) pv = 0.f;
+        }
+        const float ds = pv * dp[st][r];
+        s[st][r] = pv;
         if constexpr (kPw) {
-          f32x16 s1 = zero16(), s2 = zero16();
-          if (!af) {
-            const T* qrow = cur.qrm[0] + roff * RT::PITCH + 8 * h;
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) s1 = mfma32x32x16(lds_read8(qrow + 16 * kk), kf[kk], s1);
-          }
-          if (!an) {
-            const T* qrow = cur.qrm[1] + roff * RT::PITCH + 8 * h;
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) s2 = mfma32x32x16(lds_read8(qrow + 16 * kk), k2f[kk], s2);
-          }
           if (an) {
-            s[st] = s1;
+            dp[st][r] = ds;
           } else if (af) {
-            s[st] = s2;
+            dp[st][r] = 0.f;
+            dsf[st][r] = ds;
           } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int qrow_i = i0 + 32 * st + perm_row(r, h);
-              s[st][r] = pw_near(qrow_i + pshift - kj, p.w) ? s1[r] : s2[r];
-            }
+            const int row = i0 + 32 * st + perm_row(r, h);
+            const bool nr = pw_near(row + pshift - kj, p.w);
+            dp[st][r] = nr ? ds : 0.f;
+            dsf[st][r] = nr ? 0.f : ds;
           }
         } else {
-          s[st] = zero16();
-          const T* qrow = cur.qrm[0] + roff * RT::PITCH + 8 * h;
-#pragma unroll
-          for (int kk = 0; kk < KK; ++kk) s[st] = mfma32x32x16(lds_read8(qrow + 16 * kk), kf[kk], s[st]);
-        }
-        // dP = dO V^t
-        dp[st] = zero16();
-        const T* dorow = cur.dorm + roff * RT::PITCH + 8 * h;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) dp[st] = mfma32x32x16(lds_read8(dorow + 16 * kk), vf[kk], dp[st]);
-        // P and dS
-        const f32x4* l4 = reinterpret_cast<const f32x4*>(cur.lse2 + 32 * st + 8 * h);
-        const f32x4* d4 = reinterpret_cast<const f32x4*>(cur.delta + 32 * st + 8 * h);
-        f32x4 lv[4] = {l4[0], l4[1], l4[4], l4[5]};
-        f32x4 dv4[4] = {d4[0], d4[1], d4[4], d4[5]};
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float l2 = lv[r >> 2][r & 3];
-          const float dl = dv4[r >> 2][r & 3];
-          float pv = exp2_fast(fmaf(s[st][r], p.scale2, -l2));
-          if constexpr (need_mask) {
-            const int qrow_i = i0 + 32 * st + perm_row(r, h);
-            if (kj > qrow_i + pshift) pv = 0.f;
-          }
-          const float ds = pv * (dp[st][r] - dl);
-          s[st][r] = pv;
-          if constexpr (kPw) {
-            if (an) {
-              dp[st][r] = ds;
-            } else if (af) {
-              dp[st][r] = 0.f;
-              dsf[st][r] = ds;
-            } else {
-              const int qrow_i = i0 + 32 * st + perm_row(r, h);
-              const bool nr = pw_near(qrow_i + pshift - kj, p.w);
-              dp[st][r] = nr ? ds : 0.f;
-              dsf[st][r] = nr ? 0.f : ds;
-            }
-          } else {
-            dp[st][r] = ds;
-          }
+          dp[st][r] = ds;
         }
       }
-      // dV^t += dO^t P ;  dK^t += Q^t dS
-      V8 pb[PT], dsb[PT], dsfb[kPw ? PT : 1];
+    }
+    V8 pb[PT], dsb[PT], dsfb[kPw ? PT : 1];
 #pragma unroll
-      for (int t = 0; t < PT; ++t) {
-        pb[t] = pack8<T>(s[t >> 1], 8 * (t & 1));
-        if (!kPw || !af) dsb[t] = pack8<T>(dp[t >> 1], 8 * (t & 1));
-        if constexpr (kPw) {
-          if (!an) dsfb[t] = pack8<T>(dsf[t >> 1], 8 * (t & 1));
-        }
-      }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const T* dotrow = cur.dotr + (32 * dt + li) * TT::PITCH + 8 * h;
-#pragma unroll
-        for (int t = 0; t < PT; ++t) dvt[dt] = mfma32x32x16(lds_read8(dotrow + 16 * t), pb[t], dvt[dt]);
-        if (!kPw || !af) {
-          const T* qtrow = cur.qtr[0] + (32 * dt + li) * TT::PITCH + 8 * h;
-#pragma unroll
-          for (int t = 0; t < PT; ++t) dkt[dt] = mfma32x32x16(lds_read8(qtrow + 16 * t), dsb[t], dkt[dt]);
-        }
-        if constexpr (kPw) {
-          if (!an) {
-            const T* qtrow = cur.qtr[1] + (32 * dt + li) * TT::PITCH + 8 * h;
-#pragma unroll
-            for (int t = 0; t < PT; ++t) dk2t[dt] = mfma32x32x16(lds_read8(qtrow + 16 * t), dsfb[t], dk2t[dt]);
-          }
-        }
-      }
+    for (int t = 0; t < PT; ++t) {
+      pb[t] = pack8<T>(s[t >> 1], 8 * (t & 1));
+      dsb[t] = pack8<T>(dp[t >> 1], 8 * (t & 1));
+      if constexpr (kPw) dsfb[t] = pack8<T>(dsf[t >> 1], 8 * (t & 1));
+    }
+    // dV^t += dO^t P ;  dK^t += Q^t dS  (dK2^t += Q2^t dS_far)
+    accum_tr<T, D, PT>(dvt, lds_addr(cur.dout), tofs, pb);
+    if (!kPw || !af) accum_tr<T, D, PT>(dkt, lds_addr(cur.q[0]), tofs, dsb);
+    if constexpr (kPw) {
+      if (!an) accum_tr<T, D, PT>(dk2t, lds_addr(cur.q[kPw ? 1 : 0]), tofs, dsfb);
+    }
   };
 
+  // Block qb is computed from stage qb % NS while block qb + NS - 1 is being
+  // loaded into the stage freed by block qb - 1.
+  int cur_stage = 0;
   for (int qb = 0; qb < nq; ++qb) {
-    const St& cur = smem[qb & 1];
-    if (qb + 1 < nq) issue(qb + 1);
-    const int i0 = q_begin + qb * kQB;
-    if (wave_valid && (!CAUSAL || i0 + kQB - 1 + pshift >= kw0)) {
-      if (CAUSAL && (i0 + pshift < kw0 + 31))
-        block(cur, i0, std::true_type{});
+    const int ahead = qb + NS - 1;
+    int ld_stage = cur_stage + NS - 1;
+    if (ld_stage >= NS) ld_stage -= NS;
+    const bool issued = ahead < nq;
+    if (issued) n_new = issue(smem.st[ld_stage], ahead);
+    const int i0 = q_begin + qb * QB;
+    const bool active = wave_valid && (!CAUSAL || i0 + QB - 1 + pshift >= kw0);
+    if (active) {
+      if (CAUSAL && (kw0 + 31 > i0 + pshift))
+        block(smem.st[cur_stage], i0, std::true_type{});
       else
-        block(cur, i0, std::false_type{});
+        block(smem.st[cur_stage], i0, std::false_type{});
     }
-    if (qb + 1 < nq) commit(smem[(qb + 1) & 1]);
-    __syncthreads();
+    if (issued)
+      wait_all_but(n_new);
+    else
+      wait_vmcnt0();
+    lds_barrier();
+    cur_stage = (cur_stage + 1 == NS) ? 0 : cur_stage + 1;
   }
 
   if (!wave_valid) return;
@@ -377,50 +470,62 @@ __global__ __launch_bounds__(kNT) void attn_dkdv_kernel(const BwdParams p) {
   }
 }
 
-// ---------------------------------------------------------------- dQ pass --
-constexpr int kQW = 32 * kWaves;  // queries per workgroup
-
+// =============================================================== dQ pass ==
 template <int D, int VAR>
-struct DqCfg {
-  // keys per streamed block; the piecewise D=128 stage is halved to fit LDS
-  static constexpr int BN = (VAR == PW && D == 128) ? 32 : 64;
+struct DqShape {
+  static constexpr int WAVES = (VAR == PW) ? 4 : 8;
+  static constexpr int NT = 64 * WAVES;
+  static constexpr int BM = 32 * WAVES;  // queries per workgroup
+  static constexpr int BN = 64;          // keys per streamed block
 };
 
 template <typename T, int D, int VAR>
 struct alignas(16) DqStage {
-  static constexpr int BN = DqCfg<D, VAR>::BN;
-  using RT = RowTile<T, BN, D, kNT>;
-  using TT = TransTile<T, BN, D, kNT>;
+  using Tile = DTile<T, DqShape<D, VAR>::BN, D, DqShape<D, VAR>::WAVES>;
   static constexpr int NK = (VAR == PW) ? 2 : 1;
-  T krm[NK][RT::ELEMS];
-  T vrm[RT::ELEMS];
-  T ktr[NK][TT::ELEMS];
+  T k[NK][Tile::ELEMS];   // K (piecewise: K1, K2)
+  T v[Tile::ELEMS];
 };
 
+template <typename T, int D, int VAR>
+constexpr int dq_stages() {
+  return 3 * (int)sizeof(DqStage<T, D, VAR>) <= kLdsBytes ? 3 : 2;
+}
+
+template <int D, int VAR>
+constexpr int dq_waves_per_eu() {
+  return DqShape<D, VAR>::WAVES / 4;
+}
+
 template <typename T, int D, int VAR, bool CAUSAL>
-__global__ __launch_bounds__(kNT) void attn_dq_kernel(const BwdParams p) {
+__global__ __launch_bounds__((DqShape<D, VAR>::NT))
+__attribute__((amdgpu_waves_per_eu(dq_waves_per_eu<D, VAR>(), dq_waves_per_eu<D, VAR>())))
+void attn_dq_kernel(const BwdParams p) {
+  using Sh = DqShape<D, VAR>;
+  constexpr int kWaves = Sh::WAVES;
+  constexpr int BM = Sh::BM;
+  constexpr int BN = Sh::BN;
+  constexpr int NS = dq_stages<T, D, VAR>();
   using V8 = typename Vec8<T>::type;
   using St = DqStage<T, D, VAR>;
-  using RT = typename St::RT;
-  using TT = typename St::TT;
-  constexpr int BN = St::BN;
+  using Dma = DmaTile<T, BN, D, kWaves>;
   constexpr int KK = D / 16;
   constexpr int DT = D / 32;
   constexpr int ST = BN / 32;
   constexpr int PT = BN / 16;
   constexpr bool kPw = VAR == PW;
-  constexpr int NK = St::NK;
 
-  __shared__ St smem[2];
+  __shared__ St smem[NS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int li = lane & 31, h = lane >> 5;
 
+  // Heads vary fastest; causal: the longest query blocks (last rows) first.
   const int bh = blockIdx.x % p.BH;
   int mb = blockIdx.x / p.BH;
   if (CAUSAL) mb = p.nblk - 1 - mb;
-  const int m0 = mb * kQW;
+  const int m0 = mb * BM;
   const int row0 = m0 + 32 * wave;
   const bool wave_valid = row0 < p.M;
   const int qi = row0 + li;
@@ -428,10 +533,13 @@ __global__ __launch_bounds__(kNT) void attn_dq_kernel(const BwdParams p) {
   const int64_t qbase = (int64_t)bh * p.M * D;
   const int64_t kbase = (int64_t)bh * p.N * D;
 
-  const T* Kp = (const T*)p.k + kbase;
-  const T* K2p = kPw ? (const T*)p.k2 + kbase : nullptr;
-  const T* Vp = (const T*)p.v + kbase;
+  const T* gk = (const T*)p.k + kbase;
+  const T* gk2 = kPw ? (const T*)p.k2 + kbase : gk;
+  const T* gv = (const T*)p.v + kbase;
+  Dma dma;
+  dma.lane_offsets(wave, lane);
 
+  // Query-side operands stay in registers for the whole pass.
   V8 qf[KK], q2f[kPw ? KK : 1], dof[KK];
   float lse2 = __builtin_huge_valf(), dl = 0.f;
   if (wave_valid) {
@@ -453,157 +561,162 @@ __global__ __launch_bounds__(kNT) void attn_dq_kernel(const BwdParams p) {
     if constexpr (kPw) dq2t[dt] = zero16();
   }
 
-  const int wg_last_row = min(p.M, m0 + kQW) - 1;
+  const int wg_last_row = min(p.M, m0 + BM) - 1;
   int n_end = p.N;
   if (CAUSAL) n_end = min(p.N, wg_last_row + pshift + 1);
   const int nkb = n_end > 0 ? (n_end + BN - 1) / BN : 0;
 
-  RT ldk[NK], ldv;
-  TT ldkt[NK];
-  bool ld_k[2] = {true, true};
-
-  auto issue = [&](int jb) {
+  auto issue = [&](St& st, int jb) -> int {
     const int64_t off = (int64_t)jb * BN * D;
+    int n = Dma::PER_WAVE;
     if constexpr (kPw) {
       bool an, af;
       pw_classify(m0, wg_last_row, jb * BN, jb * BN + BN - 1, pshift, p.w, an, af);
-      ld_k[0] = !af;
-      ld_k[1] = !an;
-      if (ld_k[0]) {
-        ldk[0].load(Kp + off, tid);
-        ldkt[0].load(Kp + off, tid);
+      if (!af) {
+        dma.load(gk + off, st.k[0], wave);
+        n += Dma::PER_WAVE;
       }
-      if (ld_k[1]) {
-        ldk[1].load(K2p + off, tid);
-        ldkt[1].load(K2p + off, tid);
+      if (!an) {
+        dma.load(gk2 + off, st.k[kPw ? 1 : 0], wave);
+        n += Dma::PER_WAVE;
       }
     } else {
-      ldk[0].load(Kp + off, tid);
-      ldkt[0].load(Kp + off, tid);
+      dma.load(gk + off, st.k[0], wave);
+      n += Dma::PER_WAVE;
     }
-    ldv.load(Vp + off, tid);
+    dma.load(gv + off, st.v, wave);
+    return n;
   };
-  auto commit = [&](St& s) {
-#pragma unroll
-    for (int j = 0; j < NK; ++j) {
-      if (!kPw || ld_k[j]) {
-        ldk[j].store(s.krm[j], tid);
-        ldkt[j].store(s.ktr[j], tid);
-      }
-    }
-    ldv.store(s.vrm, tid);
+  auto wait_all_but = [&](int n) {
+    if constexpr (kPw)
+      wait_vmcnt_any<3 * Dma::PER_WAVE, 2 * Dma::PER_WAVE>(n);
+    else
+      wait_vmcnt<2 * Dma::PER_WAVE>();
   };
 
-  if (nkb > 0) {
-    issue(0);
-    commit(smem[0]);
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // resident Q/dO loads and the first block
-  __syncthreads();
+  // Prologue: the query operands have landed; blocks 0 .. NS-2 are in
+  // flight and block 0 has landed.
+  wait_vmcnt0();
+  int n_new = 0;
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < nkb) n_new = issue(smem[j], j);
+  if (NS == 3 && nkb > 1)
+    wait_all_but(n_new);
+  else
+    wait_vmcnt0();
+  lds_barrier();
+
+  uint32_t rofs[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) rofs[kk] = row_chunk_ofs<D>(li, 2 * kk + h);
+  const TrLane tl(lane);
+  uint32_t tofs[DT][2];
+  tr_offsets<D>(tl, tofs);
+  auto rd8 = [&](const T* tile, int st, int kk) -> V8 {
+    return *reinterpret_cast<const V8*>(reinterpret_cast<const char*>(tile) + rofs[kk] + st * 32 * D * 2);
+  };
 
   // One key block for this wave; MASK selects the causal-diagonal path.
   auto block = [&](const St& cur, int n0, auto mask_tag) {
-      constexpr bool need_mask = decltype(mask_tag)::value;
-      bool an = true, af = false;
-      if constexpr (kPw) pw_classify(row0, row0 + 31, n0, n0 + BN - 1, pshift, p.w, an, af);
-      f32x16 s[ST], dp[ST], dsf[kPw ? ST : 1];
+    constexpr bool MASK = decltype(mask_tag)::value;
+    bool an = true, af = false;
+    if constexpr (kPw) pw_classify(row0, row0 + 31, n0, n0 + BN - 1, pshift, p.w, an, af);
+    V8 dsb[PT], dsfb[kPw ? PT : 1];
 #pragma unroll
-      for (int st = 0; st < ST; ++st) {
-        const int roff = 32 * st + li;
+    for (int st = 0; st < ST; ++st) {
+      // S^t = K Q^t (rows: keys in swap23 order; column: this query)
+      f32x16 s;
+      if constexpr (kPw) {
+        f32x16 s1 = zero16(), s2 = zero16();
+        if (!af) {
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) s1 = mfma32x32x16(rd8(cur.k[0], st, kk), qf[kk], s1);
+        }
+        if (!an) {
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) s2 = mfma32x32x16(rd8(cur.k[kPw ? 1 : 0], st, kk), q2f[kk], s2);
+        }
+        if (an) {
+          s = s1;
+        } else if (af) {
+          s = s2;
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = n0 + 32 * st + perm_row(r, h);
+            s[r] = pw_near(qi + pshift - key, p.w) ? s1[r] : s2[r];
+          }
+        }
+      } else {
+        s = zero16();
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) s = mfma32x32x16(rd8(cur.k[0], st, kk), qf[kk], s);
+      }
+      // dP^t = V dO^t
+      f32x16 dp = zero16();
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) dp = mfma32x32x16(rd8(cur.v, st, kk), dof[kk], dp);
+      f32x16 dsf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pv = exp2_fast(fmaf(s[r], p.scale2, -lse2));
+        if constexpr (MASK) {
+          const int key = n0 + 32 * st + perm_row(r, h);
+          if (key > qi + pshift) pv = 0.f;
+        }
+        const float ds = pv * (dp[r] - dl);
         if constexpr (kPw) {
-          f32x16 s1 = zero16(), s2 = zero16();
-          if (!af) {
-            const T* krow = cur.krm[0] + roff * RT::PITCH + 8 * h;
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) s1 = mfma32x32x16(lds_read8(krow + 16 * kk), qf[kk], s1);
-          }
-          if (!an) {
-            const T* krow = cur.krm[1] + roff * RT::PITCH + 8 * h;
-#pragma unroll
-            for (int kk = 0; kk < KK; ++kk) s2 = mfma32x32x16(lds_read8(krow + 16 * kk), q2f[kk], s2);
-          }
           if (an) {
-            s[st] = s1;
+            dp[r] = ds;
           } else if (af) {
-            s[st] = s2;
+            dp[r] = 0.f;
+            dsf[r] = ds;
           } else {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = n0 + 32 * st + perm_row(r, h);
-              s[st][r] = pw_near(qi + pshift - key, p.w) ? s1[r] : s2[r];
-            }
+            const int key = n0 + 32 * st + perm_row(r, h);
+            const bool nr = pw_near(qi + pshift - key, p.w);
+            dp[r] = nr ? ds : 0.f;
+            dsf[r] = nr ? 0.f : ds;
           }
         } else {
-          s[st] = zero16();
-          const T* krow = cur.krm[0] + roff * RT::PITCH + 8 * h;
-#pragma unroll
-          for (int kk = 0; kk < KK; ++kk) s[st] = mfma32x32x16(lds_read8(krow + 16 * kk), qf[kk], s[st]);
-        }
-        dp[st] = zero16();
-        const T* vrow = cur.vrm + roff * RT::PITCH + 8 * h;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) dp[st] = mfma32x32x16(lds_read8(vrow + 16 * kk), dof[kk], dp[st]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = n0 + 32 * st + perm_row(r, h);
-          float pv = exp2_fast(fmaf(s[st][r], p.scale2, -lse2));
-          if constexpr (need_mask) {
-            if (key > qi + pshift) pv = 0.f;
-          }
-          const float ds = pv * (dp[st][r] - dl);
-          if constexpr (kPw) {
-            if (an) {
-              dp[st][r] = ds;
-            } else if (af) {
-              dp[st][r] = 0.f;
-              dsf[st][r] = ds;
-            } else {
-              const bool nr = pw_near(qi + pshift - key, p.w);
-              dp[st][r] = nr ? ds : 0.f;
-              dsf[st][r] = nr ? 0.f : ds;
-            }
-          } else {
-            dp[st][r] = ds;
-          }
+          dp[r] = ds;
         }
       }
-      V8 dsb[PT], dsfb[kPw ? PT : 1];
-#pragma unroll
-      for (int t = 0; t < PT; ++t) {
-        if (!kPw || !af) dsb[t] = pack8<T>(dp[t >> 1], 8 * (t & 1));
-        if constexpr (kPw) {
-          if (!an) dsfb[t] = pack8<T>(dsf[t >> 1], 8 * (t & 1));
-        }
+      dsb[2 * st] = pack8<T>(dp, 0);
+      dsb[2 * st + 1] = pack8<T>(dp, 8);
+      if constexpr (kPw) {
+        dsfb[2 * st] = pack8<T>(dsf, 0);
+        dsfb[2 * st + 1] = pack8<T>(dsf, 8);
       }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        if (!kPw || !af) {
-          const T* ktrow = cur.ktr[0] + (32 * dt + li) * TT::PITCH + 8 * h;
-#pragma unroll
-          for (int t = 0; t < PT; ++t) dqt[dt] = mfma32x32x16(lds_read8(ktrow + 16 * t), dsb[t], dqt[dt]);
-        }
-        if constexpr (kPw) {
-          if (!an) {
-            const T* ktrow = cur.ktr[1] + (32 * dt + li) * TT::PITCH + 8 * h;
-#pragma unroll
-            for (int t = 0; t < PT; ++t) dq2t[dt] = mfma32x32x16(lds_read8(ktrow + 16 * t), dsfb[t], dq2t[dt]);
-          }
-        }
-      }
+    }
+    // dQ^t += K^t dS^t  (dQ2^t += K2^t dS_far^t)
+    if (!kPw || !af) accum_tr<T, D, PT>(dqt, lds_addr(cur.k[0]), tofs, dsb);
+    if constexpr (kPw) {
+      if (!an) accum_tr<T, D, PT>(dq2t, lds_addr(cur.k[kPw ? 1 : 0]), tofs, dsfb);
+    }
   };
 
+  int cur_stage = 0;
   for (int jb = 0; jb < nkb; ++jb) {
-    const St& cur = smem[jb & 1];
-    if (jb + 1 < nkb) issue(jb + 1);
+    const int ahead = jb + NS - 1;
+    int ld_stage = cur_stage + NS - 1;
+    if (ld_stage >= NS) ld_stage -= NS;
+    const bool issued = ahead < nkb;
+    if (issued) n_new = issue(smem[ld_stage], ahead);
     const int n0 = jb * BN;
-    if (wave_valid && (!CAUSAL || n0 <= row0 + 31 + pshift)) {
+    const bool active = wave_valid && (!CAUSAL || n0 <= row0 + 31 + pshift);
+    if (active) {
       if (CAUSAL && (n0 + BN - 1 > row0 + pshift))
-        block(cur, n0, std::true_type{});
+        block(smem[cur_stage], n0, std::true_type{});
       else
-        block(cur, n0, std::false_type{});
+        block(smem[cur_stage], n0, std::false_type{});
     }
-    if (jb + 1 < nkb) commit(smem[(jb + 1) & 1]);
-    __syncthreads();
+    if (NS == 3 && issued)
+      wait_all_but(n_new);
+    else
+      wait_vmcnt0();
+    lds_barrier();
+    cur_stage = (cur_stage + 1 == NS) ? 0 : cur_stage + 1;
   }
 
   if (!wave_valid) return;
@@ -642,9 +755,10 @@ BwdParams make_params(const BwdArgs& a) {
 
 template <typename T, int D, int VAR>
 hipError_t dkdv_t(const BwdArgs& a, hipStream_t s) {
+  using Sh = DkdvShape<D, VAR>;
   BwdParams p = make_params(a);
-  p.nblk = (a.N + kKB - 1) / kKB;
-  dim3 grid(p.nblk * p.BH), block(kNT);
+  p.nblk = (a.N + Sh::KB - 1) / Sh::KB;
+  dim3 grid(p.nblk * p.BH), block(Sh::NT);
   if (a.causal)
     hipLaunchKernelGGL((attn_dkdv_kernel<T, D, VAR, true>), grid, block, 0, s, p);
   else
@@ -654,9 +768,10 @@ hipError_t dkdv_t(const BwdArgs& a, hipStream_t s) {
 
 template <typename T, int D, int VAR>
 hipError_t dq_t(const BwdArgs& a, hipStream_t s) {
+  using Sh = DqShape<D, VAR>;
   BwdParams p = make_params(a);
-  p.nblk = (a.M + kQW - 1) / kQW;
-  dim3 grid(p.nblk * p.BH), block(kNT);
+  p.nblk = (a.M + Sh::BM - 1) / Sh::BM;
+  dim3 grid(p.nblk * p.BH), block(Sh::NT);
   if (a.causal)
     hipLaunchKernelGGL((attn_dq_kernel<T, D, VAR, true>), grid, block, 0, s, p);
   else

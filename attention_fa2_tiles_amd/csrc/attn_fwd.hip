@@ -9,9 +9,10 @@
 // ENABLE_JVP path; the piecewise variant takes its scores from (q1, k1) or
 // (q2, k2) by query-key distance (FlagAttention piecewise.py, _fwd_kernel).
 //
-// How it maps to CDNA4: 4 waves per workgroup, 32 query rows per wave
-// (BM = 128), K/V blocks of 64 keys double-buffered in LDS and filled by
-// direct global -> LDS loads (no staging registers).  Scores are formed
+// How it maps to CDNA4: 8 waves per workgroup (4 for the JVP variant at
+// D = 128), 32 query rows per wave, K/V blocks of 64 keys streamed through a
+// three-stage LDS ring (two blocks prefetched) filled by direct global -> LDS
+// loads (no staging registers).  Scores are formed
 // transposed, S^t = K Q^t, so that each lane owns one query row: row max and
 // row sum are in-lane reductions plus one exchange with the other half-wave,
 // and the rescale of the output accumulator is lane-local because that
@@ -189,31 +190,50 @@ void attn_fwd_kernel(const FwdParams p) {
     all_far = (p.w < 0) || (dmin > p.w) || (dmax < -p.w);
   };
 
-  // Issue the direct loads of K/V block jb into stage st (completion: vmcnt).
-  auto issue = [&](St& st, int jb) {
+  // Issue the direct loads of K/V block jb into stage st (completion:
+  // vmcnt); returns the number of load instructions this wave issued.
+  constexpr int kTileLoads = DmaTile<T, kBN, D, kWaves>::PER_WAVE;
+  auto issue = [&](St& st, int jb) -> int {
     const int64_t off = (int64_t)jb * kBN * D;
+    int n = kTileLoads * St::NV;
     if constexpr (kPw) {
       bool an, af;
       pw_class(m0, wg_last_row, jb * kBN, an, af);
-      if (!af) dma.load(gk + off, st.k[0], wave);
-      if (!an) dma.load(gk2 + off, st.k[1], wave);
+      if (!af) {
+        dma.load(gk + off, st.k[0], wave);
+        n += kTileLoads;
+      }
+      if (!an) {
+        dma.load(gk2 + off, st.k[1], wave);
+        n += kTileLoads;
+      }
     } else {
       dma.load(gk + off, st.k[0], wave);
       if constexpr (kJvp) dma.load(gk2 + off, st.k[1], wave);
+      n += kTileLoads * St::NK;
     }
     dma.load(gv + off, st.v[0], wave);
     if constexpr (kJvp) dma.load(gv2 + off, st.v[1], wave);
+    return n;
+  };
+  // Wait until every load but the newest n (one block's) has landed; loads
+  // complete in issue order.  A piecewise block may skip one K tile.
+  auto wait_all_but = [&](int n) {
+    if constexpr (kPw)
+      wait_vmcnt_any<3 * kTileLoads, 2 * kTileLoads>(n);
+    else
+      wait_vmcnt<kTileLoads * (St::NK + St::NV)>();
   };
 
   // Prologue: the query operands have landed; blocks 0 .. NS-2 are in
-  // flight and block 0 has landed (loads complete in issue order).
-  constexpr int kLoadsPerBlock = DmaTile<T, kBN, D, kWaves>::PER_WAVE * (St::NK + St::NV);
+  // flight and block 0 has landed.
   wait_vmcnt0();
+  int n_new = 0;
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
-    if (j < nblk) issue(smem[j], j);
+    if (j < nblk) n_new = issue(smem[j], j);
   if (NS == 3 && nblk > 1)
-    wait_vmcnt<kLoadsPerBlock>();
+    wait_all_but(n_new);
   else
     wait_vmcnt0();
   lds_barrier();
@@ -388,7 +408,7 @@ void attn_fwd_kernel(const FwdParams p) {
     int ld_stage = cur_stage + NS - 1;
     if (ld_stage >= NS) ld_stage -= NS;
     const bool issued = ahead < nblk;
-    if (issued) issue(smem[ld_stage], ahead);
+    if (issued) n_new = issue(smem[ld_stage], ahead);
     const int n0 = jb * kBN;
     const bool active = wave_valid && (!CAUSAL || n0 <= row0 + 31 + pshift);
     if (active) {
@@ -398,7 +418,7 @@ void attn_fwd_kernel(const FwdParams p) {
         block(smem[cur_stage], n0, std::false_type{});
     }
     if (NS == 3 && issued)
-      wait_vmcnt<kLoadsPerBlock>();
+      wait_all_but(n_new);
     else
       wait_vmcnt0();
     lds_barrier();

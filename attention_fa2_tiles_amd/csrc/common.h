@@ -71,6 +71,22 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_vmcnt0() { wait_vmcnt<0>(); }
 
+// Wait until at most n vector-memory operations of this wave are
+// outstanding, where n (wave-uniform) is one of the listed counts.  List the
+// counts in decreasing order: a value matching none of them waits for the
+// last (smallest), which is always safe.
+template <int A, int... Rest>
+__device__ __forceinline__ void wait_vmcnt_any(int n) {
+  if constexpr (sizeof...(Rest) == 0) {
+    wait_vmcnt<A>();
+  } else {
+    if (n == A)
+      wait_vmcnt<A>();
+    else
+      wait_vmcnt_any<Rest...>(n);
+  }
+}
+
 // Workgroup barrier without the release/acquire fences of __syncthreads():
 // those make the compiler wait for every outstanding load (including the
 // direct LDS loads of stages still being prefetched) before the barrier.
@@ -87,7 +103,7 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
-__device__ __forceinline__ int swap23(int r) {
+__device__ __forceinline__ constexpr int swap23(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
@@ -199,8 +215,8 @@ struct TransTile {
 // 16 bytes: lane l's 16 bytes land at the instruction's LDS base + 16 * l).
 //
 // A tile holds R rows of D 2-byte elements, row-major with no padding.  LDS
-// row m holds global row swap23(m) of the tile, and 16-byte chunk c of LDS
-// row m sits at chunk slot c ^ swz<D>(m).  The XOR pattern makes both ways
+// row m holds global row swap23(m) of the tile (global row m when PERM is
+// false), and 16-byte chunk c of LDS row m sits at chunk slot c ^ swz<D>(m).  The XOR pattern makes both ways
 // the kernels read a tile free of bank conflicts:
 //  * row reads (ds_read_b128): 16 lanes read one chunk of 16 consecutive
 //    rows -> 16 distinct 16-byte slots of the 256-byte bank window;
@@ -217,7 +233,9 @@ __device__ __forceinline__ int swz(int m) {
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-template <typename T, int R, int D, int NW>
+__device__ __forceinline__ constexpr int tile_row(int m, bool perm) { return perm ? swap23(m) : m; }
+
+template <typename T, int R, int D, int NW, bool PERM = true>
 struct DTile {
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
   static constexpr int ROWS_PER_INSTR = 64 / CPR;   // rows per wave instruction
@@ -234,7 +252,7 @@ struct DTile {
       const int ins = wave * PER_WAVE + j;
       const int p = ins * 64 + lane;
       const int m = p / CPR, slot = p % CPR;
-      const T* src = g + swap23(m) * D + ((slot ^ swz<D>(m)) * 8);
+      const T* src = g + tile_row(m, PERM) * D + ((slot ^ swz<D>(m)) * 8);
       __builtin_amdgcn_global_load_lds(
           (const void __attribute__((address_space(1)))*)src,
           (void __attribute__((address_space(3)))*)(lds + ins * 512), 16, 0, 0);
@@ -251,9 +269,9 @@ struct DTile {
 // inside the tile (computed once by lane_offsets): a tile is issued from a
 // uniform base pointer plus those 32-bit offsets, which the compiler can
 // encode with a scalar base register, so issuing costs no vector arithmetic.
-template <typename T, int R, int D, int NW>
+template <typename T, int R, int D, int NW, bool PERM = true>
 struct DmaTile {
-  using Tile = DTile<T, R, D, NW>;
+  using Tile = DTile<T, R, D, NW, PERM>;
   static constexpr int PER_WAVE = Tile::PER_WAVE;
   uint32_t voff[PER_WAVE];
 
@@ -263,7 +281,7 @@ struct DmaTile {
       const int ins = wave * PER_WAVE + j;
       const int p = ins * 64 + lane;
       const int m = p / Tile::CPR, slot = p % Tile::CPR;
-      voff[j] = (uint32_t)((swap23(m) * D + ((slot ^ swz<D>(m)) * 8)) * 2);
+      voff[j] = (uint32_t)((tile_row(m, PERM) * D + ((slot ^ swz<D>(m)) * 8)) * 2);
     }
   }
   // Load the tile whose first row is at g (row stride D) into lds.
