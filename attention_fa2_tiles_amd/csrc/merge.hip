@@ -11,17 +11,20 @@
 //   gx  = b gy + gl1 (rho q - (x.q) rho^3 x / D),   gq = sum_rows gl1 rho x
 //
 // CDNA4 mapping: the merge is bandwidth-bound (about one flop per byte), so
-// there is no MFMA.  One wavefront owns one row at a time; each lane holds
-// D/64 elements as 16-byte chunks (lane-interleaved, so every load and store
-// instruction moves 1 KiB of contiguous memory).  The row stays in registers
-// between the reductions (x.x, x.q, gy.(y0-x): butterfly shuffles across the
-// wavefront) and the output pass, so every input byte is read from HBM once.
-// The pseudo-query q is loaded once per wavefront and reused for all of its
-// rows (grid-stride loop).  gq is reduced deterministically: each wavefront
-// accumulates its rows in registers, the 8 wavefronts of a workgroup are
-// summed in LDS in fixed order into one partial row per workgroup, and a
-// second kernel adds the partial rows in index order.  The page's kernel
-// uses relaxed float atomics there instead, whose result depends on timing.
+// there is no MFMA.  A row is owned by a team of four wavefronts (one
+// wavefront for narrow rows); each thread holds a few 16-byte chunks of x,
+// y0 (and gy), lane-interleaved so that every load and store instruction
+// moves 1 KiB of contiguous memory, and loads the next row's chunks while
+// the current row is reduced and written.  The row stays in registers
+// between the reductions (x.x, x.q, gy.(y0-x): butterflies across the
+// wavefront, then the team's partial sums in LDS in wavefront order) and the
+// output pass, so every input byte is read from HBM once.  The pseudo-query
+// q is loaded once per thread.  gq is reduced deterministically: each thread
+// accumulates its columns over the rows of its workgroup, the workgroup
+// writes one partial row, and a second kernel adds the partial rows in index
+// order.  The page's kernel uses relaxed float atomics there instead, whose
+// result depends on timing.  Rows whose width does not split into whole
+// chunks per thread take a generic path that reads each row twice.
 #include "common.h"
 #include "kernels.h"
 
@@ -76,145 +79,236 @@ __device__ __forceinline__ Mix mix(float sxx, float sxq, float l0, int D, float 
 }
 
 // ------------------------------------------------------- register path ----
-// NC = D / 512 chunks of 8 elements per lane.
-template <typename T, int NC>
-__global__ __launch_bounds__(kNTM) void merge_fwd_kernel(MergeArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * kWPB + (threadIdx.x >> 6);
-  const int nw = gridDim.x * kWPB;
-  const int D = a.D;
-  const Chunk<T>* qc = reinterpret_cast<const Chunk<T>*>(a.q);
-  Chunk<T> qr[NC];
+// A team of WPR wavefronts (WPR = 1 or 4; a workgroup is 4 wavefronts) owns
+// one row at a time.  Team thread t holds NCH 16-byte chunks of the row,
+// chunk j at index t + j * 64 * WPR, so every load and store instruction of
+// a wavefront moves 1 KiB of contiguous memory.  The next row's inputs are
+// loaded while the current row is reduced and written.  Row sums are reduced
+// across the wavefront with butterflies and, for WPR = 4, across the team
+// through LDS in wavefront order.
+constexpr int kTeamWG = 256;  // threads per workgroup on this path
+
+template <typename T>
+struct Elems {
+  static constexpr int N = 16 / sizeof(T);
+};
+
+template <typename T>
+__device__ __forceinline__ void chunk_f32(const u32x4& c, float (&f)[Elems<T>::N]) {
+  const T* e = reinterpret_cast<const T*>(&c);
 #pragma unroll
-  for (int c = 0; c < NC; ++c) qr[c] = qc[c * 64 + lane];
-  for (int row = gw; row < a.rows; row += nw) {
-    const int64_t base = (int64_t)row * (D / 8);
-    const Chunk<T>* xc = reinterpret_cast<const Chunk<T>*>(a.x) + base;
-    const Chunk<T>* yc = reinterpret_cast<const Chunk<T>*>(a.y0) + base;
-    Chunk<T> xr[NC], yr[NC];
+  for (int i = 0; i < Elems<T>::N; ++i) f[i] = (float)e[i];
+}
+
+template <typename T>
+__device__ __forceinline__ u32x4 f32_chunk(const float (&f)[Elems<T>::N]) {
+  u32x4 c;
+  T* e = reinterpret_cast<T*>(&c);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      xr[c] = xc[c * 64 + lane];
-      yr[c] = yc[c * 64 + lane];
+  for (int i = 0; i < Elems<T>::N; ++i) e[i] = (T)f[i];
+  return c;
+}
+
+template <int WPR>
+struct Team {
+  int lane, wave, sub, t;
+  __device__ __forceinline__ Team() {
+    lane = threadIdx.x & 63;
+    wave = threadIdx.x >> 6;
+    sub = wave / WPR;            // which of the workgroup's rows
+    t = (wave % WPR) * 64 + lane;  // thread index inside the team
+  }
+};
+
+// Sum of NV per-thread values over the team; red is 2 x 4 x 4 floats of LDS
+// (double-buffered by row parity, one barrier per row).
+template <int WPR, int NV>
+__device__ __forceinline__ void team_sum(float (&v)[NV], float* red, int parity, const Team<WPR>& tm) {
+#pragma unroll
+  for (int k = 0; k < NV; ++k) v[k] = wsum(v[k]);
+  if constexpr (WPR > 1) {
+    float* slot = red + parity * 16;
+    if (tm.lane == 0) {
+#pragma unroll
+      for (int k = 0; k < NV; ++k) slot[tm.wave * 4 + k] = v[k];
     }
-    const float l0 = a.l0[row];
-    float sxx = 0.f, sxq = 0.f;
+    __syncthreads();
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      float xf[8], qf[8];
-      to_f32(xr[c], xf);
-      to_f32(qr[c], qf);
+    for (int k = 0; k < NV; ++k) {
+      float acc = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        sxx += xf[i] * xf[i];
-        sxq += xf[i] * qf[i];
-      }
+      for (int w = 0; w < WPR; ++w) acc += slot[(tm.sub * WPR + w) * 4 + k];
+      v[k] = acc;
     }
-    sxx = wsum(sxx);
-    sxq = wsum(sxq);
-    const Mix mx = mix(sxx, sxq, l0, D, a.eps);
-    Chunk<T>* oc = reinterpret_cast<Chunk<T>*>(a.y) + base;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      float xf[8], yf[8], of[8];
-      to_f32(xr[c], xf);
-      to_f32(yr[c], yf);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) of[i] = mx.alpha * yf[i] + mx.beta * xf[i];
-      oc[c * 64 + lane] = from_f32<T>(of);
-    }
-    if (lane == 0) a.lse[row] = mx.m + logf(mx.Z);
   }
 }
 
-template <typename T, int NC>
-__global__ __launch_bounds__(kNTM) void merge_bwd_kernel(MergeArgs a) {
-  __shared__ float red[512 * NC];
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int gw = blockIdx.x * kWPB + wid;
-  const int nw = gridDim.x * kWPB;
+template <typename T, int WPR, int NCH>
+__global__ __launch_bounds__(kTeamWG) void merge_fwd_kernel(MergeArgs a) {
+  constexpr int E = Elems<T>::N;
+  constexpr int RPI = 4 / WPR;  // rows per workgroup iteration
+  __shared__ float red[32];
+  const Team<WPR> tm;
   const int D = a.D;
-  const Chunk<T>* qc = reinterpret_cast<const Chunk<T>*>(a.q);
-  Chunk<T> qr[NC];
-  float gq[NC][8];
+  const int64_t cpr = D / E;    // chunks per row
+  const u32x4* qc = reinterpret_cast<const u32x4*>(a.q);
+  float qf[NCH][E];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    qr[c] = qc[c * 64 + lane];
+  for (int j = 0; j < NCH; ++j) chunk_f32<T>(qc[tm.t + j * 64 * WPR], qf[j]);
+  const int stride = gridDim.x * RPI;
+  int row = blockIdx.x * RPI + tm.sub;
+  u32x4 xr[NCH], yr[NCH];
+  auto load = [&](int r) {
+    const u32x4* xc = reinterpret_cast<const u32x4*>(a.x) + (int64_t)r * cpr;
+    const u32x4* yc = reinterpret_cast<const u32x4*>(a.y0) + (int64_t)r * cpr;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) gq[c][i] = 0.f;
-  }
-  for (int row = gw; row < a.rows; row += nw) {
-    const int64_t base = (int64_t)row * (D / 8);
-    const Chunk<T>* xc = reinterpret_cast<const Chunk<T>*>(a.x) + base;
-    const Chunk<T>* yc = reinterpret_cast<const Chunk<T>*>(a.y0) + base;
-    const Chunk<T>* gc = reinterpret_cast<const Chunk<T>*>(a.gy) + base;
-    Chunk<T> xr[NC], yr[NC], gr[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      xr[c] = xc[c * 64 + lane];
-      yr[c] = yc[c * 64 + lane];
-      gr[c] = gc[c * 64 + lane];
+    for (int j = 0; j < NCH; ++j) {
+      xr[j] = xc[tm.t + j * 64 * WPR];
+      yr[j] = yc[tm.t + j * 64 * WPR];
     }
-    const float l0 = a.l0[row];
-    const float gl = a.gl ? a.gl[row] : 0.f;
-    float sxx = 0.f, sxq = 0.f, s = 0.f;
+  };
+  if (row < a.rows) load(row);
+  for (int parity = 0; row < a.rows; row += stride, parity ^= 1) {
+    u32x4 xc[NCH], yc[NCH];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      float xf[8], yf[8], gf[8], qf[8];
-      to_f32(xr[c], xf);
-      to_f32(yr[c], yf);
-      to_f32(gr[c], gf);
-      to_f32(qr[c], qf);
+    for (int j = 0; j < NCH; ++j) {
+      xc[j] = xr[j];
+      yc[j] = yr[j];
+    }
+    if (row + stride < a.rows) load(row + stride);
+    float v[2] = {0.f, 0.f};  // x.x, x.q
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        sxx += xf[i] * xf[i];
-        sxq += xf[i] * qf[i];
-        s += gf[i] * (yf[i] - xf[i]);
+    for (int j = 0; j < NCH; ++j) {
+      float xf[E];
+      chunk_f32<T>(xc[j], xf);
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        v[0] += xf[i] * xf[i];
+        v[1] += xf[i] * qf[j][i];
       }
     }
-    sxx = wsum(sxx);
-    sxq = wsum(sxq);
-    s = wsum(s);
-    const Mix mx = mix(sxx, sxq, l0, D, a.eps);
+    team_sum<WPR, 2>(v, red, parity, tm);
+    const Mix mx = mix(v[0], v[1], a.l0[row], D, a.eps);
+    u32x4* oc = reinterpret_cast<u32x4*>(a.y) + (int64_t)row * cpr;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      float xf[E], yf[E], of[E];
+      chunk_f32<T>(xc[j], xf);
+      chunk_f32<T>(yc[j], yf);
+#pragma unroll
+      for (int i = 0; i < E; ++i) of[i] = mx.alpha * yf[i] + mx.beta * xf[i];
+      oc[tm.t + j * 64 * WPR] = f32_chunk<T>(of);
+    }
+    if (tm.t == 0) a.lse[row] = mx.m + logf(mx.Z);
+  }
+}
+
+template <typename T, int WPR, int NCH>
+__global__ __launch_bounds__(kTeamWG) void merge_bwd_kernel(MergeArgs a) {
+  constexpr int E = Elems<T>::N;
+  constexpr int RPI = 4 / WPR;
+  __shared__ float red[32];
+  __shared__ float gqs[WPR == 1 ? 64 * NCH * E : 1];
+  const Team<WPR> tm;
+  const int D = a.D;
+  const int64_t cpr = D / E;
+  const u32x4* qc = reinterpret_cast<const u32x4*>(a.q);
+  float qf[NCH][E], gq[NCH][E];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    chunk_f32<T>(qc[tm.t + j * 64 * WPR], qf[j]);
+#pragma unroll
+    for (int i = 0; i < E; ++i) gq[j][i] = 0.f;
+  }
+  const int stride = gridDim.x * RPI;
+  int row = blockIdx.x * RPI + tm.sub;
+  u32x4 xr[NCH], yr[NCH], gr[NCH];
+  auto load = [&](int r) {
+    const u32x4* xc = reinterpret_cast<const u32x4*>(a.x) + (int64_t)r * cpr;
+    const u32x4* yc = reinterpret_cast<const u32x4*>(a.y0) + (int64_t)r * cpr;
+    const u32x4* gc = reinterpret_cast<const u32x4*>(a.gy) + (int64_t)r * cpr;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      xr[j] = xc[tm.t + j * 64 * WPR];
+      yr[j] = yc[tm.t + j * 64 * WPR];
+      gr[j] = gc[tm.t + j * 64 * WPR];
+    }
+  };
+  if (row < a.rows) load(row);
+  for (int parity = 0; row < a.rows; row += stride, parity ^= 1) {
+    u32x4 xc[NCH], yc[NCH], gc[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      xc[j] = xr[j];
+      yc[j] = yr[j];
+      gc[j] = gr[j];
+    }
+    if (row + stride < a.rows) load(row + stride);
+    float v[3] = {0.f, 0.f, 0.f};  // x.x, x.q, gy.(y0 - x)
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      float xf[E], yf[E], gf[E];
+      chunk_f32<T>(xc[j], xf);
+      chunk_f32<T>(yc[j], yf);
+      chunk_f32<T>(gc[j], gf);
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        v[0] += xf[i] * xf[i];
+        v[1] += xf[i] * qf[j][i];
+        v[2] += gf[i] * (yf[i] - xf[i]);
+      }
+    }
+    team_sum<WPR, 3>(v, red, parity, tm);
+    const float gl = a.gl ? a.gl[row] : 0.f;
+    const Mix mx = mix(v[0], v[1], a.l0[row], D, a.eps);
+    const float s = v[2];
     const float ab = mx.alpha * mx.beta;
     const float gl1 = mx.beta * gl - ab * s;
-    const float cq = gl1 * mx.rho;                                   // coefficient of q
+    const float cq = gl1 * mx.rho;                                        // coefficient of q
     const float cx = -gl1 * mx.xq * mx.rho * mx.rho * mx.rho / (float)D;  // coefficient of x
-    const float cg = gl1 * mx.rho;                                   // gq += cg * x
-    Chunk<T>* gxc = reinterpret_cast<Chunk<T>*>(a.gx) + base;
-    Chunk<T>* gyc = reinterpret_cast<Chunk<T>*>(a.gy0) + base;
+    const float cg = gl1 * mx.rho;                                        // gq += cg * x
+    u32x4* gxc = reinterpret_cast<u32x4*>(a.gx) + (int64_t)row * cpr;
+    u32x4* gyc = reinterpret_cast<u32x4*>(a.gy0) + (int64_t)row * cpr;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      float xf[8], gf[8], qf[8], gx[8], gy0[8];
-      to_f32(xr[c], xf);
-      to_f32(gr[c], gf);
-      to_f32(qr[c], qf);
+    for (int j = 0; j < NCH; ++j) {
+      float xf[E], gf[E], gx[E], gy0[E];
+      chunk_f32<T>(xc[j], xf);
+      chunk_f32<T>(gc[j], gf);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < E; ++i) {
         gy0[i] = mx.alpha * gf[i];
-        gx[i] = mx.beta * gf[i] + cq * qf[i] + cx * xf[i];
-        gq[c][i] += cg * xf[i];
+        gx[i] = mx.beta * gf[i] + cq * qf[j][i] + cx * xf[i];
+        gq[j][i] += cg * xf[i];
       }
-      gxc[c * 64 + lane] = from_f32<T>(gx);
-      gyc[c * 64 + lane] = from_f32<T>(gy0);
+      gxc[tm.t + j * 64 * WPR] = f32_chunk<T>(gx);
+      gyc[tm.t + j * 64 * WPR] = f32_chunk<T>(gy0);
     }
-    if (lane == 0) a.gl0[row] = mx.alpha * gl + ab * s;
+    if (tm.t == 0) a.gl0[row] = mx.alpha * gl + ab * s;
   }
-  // Workgroup partial of gq: wavefronts add into LDS one after another.
-  for (int w = 0; w < kWPB; ++w) {
-    if (wid == w) {
-#pragma unroll
-      for (int c = 0; c < NC; ++c)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int d = (c * 64 + lane) * 8 + i;
-          red[d] = (w == 0 ? 0.f : red[d]) + gq[c][i];
-        }
-    }
-    __syncthreads();
-  }
+  // Workgroup partial of gq.  WPR = 4: each column belongs to one thread.
+  // WPR = 1: the 4 wavefronts hold the same columns; they are added in LDS
+  // one after another.
   float* part = a.partial + (int64_t)blockIdx.x * D;
-  for (int d = threadIdx.x; d < D; d += kNTM) part[d] = red[d];
+  if constexpr (WPR == 4) {
+#pragma unroll
+    for (int j = 0; j < NCH; ++j)
+#pragma unroll
+      for (int i = 0; i < E; ++i) part[(tm.t + j * 256) * E + i] = gq[j][i];
+  } else {
+    for (int w = 0; w < 4; ++w) {
+      if (tm.wave == w) {
+#pragma unroll
+        for (int j = 0; j < NCH; ++j)
+#pragma unroll
+          for (int i = 0; i < E; ++i) {
+            const int d = (tm.lane + j * 64) * E + i;
+            gqs[d] = (w == 0 ? 0.f : gqs[d]) + gq[j][i];
+          }
+      }
+      __syncthreads();
+    }
+    for (int d = threadIdx.x; d < D; d += kTeamWG) part[d] = gqs[d];
+  }
 }
 
 // --------------------------------------------------------- generic path ----
@@ -320,14 +414,43 @@ __global__ __launch_bounds__(kNTM) void merge_bwd_generic(MergeArgs a) {
   }
 }
 
-// gq[d] = sum over partial rows p = 0 .. np-1 of partial[p][d], in order.
-__global__ __launch_bounds__(256) void gq_reduce_kernel(const float* __restrict__ partial, float* __restrict__ gq,
-                                                        int np, int D) {
+// gq[d] = sum over the np partial rows, in a fixed order, in two steps.
+// Step 1: slice s (a fixed contiguous range of partial rows) of a 128-column
+// block: thread (r, c) sums rows r, r + 8, ... of the range for 4 columns,
+// and the 8 row groups are added in order through LDS.  Step 2 adds the
+// kRedSlices slice rows in order.
+constexpr int kRedSlices = 8;
+
+__global__ __launch_bounds__(256) void gq_reduce_slices(const float* __restrict__ partial,
+                                                        float* __restrict__ slices, int np, int D) {
+  __shared__ f32x4 red[8][32];
+  const int c = threadIdx.x & 31, r = threadIdx.x >> 5;
+  const int d = blockIdx.x * 128 + 4 * c;
+  const int sl = blockIdx.y;
+  const int p0 = (int)((int64_t)np * sl / kRedSlices);
+  const int p1 = (int)((int64_t)np * (sl + 1) / kRedSlices);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (d < D) {
+    for (int p = p0 + r; p < p1; p += 8) acc += *reinterpret_cast<const f32x4*>(partial + (int64_t)p * D + d);
+  }
+  red[r][c] = acc;
+  __syncthreads();
+  if (r == 0 && d < D) {
+    f32x4 t = red[0][c];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) t += red[k][c];
+    *reinterpret_cast<f32x4*>(slices + (int64_t)sl * D + d) = t;
+  }
+}
+
+__global__ __launch_bounds__(256) void gq_reduce_final(const float* __restrict__ slices, float* __restrict__ gq,
+                                                       int D) {
   const int d = blockIdx.x * 256 + threadIdx.x;
   if (d >= D) return;
-  float s = 0.f;
-  for (int p = 0; p < np; ++p) s += partial[(int64_t)p * D + d];
-  gq[d] = s;
+  float t = 0.f;
+#pragma unroll
+  for (int sl = 0; sl < kRedSlices; ++sl) t += slices[(int64_t)sl * D + d];
+  gq[d] = t;
 }
 
 int grid_for(int rows) {
@@ -335,28 +458,102 @@ int grid_for(int rows) {
   return g < kMaxWG ? g : kMaxWG;
 }
 
-// Rows are kept in registers when they fit: D a multiple of 512 with
-// D/512 chunks per lane a power of two, at most max_nc of them.
-bool register_path(int D, int max_nc) {
-  if (D % 512 != 0) return false;
-  const int nc = D / 512;
-  return nc <= max_nc && (nc & (nc - 1)) == 0;
+// Register path shape: 16-byte chunks per row C = D * sizeof(T) / 16 split as
+// C = 64 * WPR * NCH with WPR in {4, 1} and NCH in {1, 2, 4, 8}; else the
+// generic path (returns false).
+struct RegShape {
+  int wpr, nch;
+};
+bool reg_shape(int D, int elem_bytes, RegShape& r) {
+  if ((D * elem_bytes) % 16 != 0) return false;
+  const int C = D * elem_bytes / 16;
+  for (int wpr : {4, 1}) {
+    if (C % (64 * wpr) != 0) continue;
+    const int nch = C / (64 * wpr);
+    if (nch == 1 || nch == 2 || nch == 4 || nch == 8) {
+      r.wpr = wpr;
+      r.nch = nch;
+      return true;
+    }
+  }
+  return false;
+}
+
+constexpr int kMaxTeamWG = 1024;  // cap on register-path workgroups (= gq partial rows)
+
+// Workgroups that fit on the device at once for a register-path kernel.
+int resident_wgs(const void* kernel) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kTeamWG, 0) != hipSuccess || cus <= 0 ||
+      per_cu <= 0) {
+    cus = 256;
+    per_cu = 2;
+  }
+  return cus * per_cu;
+}
+
+// Workgroups of the register path: one per row group, but no more than fit
+// on the device at once (the kernels loop over rows, so a second partial
+// wave of workgroups would only add a tail) and, for the backward, no more
+// than kMaxTeamWG.
+int team_grid(int resident, int rows, int wpr, bool capped) {
+  const int rpi = 4 / wpr;
+  int g = (rows + rpi - 1) / rpi;
+  if (g > resident) g = resident;
+  if (capped && g > kMaxTeamWG) g = kMaxTeamWG;
+  return g;
+}
+
+template <typename T, int WPR, int NCH>
+void fwd_launch(const MergeArgs& a, hipStream_t s) {
+  static const int resident = resident_wgs((const void*)merge_fwd_kernel<T, WPR, NCH>);
+  hipLaunchKernelGGL((merge_fwd_kernel<T, WPR, NCH>), dim3(team_grid(resident, a.rows, WPR, false)),
+                     dim3(kTeamWG), 0, s, a);
+}
+
+template <typename T, int WPR, int NCH>
+int bwd_launch(const MergeArgs& a, hipStream_t s) {
+  static const int resident = resident_wgs((const void*)merge_bwd_kernel<T, WPR, NCH>);
+  const int g = team_grid(resident, a.rows, WPR, true);
+  hipLaunchKernelGGL((merge_bwd_kernel<T, WPR, NCH>), dim3(g), dim3(kTeamWG), 0, s, a);
+  return g;
+}
+
+// WPR = 1 is only chosen for rows of 64 or 128 chunks (NCH = 1, 2): wider
+// rows that split into whole chunks per thread go to WPR = 4.
+template <typename T, int WPR>
+void launch_fwd_nch(const MergeArgs& a, int nch, hipStream_t s) {
+  switch (nch) {
+    case 1: fwd_launch<T, WPR, 1>(a, s); break;
+    case 2: fwd_launch<T, WPR, 2>(a, s); break;
+    case 4: if constexpr (WPR == 4) fwd_launch<T, WPR, 4>(a, s); break;
+    case 8: if constexpr (WPR == 4) fwd_launch<T, WPR, 8>(a, s); break;
+  }
+}
+
+template <typename T, int WPR>
+int launch_bwd_nch(const MergeArgs& a, int nch, hipStream_t s) {
+  switch (nch) {
+    case 1: return bwd_launch<T, WPR, 1>(a, s);
+    case 2: return bwd_launch<T, WPR, 2>(a, s);
+    case 4: if constexpr (WPR == 4) return bwd_launch<T, WPR, 4>(a, s); break;
+    case 8: if constexpr (WPR == 4) return bwd_launch<T, WPR, 8>(a, s); break;
+  }
+  return 0;
 }
 
 template <typename T>
 hipError_t fwd_t(const MergeArgs& a, hipStream_t s) {
-  dim3 grid(grid_for(a.rows)), block(kNTM);
-  if (register_path(a.D, sizeof(T) == 2 ? 16 : 8)) {
-    switch (a.D / 512) {
-      case 1: hipLaunchKernelGGL((merge_fwd_kernel<T, 1>), grid, block, 0, s, a); break;
-      case 2: hipLaunchKernelGGL((merge_fwd_kernel<T, 2>), grid, block, 0, s, a); break;
-      case 4: hipLaunchKernelGGL((merge_fwd_kernel<T, 4>), grid, block, 0, s, a); break;
-      case 8: hipLaunchKernelGGL((merge_fwd_kernel<T, 8>), grid, block, 0, s, a); break;
-      case 16:
-        if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((merge_fwd_kernel<T, 16>), grid, block, 0, s, a);
-        break;
-    }
+  RegShape r;
+  if (reg_shape(a.D, sizeof(T), r)) {
+    if (r.wpr == 4)
+      launch_fwd_nch<T, 4>(a, r.nch, s);
+    else
+      launch_fwd_nch<T, 1>(a, r.nch, s);
   } else {
+    dim3 grid(grid_for(a.rows)), block(kNTM);
     hipLaunchKernelGGL((merge_fwd_generic<T>), grid, block, 0, s, a);
   }
   return hipGetLastError();
@@ -364,36 +561,34 @@ hipError_t fwd_t(const MergeArgs& a, hipStream_t s) {
 
 template <typename T>
 hipError_t bwd_t(const MergeArgs& a, hipStream_t s) {
-  const int g = grid_for(a.rows);
-  dim3 grid(g), block(kNTM);
+  RegShape r;
   int np;
-  if (register_path(a.D, sizeof(T) == 2 ? 8 : 4)) {
-    switch (a.D / 512) {
-      case 1: hipLaunchKernelGGL((merge_bwd_kernel<T, 1>), grid, block, 0, s, a); break;
-      case 2: hipLaunchKernelGGL((merge_bwd_kernel<T, 2>), grid, block, 0, s, a); break;
-      case 4: hipLaunchKernelGGL((merge_bwd_kernel<T, 4>), grid, block, 0, s, a); break;
-      case 8:
-        if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((merge_bwd_kernel<T, 8>), grid, block, 0, s, a);
-        break;
-    }
-    np = g;
+  if (reg_shape(a.D, sizeof(T), r)) {
+    np = (r.wpr == 4) ? launch_bwd_nch<T, 4>(a, r.nch, s) : launch_bwd_nch<T, 1>(a, r.nch, s);
   } else {
-    hipLaunchKernelGGL((merge_bwd_generic<T>), grid, block, 0, s, a);
+    const int g = grid_for(a.rows);
+    hipLaunchKernelGGL((merge_bwd_generic<T>), dim3(g), dim3(kNTM), 0, s, a);
     np = g * kWPB;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 rgrid((a.D + 255) / 256), rblock(256);
-  hipLaunchKernelGGL(gq_reduce_kernel, rgrid, rblock, 0, s, a.partial, a.gq, np, a.D);
+  // the slice rows follow the np partial rows in the workspace
+  float* slices = a.partial + (int64_t)np * a.D;
+  hipLaunchKernelGGL(gq_reduce_slices, dim3((a.D + 127) / 128, kRedSlices), dim3(256), 0, s, a.partial, slices, np,
+                     a.D);
+  hipLaunchKernelGGL(gq_reduce_final, dim3((a.D + 255) / 256), dim3(256), 0, s, slices, a.gq, a.D);
   return hipGetLastError();
 }
 
 }  // namespace
 
 int merge_bwd_partial_rows(int rows, int D) {
-  // upper bound over both paths: one partial row per wavefront
+  // upper bound over both paths and every dtype: one partial row per
+  // wavefront of the generic path (min(rows rounded up to 8, 4096)), which is
+  // at least the register path's one per workgroup (min(rows, 1024)), plus
+  // the kRedSlices rows of the reduction's first step
   (void)D;
-  return grid_for(rows) * kWPB;
+  return grid_for(rows) * kWPB + kRedSlices;
 }
 
 hipError_t launch_merge_fwd(const MergeArgs& a, hipStream_t s) {

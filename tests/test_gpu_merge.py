@@ -50,15 +50,19 @@ def compare(wl, t, got, with_gl=True, l0=None):
 
 
 SMALL = [
-    # dtype, rows, D, eps
-    (BF16, 37, 4096, 1e-6),     # register path, ragged row count
-    (F16, 300, 1024, 1e-6),
-    (BF16, 129, 512, 1.1920929e-07),
-    (F32, 50, 2048, 1e-6),
-    (F32, 17, 8192, 1e-6),      # fp32 beyond the register budget -> generic path
-    (BF16, 33, 1000, 1e-6),     # generic path (D not a multiple of 512)
-    (F16, 5000, 24, 1e-6),      # tiny rows, many of them
-    (BF16, 9000, 3072, 1e-6),   # more rows than wavefronts: grid-stride loop
+    # dtype, rows, D, eps          register path: 16-byte chunks per row C = 64 * WPR * NCH
+    (BF16, 37, 4096, 1e-6),       # WPR 4, NCH 2, ragged row count
+    (F16, 300, 1024, 1e-6),       # WPR 1 (one wavefront per row), NCH 2
+    (BF16, 129, 512, 1.1920929e-07),  # WPR 1, NCH 1
+    (F32, 50, 2048, 1e-6),        # WPR 4, NCH 2 (4 elements per chunk)
+    (F32, 17, 8192, 1e-6),        # WPR 4, NCH 8
+    (BF16, 1000, 2048, 1e-6),     # WPR 4, NCH 1
+    (BF16, 77, 8192, 1e-6),       # WPR 4, NCH 4
+    (F16, 50, 16384, 1e-6),       # WPR 4, NCH 8
+    (BF16, 33, 1000, 1e-6),       # generic path (D not a whole number of chunks per thread)
+    (F16, 5000, 24, 1e-6),        # generic path, tiny rows, many of them
+    (BF16, 9000, 3072, 1e-6),     # generic path, more rows than wavefronts
+    (BF16, 3000, 4096, 1e-6),     # more rows than resident workgroups: grid-stride loop
 ]
 
 
