@@ -267,11 +267,13 @@ void attn_dkdv_kernel(const BwdParams p) {
   // E of them per wave, so every wave issues exactly one such load.
   constexpr int E = 2 * QB / kWaves;
   static_assert(64 % E == 0, "row statistics split");
+  // A wave's E elements lie all in the LSE half or all in the Delta half
+  // (E divides QB), so the source array is the same for the whole wave.
+  static_assert(QB % E == 0, "row statistics split");
   const int st_first = wave * E;
   const int st_ins = st_first / 64;
   const bool st_lane = lane >= st_first % 64 && lane < st_first % 64 + E;
-  const int st_elem = st_ins * 64 + lane;
-  const float* st_src = st_elem < QB ? p.lse + lbase + st_elem : p.delta + lbase + (st_elem - QB);
+  const float* st_src = (st_first < QB ? p.lse + lbase + st_ins * 64 : p.delta + lbase + (st_ins * 64 - QB));
 
   // Issue the direct loads of query block qb into stage st; returns the
   // number of vector-memory instructions this wave issued.
@@ -296,7 +298,7 @@ void attn_dkdv_kernel(const BwdParams p) {
     }
     dma.load(gdo + off, st.dout, wave);
     if (st_lane)
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(st_src + i0),
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(st_src + (i0 + lane)),
                                        (void __attribute__((address_space(3)))*)(st.stats + st_ins * 64), 4, 0,
                                        0);
     return n;
@@ -394,12 +396,13 @@ void attn_dkdv_kernel(const BwdParams p) {
       dp[st] = dinit;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) dp[st] = mfma32x32x16(rd8(cur.dout, st, kk), rd8(vres, 0, kk), dp[st]);
+      // causal mask: key kj is beyond row i0 + 32 st + perm_row(r, h)
+      const int thr = kj - pshift - i0 - 32 * st - 8 * h;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float pv = exp2_fast(s[st][r] * p.scale2);
         if constexpr (MASK) {
-          const int row = i0 + 32 * st + perm_row(r, h);
-          if (kj > row + pshift) pv = 0.f;
+          if (thr > perm_row(r, 0)) pv = 0.f;
         }
         const float ds = pv * dp[st][r];
         s[st][r] = pv;
@@ -658,12 +661,13 @@ void attn_dq_kernel(const BwdParams p) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) dp = mfma32x32x16(rd8(cur.v, st, kk), dof[kk], dp);
       f32x16 dsf;
+      // causal mask: key n0 + 32 st + perm_row(r, h) is beyond this query
+      const int thr = qi + pshift - n0 - 32 * st - 8 * h;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float pv = exp2_fast(fmaf(s[r], p.scale2, -lse2));
         if constexpr (MASK) {
-          const int key = n0 + 32 * st + perm_row(r, h);
-          if (key > qi + pshift) pv = 0.f;
+          if (perm_row(r, 0) > thr) pv = 0.f;
         }
         const float ds = pv * (dp[r] - dl);
         if constexpr (kPw) {

@@ -91,7 +91,6 @@ void attn_fwd_kernel(const FwdParams p) {
   constexpr int NS = fwd_stages<T, D, VAR>();
   using V8 = typename Vec8<T>::type;
   using St = FwdStage<T, D, VAR>;
-  using Tile = typename St::Tile;
   constexpr int KK = D / 16;     // 16-wide k steps over the head dim
   constexpr int DT = D / 32;     // 32-wide tiles of the output's head dim
   constexpr int ST = kBN / 32;   // 32-key score tiles per block
@@ -280,31 +279,49 @@ void attn_fwd_kernel(const FwdParams p) {
           }
         }
       }
+    } else if constexpr (!kJvp) {
+      // All ST * KK row reads of the K tile are put in flight first; product
+      // i then waits only for read i.  Reads and products alternate between
+      // the ST score tiles (independent accumulation chains).
+      static_assert(ST * KK <= 16, "row reads in flight");
+      RowReads<ST * KK> kr;
+      const uint32_t kb = lds_addr(cur.k[0]);
+      static_for<ST * KK>([&](auto ic) {
+        constexpr int I = decltype(ic)::value;
+        kr.template issue<I, (I % ST) * 32 * D * 2>(kb + kofs[I / ST]);
+      });
+#pragma unroll
+      for (int st = 0; st < ST; ++st) s[st] = zero16();
+      static_for<ST * KK>([&](auto ic) {
+        constexpr int I = decltype(ic)::value;
+        kr.template wait<I>();
+        s[I % ST] = mfma32x32x16(kr.template get<V8>(I), qf[I / ST], s[I % ST]);
+        __builtin_amdgcn_sched_barrier(0);
+      });
     } else {
 #pragma unroll
       for (int st = 0; st < ST; ++st) {
         s[st] = zero16();
-        if constexpr (kJvp) sd[st] = zero16();
+        sd[st] = zero16();
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           const V8 a = krow8(cur.k[0], st, kk);
           s[st] = mfma32x32x16(a, qf[kk], s[st]);
-          if constexpr (kJvp) sd[st] = mfma32x32x16(a, tqf[kk], sd[st]);
+          sd[st] = mfma32x32x16(a, tqf[kk], sd[st]);
         }
-        if constexpr (kJvp) {
 #pragma unroll
-          for (int kk = 0; kk < KK; ++kk) sd[st] = mfma32x32x16(krow8(cur.k[1], st, kk), qf[kk], sd[st]);
-        }
+        for (int kk = 0; kk < KK; ++kk) sd[st] = mfma32x32x16(krow8(cur.k[1], st, kk), qf[kk], sd[st]);
       }
     }
     // ---- online softmax ---------------------------------------------------
     if constexpr (MASK) {
 #pragma unroll
       for (int st = 0; st < ST; ++st) {
+        // key n0 + 32 st + perm_row(r, h) is beyond this query
+        const int thr = qi + pshift - n0 - 32 * st - 8 * h;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = n0 + 32 * st + perm_row(r, h);
-          if (key > qi + pshift) s[st][r] = kNegInf;
+          if (perm_row(r, 0) > thr) s[st][r] = kNegInf;
         }
       }
     }

@@ -22,6 +22,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -100,6 +103,11 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Index of this wavefront in the workgroup, as a value the compiler knows to
+// be the same for every lane (branches on it become scalar branches rather
+// than exec-masked regions).
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6); }
 
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
 
@@ -385,6 +393,25 @@ struct TrOps {
       op[t] = __builtin_bit_cast(typename Vec8<T>::type, w);
     }
   }
+  // Same reads from per-lane LDS byte addresses a[s] (allocation base plus
+  // the lane's half-s offset for key group 0) with the tile's byte offset
+  // inside the allocation, IMM, folded into the instruction's immediate.
+  template <int D, int IMM>
+  __device__ __forceinline__ void issue_imm(const uint32_t (&a)[2]) {
+    static_assert(IMM >= 0 && IMM + (NOPS - 1) * 16 * D * 2 <= 65535, "LDS immediate offset range");
+#pragma unroll
+    for (int t = 0; t < NOPS; ++t) {
+      u32x2 part[2];
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(part[0]) : "v"(a[0]), "i"(IMM + t * 16 * D * 2));
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(part[1]) : "v"(a[1]), "i"(IMM + t * 16 * D * 2));
+      u32x4 w;
+      w[0] = part[0][0];
+      w[1] = part[0][1];
+      w[2] = part[1][0];
+      w[3] = part[1][1];
+      op[t] = __builtin_bit_cast(typename Vec8<T>::type, w);
+    }
+  }
   __device__ __forceinline__ void wait() {
     if constexpr (NOPS == 1) {
       asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(op[0]));
@@ -395,6 +422,40 @@ struct TrOps {
     } else {
       static_assert(NOPS == 1 || NOPS == 2 || NOPS == 4, "operand count");
     }
+  }
+};
+
+// f(std::integral_constant<int, I>{}) for I = 0 .. N-1, unrolled.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// N 16-byte LDS reads (ds_read_b128) issued back to back as inline asm, so
+// that they are all in flight together; wait<I>() makes results 0 .. I valid
+// (LDS reads of one wave complete in issue order) and ties them to that wait.
+// As with TrOps, inline asm keeps the compiler's wait-count pass from
+// waiting for the direct loads of later stages before these reads.
+template <int N>
+struct RowReads {
+  static_assert(N >= 1 && N <= 16, "lgkmcnt counts up to 15 outstanding reads");
+  u32x4 r[N];
+  template <int I, int IMM>
+  __device__ __forceinline__ void issue(uint32_t addr) {
+    static_assert(I >= 0 && I < N && IMM >= 0 && IMM <= 65535, "read slot / immediate offset");
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r[I]) : "v"(addr), "i"(IMM));
+  }
+  template <int I>
+  __device__ __forceinline__ void wait() {
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r[I]) : "n"(N - 1 - I));
+  }
+  template <typename V>
+  __device__ __forceinline__ V get(int i) const {
+    return __builtin_bit_cast(V, r[i]);
   }
 };
 

@@ -368,8 +368,10 @@ COPY_BYTES = 256 << 20
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    # a few hundred warm-up steps (~0.2 s): the GPU's clocks need that long to
+    # ramp up, and timings taken earlier read up to ~20% slow
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-components", action="store_true", help="time only the headline step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
