@@ -130,10 +130,13 @@ KERNEL_SOURCES = {
     "dkdv": ["attention_fa2_tiles_amd/csrc/attn_bwd.hip", "attention_fa2_tiles_amd/csrc/common.h"],
     "dq": ["attention_fa2_tiles_amd/csrc/attn_bwd.hip", "attention_fa2_tiles_amd/csrc/common.h"],
     "delta": ["attention_fa2_tiles_amd/csrc/attn_bwd.hip"],
+    "merge_fwd": ["attention_fa2_tiles_amd/csrc/merge.hip", "attention_fa2_tiles_amd/csrc/common.h"],
+    "merge_bwd": ["attention_fa2_tiles_amd/csrc/merge.hip", "attention_fa2_tiles_amd/csrc/common.h"],
 }
+MERGE_NAME = "merge_bf16_rows32768_d4096"
 
 
-def measured_traffic(kernel):
+def measured_traffic(workload, kernel):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when there is none or the kernel's source changed since."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
@@ -141,7 +144,7 @@ def measured_traffic(kernel):
         return None
     with open(path) as f:
         data = json.load(f)
-    rec = data.get(HEADLINE, {}).get(kernel)
+    rec = data.get(workload, {}).get(kernel)
     if not rec or rec.get("source_digest") != source_digest(KERNEL_SOURCES[kernel]):
         return None
     return rec.get("bytes_per_launch")
@@ -202,7 +205,7 @@ def bench_headline(torch, args, timer):
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-        "traffic": measured_traffic(dominant),
+        "traffic": measured_traffic(HEADLINE, dominant),
         "avg_launch_ms": round(per[dominant], 5),
         "algorithmic_flops_per_launch": amount,
     }
@@ -299,7 +302,9 @@ def bench_merge(torch, timer, iters):
     b_gb = wl.bwd_bytes() / (b_ms * 1e-3) / 1e9
     return {"fwd_ms": round(f_ms, 4), "fwd_GB/s": round(f_gb, 1), "fwd_frac_hbm": round(f_gb / PEAK_HBM_GBPS, 4),
             "bwd_ms": round(b_ms, 4), "bwd_GB/s": round(b_gb, 1), "bwd_frac_hbm": round(b_gb / PEAK_HBM_GBPS, 4),
-            "fwd_bytes": wl.fwd_bytes(), "bwd_bytes": wl.bwd_bytes()}
+            "fwd_bytes": wl.fwd_bytes(), "bwd_bytes": wl.bwd_bytes(),
+            "fwd_traffic": measured_traffic(MERGE_NAME, "merge_fwd"),
+            "bwd_traffic": measured_traffic(MERGE_NAME, "merge_bwd")}
 
 
 def cpu_baseline(target_s):
@@ -340,10 +345,14 @@ def cpu_baseline(target_s):
 
 
 def profile_mode(torch):
-    """Launch each kernel of the headline step a few times, then copy 256 MiB
-    device-to-device; rocprofv3 --pmc runs wrap this to count HBM bytes per
-    dispatch, and the copy's counter value per byte is the calibration."""
-    from attention_fa2_tiles_amd.inputs import WORKLOADS
+    """Launch each kernel of the headline step and the residual merge a few
+    times, then copy 256 MiB device-to-device; rocprofv3 --pmc runs wrap this
+    to count HBM bytes per dispatch, and the copy's counter value per byte is
+    the calibration."""
+    from attention_fa2_tiles_amd import lib
+    from attention_fa2_tiles_amd.inputs import MERGE_WORKLOAD, WORKLOADS, merge_inputs
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_util import dev, empty, empty_f32
     wl = WORKLOADS[HEADLINE]
     _, d = attn_setup(torch, wl, ("q", "k", "v", "do"))
     b = attn_buffers(torch, wl, d)
@@ -354,10 +363,32 @@ def profile_mode(torch):
             calls[k]()
         torch.cuda.synchronize()
         progress(f"profiled {k}")
+    del d, b, calls
+    mw = MERGE_WORKLOAD
+    t = merge_inputs(mw)
+    x, y0, q, l0, gy, gl = (dev(t[n]) for n in ("x", "y0", "q", "l0", "gy", "gl"))
+    del t
+    R, D = mw.rows, mw.D
+    y, lse = empty((R, D), mw.dtype), empty_f32((R,))
+    gx, gy0, gq, gl0 = empty((R, D), mw.dtype), empty((R, D), mw.dtype), empty_f32((D,)), empty_f32((R,))
+    nb = lib.resmerge_bwd_workspace_size(R, D)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        lib.resmerge_fwd(mw.dtype, x, q, y0, l0, y, lse, R, D, mw.eps)
+    torch.cuda.synchronize()
+    progress("profiled merge fwd")
+    for _ in range(3):
+        lib.resmerge_bwd(mw.dtype, x, q, y0, l0, gy, gl, gx, gq, gy0, gl0, ws, nb, R, D, mw.eps)
+    torch.cuda.synchronize()
+    progress("profiled merge bwd")
+    del x, y0, q, l0, gy, gl, y, lse, gx, gy0, gq, gl0, ws
+    torch.cuda.empty_cache()
+    # calibration: an elementwise copy (dst = -src) of COPY_BYTES, launched
+    # over the whole device like the kernels above
     src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
     for _ in range(3):
-        dst.copy_(src)
+        torch.neg(src, out=dst)
     torch.cuda.synchronize()
     progress("profiled copy")
 
@@ -376,8 +407,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--profile", action="store_true",
-                    help="counter-collection mode: a few launches of each kernel of the step, then a plain "
-                         "device-to-device copy of 256 MiB (the byte-count calibration), no timing output")
+                    help="counter-collection mode: a few launches of each kernel of the step and of the merge, "
+                         "then an elementwise copy of 256 MiB (the byte-count calibration), no timing output")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "

@@ -32,7 +32,11 @@
  *   fails nothing is launched and the matching negative fa_status is
  *   returned.  A failed launch returns FA_ERR_HIP.  No C++ exception crosses
  *   this boundary.
- * - Pointers must be 16-byte aligned (FA_ERR_ALIGN).
+ * - Alignment (FA_ERR_ALIGN otherwise): tensors of the call's dtype (q, k,
+ *   v, o, dout, the gradients and tangents, the merge's row tensors and q)
+ *   16 bytes; fp32 per-row vectors (lse, delta, l0, gl, gl0, gq) and the
+ *   attention backward's workspace 4 bytes; the merge backward's workspace
+ *   16 bytes.
  * - Supported attention shapes: B, H >= 1; M, N multiples of 64; D in
  *   {64, 128} (FA_ERR_UNSUPPORTED otherwise).
  *
@@ -59,7 +63,7 @@ typedef enum {
   FA_ERR_NULL = -1,        /* a required pointer is NULL                    */
   FA_ERR_SHAPE = -2,       /* a size is <= 0 or the sizes overflow         */
   FA_ERR_DTYPE = -3,       /* unknown dtype code                            */
-  FA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned             */
+  FA_ERR_ALIGN = -4,       /* a pointer is not aligned as required          */
   FA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required    */
   FA_ERR_UNSUPPORTED = -6, /* valid but unsupported (D, M/N granularity...)  */
   FA_ERR_HIP = -7          /* a HIP launch or runtime call failed           */
