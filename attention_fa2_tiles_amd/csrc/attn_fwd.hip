@@ -337,7 +337,7 @@ void attn_fwd_kernel(const FwdParams p) {
     const float mloc = halves_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))) * p.scale2;
     if (__ballot(mloc > m_i + kRescaleSlack) != 0) {
       const float m_new = fmaxf(m_i, mloc);
-      const float alpha = exp2_fast(m_i - m_new);  // m_i = -inf -> 0
+      const float alpha = (m_new == kNegInf) ? 1.f : exp2_fast(m_i - m_new);  // m_i = -inf -> 0
       l_i *= alpha;
       if constexpr (kJvp) mu_i *= alpha;
 #pragma unroll
@@ -352,14 +352,13 @@ void attn_fwd_kernel(const FwdParams p) {
       m_i = m_new;
     }
     const float neg_m = (m_i == kNegInf) ? 0.f : -m_i;
-    float ls[4] = {0.f, 0.f, 0.f, 0.f}, mus[4] = {0.f, 0.f, 0.f, 0.f};
+    float mus[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < ST; ++st) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float pv = exp2_fast(fmaf(s[st][r], p.scale2, neg_m));
         s[st][r] = pv;
-        ls[r & 3] += pv;
         if constexpr (kJvp) {
           const float ps = pv * sd[st][r] * p.sm_scale;
           sd[st][r] = ps;
@@ -367,16 +366,20 @@ void attn_fwd_kernel(const FwdParams p) {
         }
       }
     }
-    l_i += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     if constexpr (kJvp) mu_i += (mus[0] + mus[1]) + (mus[2] + mus[3]);
     // ---- O^t += V^t P^t (and the tangent accumulator) ----------------------
+    // The row sum is taken over P as rounded for the product (pair dot
+    // products with 1), so O = acc / l is normalised with the same weights.
     V8 pb[PT];
     V8 psb[kJvp ? PT : 1];
+    float ls = 0.f;
 #pragma unroll
     for (int t = 0; t < PT; ++t) {
       pb[t] = pack8<T>(s[t >> 1], 8 * (t & 1));
+      ls = add_sum8(ls, pb[t]);
       if constexpr (kJvp) psb[t] = pack8<T>(sd[t >> 1], 8 * (t & 1));
     }
+    l_i += ls;
     // V^t operands come from transposing LDS reads issued as inline asm
     // (see TrOps): the reads of d-tile dt + 1 are in flight while the
     // products of d-tile dt run.
@@ -466,6 +469,310 @@ void attn_fwd_kernel(const FwdParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Software-pipelined forward, plain variant.
+//
+// Iteration j works on two K/V blocks.  The 16 (D = 128) or 8 (D = 64) score
+// products of block j + 1 are issued one at a time, each followed by the
+// exponent work of a few scores of block j, so the matrix core and the vector
+// ALU of a SIMD work side by side; then the products P_j V_j are issued, each
+// followed by a step of block j + 1's row max.  The K tile of block j + 1 is
+// needed one iteration earlier than in the single-block loop, so the LDS ring
+// has four stages: block j (V read), j + 1 (K read), j + 2 (landed) and j + 3
+// (loading).  The loop is unrolled by the four stages so every LDS address is
+// a per-lane register plus an immediate.
+// ---------------------------------------------------------------------------
+constexpr int kPipeNS = 4;
+constexpr int kPipeWaves = 8;
+
+template <typename T, int D>
+struct alignas(256) PipeSmem {
+  using Tile = DTile<T, kBN, D, kPipeWaves>;
+  T k[kPipeNS][Tile::ELEMS];
+  T v[kPipeNS][Tile::ELEMS];
+};
+
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(64 * kPipeWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_pipe_kernel(const FwdParams p) {
+  constexpr int kWaves = kPipeWaves;
+  constexpr int kBM = 32 * kWaves;
+  constexpr int NS = kPipeNS;
+  using V8 = typename Vec8<T>::type;
+  using Sm = PipeSmem<T, D>;
+  using Tile = typename Sm::Tile;
+  using Dma = DmaTile<T, kBN, D, kWaves>;
+  constexpr int KK = D / 16;
+  constexpr int DT = D / 32;
+  constexpr int ST = kBN / 32;
+  constexpr int PT = kBN / 16;
+  constexpr int NR = ST * KK;        // K row reads (= score products) per block
+  constexpr int NSC = 16 * ST;       // scores per lane per block
+  constexpr int EPM = NSC / NR;      // scores whose exponent follows each product
+  constexpr int NPV = DT * PT;       // P V products per block
+  constexpr int MPP = NSC / NPV;     // scores folded into the max per P V product
+  constexpr int kTileBytes = Tile::ELEMS * 2;
+  static_assert(sizeof(Sm) <= kLdsBytes, "LDS budget");
+  static_assert(NSC % NR == 0 && NSC % NPV == 0 && MPP % 2 == 0, "interleave shape");
+  static_assert((NS - 1) * kTileBytes + (ST - 1) * 32 * D * 2 <= 65535, "K read immediates");
+  static_assert((NS - 1) * kTileBytes + (PT - 1) * 16 * D * 2 <= 65535, "V read immediates");
+
+  __shared__ Sm smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = wave_id();
+  const int li = lane & 31, h = lane >> 5;
+
+  // Workgroup -> (head, query block): heads vary fastest (one head's K/V in
+  // one XCD's L2); causal: longest query blocks first.
+  const int bh = blockIdx.x % p.BH;
+  int mb = blockIdx.x / p.BH;
+  if (CAUSAL) mb = p.nmb - 1 - mb;
+  const int m0 = mb * kBM;
+  const int row0 = m0 + 32 * wave;
+  const bool wave_valid = row0 < p.M;
+  const int qi = row0 + li;
+  const int pshift = p.N - p.M;
+  const int64_t qbase = (int64_t)bh * p.M * D;
+  const int64_t kbase = (int64_t)bh * p.N * D;
+  const T* gk = (const T*)p.k + kbase;
+  const T* gv = (const T*)p.v + kbase;
+  Dma dma;
+  dma.lane_offsets(wave, lane);
+
+  int n_end = p.N;
+  const int wg_last_row = min(p.M, m0 + kBM) - 1;
+  if (CAUSAL) n_end = min(p.N, wg_last_row + pshift + 1);
+  const int nblk = n_end > 0 ? (n_end + kBN - 1) / kBN : 0;
+
+  V8 qf[KK];
+  if (wave_valid) {
+    const T* qrow = (const T*)p.q + qbase + (int64_t)qi * D + 8 * h;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const V8*>(qrow + 16 * kk);
+  }
+
+  f32x16 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = zero16();
+  float m_i = kNegInf;  // running max, log2 units (raised lazily, see kRescaleSlack)
+  float l_i = 0.f;      // running sum, this half-wave's keys
+
+  // Per-lane LDS addresses.  K row reads: row li, chunk 2 kk + h of a K tile
+  // (stage and 32-row sub-tile are immediates).  V^t transposing reads of
+  // d-tile dt, halves 0 and 1, key group 0 of a V tile.
+  const uint32_t lbase = lds_addr(&smem);
+  uint32_t kaddr[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+    kaddr[kk] = lbase + (uint32_t)((li * D + (((2 * kk + h) ^ swz<D>(li)) * 8)) * 2);
+  const TrLane tl(lane);
+  uint32_t vaddr[DT][2];
+  const uint32_t vb = lbase + (uint32_t)__builtin_offsetof(Sm, v);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int m = swap23(8 * tl.hh + 4 * s2 + tl.r);
+      const int d = 32 * dt + tl.dcol;
+      vaddr[dt][s2] = vb + (uint32_t)((m * D + (((d >> 3) ^ swz<D>(m)) * 8) + (d & 7)) * 2);
+    }
+  }
+
+  auto issue = [&](int jb) {
+    const int st = jb % NS;
+    const int64_t off = (int64_t)jb * kBN * D;
+    dma.load(gk + off, smem.k[st], wave);
+    dma.load(gv + off, smem.v[st], wave);
+  };
+  constexpr int kLoads = 2 * Dma::PER_WAVE;
+  auto active = [&](int jb) { return wave_valid && (!CAUSAL || jb * kBN <= row0 + 31 + pshift); };
+  auto needs_mask = [&](int jb) { return CAUSAL && (jb * kBN + kBN - 1 > row0 + pshift); };
+
+  // K row read i of stage S (i = kk * ST + st), as inline asm.
+  auto kread = [&](auto stage_c, auto i_c, u32x4& r) {
+    constexpr int S = decltype(stage_c)::value;
+    constexpr int I = decltype(i_c)::value;
+    const uint32_t a = kaddr[I / ST];
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(S * kTileBytes + (I % ST) * 32 * D * 2));
+  };
+  // Wait for K read i.  Reads are kept kWin deep: 0 .. kWin-1 are issued
+  // first and read i + kWin right after product i (reads complete in issue
+  // order).
+  constexpr int kWin = 4;
+  auto kwait = [&](auto i_c, u32x4& r) {
+    constexpr int I = decltype(i_c)::value;
+    constexpr int CNT = (NR - 1 - I < kWin - 1) ? (NR - 1 - I) : (kWin - 1);
+    asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "n"(CNT));
+  };
+
+  // Score products of the block in stage S into sn; after product i, run
+  // between(i) (exponent work of the previous block, or nothing).
+  auto scores = [&](auto stage_c, f32x16 (&sn)[ST], auto&& between) {
+    u32x4 kr[NR];
+    static_for<kWin>([&](auto ic) { kread(stage_c, ic, kr[decltype(ic)::value]); });
+#pragma unroll
+    for (int st = 0; st < ST; ++st) sn[st] = zero16();
+    static_for<NR>([&](auto ic) {
+      constexpr int I = decltype(ic)::value;
+      kwait(ic, kr[I]);
+      sn[I % ST] = mfma32x32x16(__builtin_bit_cast(V8, kr[I]), qf[I / ST], sn[I % ST]);
+      if constexpr (I + kWin < NR) kread(stage_c, std::integral_constant<int, I + kWin>{}, kr[I + kWin]);
+      between(ic);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // Causal mask of a block's raw scores (keys beyond this query -> -inf).
+  auto apply_mask = [&](f32x16 (&sc)[ST], int n0) {
+#pragma unroll
+    for (int st = 0; st < ST; ++st) {
+      const int thr = qi + pshift - n0 - 32 * st - 8 * h;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (perm_row(r, 0) > thr) sc[st][r] = kNegInf;
+    }
+  };
+
+  // Exponent work on scores [I*EPM, (I+1)*EPM) of sc against neg_m.
+  auto exp_step = [&](f32x16 (&sc)[ST], float neg_m, auto i_c) {
+    constexpr int I = decltype(i_c)::value;
+#pragma unroll
+    for (int u = 0; u < EPM; ++u) {
+      const int e = I * EPM + u;
+      sc[e / 16][e % 16] = exp2_fast(fmaf(sc[e / 16][e % 16], p.scale2, neg_m));
+    }
+  };
+  // P of a block (already exponentiated in sc) -> packed operands and row sum.
+  auto pack_sum = [&](f32x16 (&sc)[ST], V8 (&pb)[PT]) {
+    float ls = 0.f;
+#pragma unroll
+    for (int t = 0; t < PT; ++t) {
+      pb[t] = pack8<T>(sc[t >> 1], 8 * (t & 1));
+      ls = add_sum8(ls, pb[t]);
+    }
+    l_i += ls;
+  };
+  // Lazy rescale after the row max mloc (log2 units) of the next block.
+  auto rescale = [&](float mloc) {
+    if (__ballot(mloc > m_i + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_i, mloc);
+      const float alpha = (m_new == kNegInf) ? 1.f : exp2_fast(m_i - m_new);
+      l_i *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dt][r] *= alpha;
+      }
+      m_i = m_new;
+    }
+  };
+  // O^t += V^t P^t for the V tile of stage S; after product i, between(i).
+  auto pv = [&](auto stage_c, const V8 (&pb)[PT], auto&& between) {
+    constexpr int S = decltype(stage_c)::value;
+    constexpr int IMM = S * kTileBytes;
+    TrOps<T, PT> va, vb2;
+    va.template issue_imm<D, IMM>(vaddr[0]);
+    va.wait();
+    static_for<DT>([&](auto dc) {
+      constexpr int DTI = decltype(dc)::value;
+      TrOps<T, PT>& cv = (DTI & 1) ? vb2 : va;
+      TrOps<T, PT>& nv = (DTI & 1) ? va : vb2;
+      if constexpr (DTI + 1 < DT) nv.template issue_imm<D, IMM>(vaddr[DTI + 1]);
+      static_for<PT>([&](auto tc) {
+        constexpr int TI = decltype(tc)::value;
+        acc[DTI] = mfma32x32x16(cv.op[TI], pb[TI], acc[DTI]);
+        between(std::integral_constant<int, DTI * PT + TI>{});
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      if constexpr (DTI + 1 < DT) nv.wait();
+    });
+  };
+
+  // Prologue: the query operands have landed; blocks 0, 1, 2 are issued and
+  // blocks 0 and 1 have landed; the scores of block 0 and its max are taken.
+  wait_vmcnt0();
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < nblk) issue(j);
+  if (nblk > NS - 2)
+    wait_vmcnt<kLoads>();
+  else
+    wait_vmcnt0();
+  lds_barrier();
+
+  f32x16 sa[ST], sb[ST];  // raw scores of the current / next block (ping-pong across stages)
+#pragma unroll
+  for (int st = 0; st < ST; ++st) {
+    sa[st] = zero16();
+    sb[st] = zero16();
+  }
+  if (nblk > 0 && active(0)) {
+    scores(std::integral_constant<int, 0>{}, sa, [](auto) {});
+    if (needs_mask(0)) apply_mask(sa, 0);
+    float mx = kNegInf;
+#pragma unroll
+    for (int st = 0; st < ST; ++st)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sa[st][r]);
+    rescale(halves_max(mx) * p.scale2);
+  }
+
+  // One iteration: block jb's V tile in stage S, block jb + 1's K tile in
+  // stage S + 1.  sc holds block jb's raw scores, sn receives block jb + 1's.
+  auto step = [&](auto stage_c, int jb, f32x16 (&sc)[ST], f32x16 (&sn)[ST]) {
+    constexpr int S = decltype(stage_c)::value;
+    constexpr int SN = (S + 1) % NS;
+    if (jb + NS - 1 < nblk) issue(jb + NS - 1);
+    const bool a_c = active(jb);
+    const bool a_n = jb + 1 < nblk && active(jb + 1);
+    const float neg_m = (m_i == kNegInf) ? 0.f : -m_i;
+    if (a_c) {
+      // scores of block jb + 1 || exponents of block jb
+      if (a_n)
+        scores(std::integral_constant<int, SN>{}, sn, [&](auto ic) { exp_step(sc, neg_m, ic); });
+      else
+        static_for<NR>([&](auto ic) { exp_step(sc, neg_m, ic); });
+      V8 pb[PT];
+      pack_sum(sc, pb);
+      if (a_n && needs_mask(jb + 1)) apply_mask(sn, (jb + 1) * kBN);
+      // P V of block jb || row max of block jb + 1 (taken whether or not
+      // that block is active; only used when it is)
+      float mx[2] = {kNegInf, kNegInf};
+      pv(stage_c, pb, [&](auto ic) {
+        constexpr int I = decltype(ic)::value;
+#pragma unroll
+        for (int u = 0; u < MPP; u += 2) {
+          const int e = I * MPP + u;
+          mx[u / 2 % 2] = fmaxf(fmaxf(mx[u / 2 % 2], sn[e / 16][e % 16]), sn[(e + 1) / 16][(e + 1) % 16]);
+        }
+      });
+      if (a_n) rescale(halves_max(fmaxf(mx[0], mx[1])) * p.scale2);
+    }
+    if (jb + NS - 1 < nblk)
+      wait_vmcnt<kLoads>();
+    else
+      wait_vmcnt0();
+    lds_barrier();
+  };
+  for (int jb = 0; jb < nblk; jb += NS) {
+    step(std::integral_constant<int, 0>{}, jb, sa, sb);
+    if (jb + 1 < nblk) step(std::integral_constant<int, 1>{}, jb + 1, sb, sa);
+    if (jb + 2 < nblk) step(std::integral_constant<int, 2>{}, jb + 2, sa, sb);
+    if (jb + 3 < nblk) step(std::integral_constant<int, 3>{}, jb + 3, sb, sa);
+  }
+
+  // Epilogue: O = acc / l, LSE = (m + log2 l) ln 2.
+  if (!wave_valid) return;
+  const float l = halves_sum(l_i);
+  const bool has = l > 0.f;
+  const float inv = has ? 1.f / l : 0.f;
+  T* orow = (T*)p.o + qbase + (int64_t)qi * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) store_acc_t<T>(orow, acc[dt], 32 * dt, h, inv);
+  if (h == 0) p.lse[(int64_t)bh * p.M + qi] = has ? (m_i + log2f(l)) * kLn2 : kNegInf;
+}
+
 template <typename T, int D, int VAR>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
   FwdParams p;
@@ -489,10 +796,18 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
   p.sm_scale = a.sm_scale;
   p.w = a.w;
   dim3 grid(p.nmb * p.BH), block(FwdShape<VAR, D>::NT);
-  if (a.causal)
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, VAR, true>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((attn_fwd_kernel<T, D, VAR, false>), grid, block, 0, s, p);
+  if constexpr (VAR == PLAIN) {
+    static_assert(FwdShape<PLAIN, D>::NT == 64 * kPipeWaves, "same launch shape");
+    if (a.causal)
+      hipLaunchKernelGGL((attn_fwd_pipe_kernel<T, D, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((attn_fwd_pipe_kernel<T, D, false>), grid, block, 0, s, p);
+  } else {
+    if (a.causal)
+      hipLaunchKernelGGL((attn_fwd_kernel<T, D, VAR, true>), grid, block, 0, s, p);
+    else
+      hipLaunchKernelGGL((attn_fwd_kernel<T, D, VAR, false>), grid, block, 0, s, p);
+  }
   return hipGetLastError();
 }
 

@@ -38,9 +38,33 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 template <typename T> struct Vec8;
 template <> struct Vec8<__bf16> { typedef bf16x8 type; };
 template <> struct Vec8<_Float16> { typedef f16x8 type; };
+
+// acc + (sum of the 8 elements of v), as four pair dot products with (1, 1)
+// in fp32 (v_dot2c_f32_{bf16,f16}).
+__device__ __forceinline__ float add_sum8(float acc, const bf16x8& v) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 pr = {v[2 * i], v[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+  }
+  return acc;
+}
+__device__ __forceinline__ float add_sum8(float acc, const f16x8& v) {
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 pr = {v[2 * i], v[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2(pr, one, acc, false);
+  }
+  return acc;
+}
 
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
