@@ -135,24 +135,99 @@ __device__ __forceinline__ void tr_offsets(const TrLane& tl, uint32_t (&ofs)[D /
   }
 }
 
-// acc[dt] += X^t B over the d-tiles of a DTile X in LDS (transposing reads,
-// the reads of d-tile dt + 1 in flight during the products of d-tile dt).
-template <typename T, int D, int NOPS>
-__device__ __forceinline__ void accum_tr(f32x16 (&acc)[D / 32], uint32_t base, const uint32_t (&ofs)[D / 32][2],
+template <int V>
+using ic = std::integral_constant<int, V>;
+
+// Per-lane LDS addresses of the transposing reads: allocation base + the
+// lane's offsets (tr_offsets).
+template <int D>
+struct TrAddr {
+  uint32_t lo[D / 32][2];
+  __device__ __forceinline__ void init(const void* alloc, const TrLane& tl) {
+    uint32_t ofs[D / 32][2];
+    tr_offsets<D>(tl, ofs);
+    const uint32_t b = lds_addr(alloc);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      lo[dt][0] = b + ofs[dt][0];
+      lo[dt][1] = b + ofs[dt][1];
+    }
+  }
+};
+
+template <int D, int NOPS, int OFF>
+constexpr bool tr_fits() {
+  return OFF + (NOPS - 1) * 16 * D * 2 <= 65535;
+}
+
+// Issue the transposing reads of d-tile dt of the tile at byte offset OFF
+// inside the LDS allocation (tiles beyond the 16-bit immediate use the
+// addresses plus 32 KiB).
+template <typename T, int D, int NOPS, int OFF>
+__device__ __forceinline__ void tr_issue(TrOps<T, NOPS>& x, const TrAddr<D>& a, int dt) {
+  if constexpr (tr_fits<D, NOPS, OFF>()) {
+    x.template issue_imm<D, OFF>(a.lo[dt]);
+  } else {
+    static_assert(tr_fits<D, NOPS, OFF - 32768>(), "tile beyond the 96 KiB reach of the hi addresses");
+    const uint32_t hi[2] = {a.lo[dt][0] + 32768u, a.lo[dt][1] + 32768u};
+    x.template issue_imm<D, OFF - 32768>(hi);
+  }
+}
+
+// acc[dt] += X^t B over the d-tiles of the tile X at byte offset OFF of the
+// LDS allocation (transposing reads; the reads of d-tile dt + 1 are in
+// flight during the products of d-tile dt).
+template <typename T, int D, int NOPS, int OFF>
+__device__ __forceinline__ void accum_tr(f32x16 (&acc)[D / 32], const TrAddr<D>& a,
                                          const typename Vec8<T>::type (&b)[NOPS]) {
   constexpr int DT = D / 32;
   TrOps<T, NOPS> xa, xb;
-  xa.template issue_at<D>(base, ofs[0]);
+  tr_issue<T, D, NOPS, OFF>(xa, a, 0);
   xa.wait();
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
     TrOps<T, NOPS>& cx = (dt & 1) ? xb : xa;
     TrOps<T, NOPS>& nx = (dt & 1) ? xa : xb;
-    if (dt + 1 < DT) nx.template issue_at<D>(base, ofs[dt + 1]);
+    if (dt + 1 < DT) tr_issue<T, D, NOPS, OFF>(nx, a, dt + 1);
 #pragma unroll
     for (int t = 0; t < NOPS; ++t) acc[dt] = mfma32x32x16(cx.op[t], b[t], acc[dt]);
     __builtin_amdgcn_sched_barrier(0);
     if (dt + 1 < DT) nx.wait();
+  }
+}
+
+// Two such accumulations over the same d-tiles, interleaved (four products
+// per batch of reads): accA += XA^t bA, accB += XB^t bB.
+template <typename T, int D, int NOPS, int OFFA, int OFFB>
+__device__ __forceinline__ void accum_tr2(f32x16 (&accA)[D / 32], f32x16 (&accB)[D / 32], const TrAddr<D>& a,
+                                          const typename Vec8<T>::type (&bA)[NOPS],
+                                          const typename Vec8<T>::type (&bB)[NOPS]) {
+  constexpr int DT = D / 32;
+  TrOps<T, NOPS> xa, xb, ya, yb;
+  tr_issue<T, D, NOPS, OFFA>(xa, a, 0);
+  tr_issue<T, D, NOPS, OFFB>(ya, a, 0);
+  xa.wait();
+  ya.wait();
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    TrOps<T, NOPS>& cx = (dt & 1) ? xb : xa;
+    TrOps<T, NOPS>& nx = (dt & 1) ? xa : xb;
+    TrOps<T, NOPS>& cy = (dt & 1) ? yb : ya;
+    TrOps<T, NOPS>& ny = (dt & 1) ? ya : yb;
+    if (dt + 1 < DT) {
+      tr_issue<T, D, NOPS, OFFA>(nx, a, dt + 1);
+      tr_issue<T, D, NOPS, OFFB>(ny, a, dt + 1);
+    }
+#pragma unroll
+    for (int t = 0; t < NOPS; ++t) {
+      accA[dt] = mfma32x32x16(cx.op[t], bA[t], accA[dt]);
+      accB[dt] = mfma32x32x16(cy.op[t], bB[t], accB[dt]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (dt + 1 < DT) {
+      nx.wait();
+      ny.wait();
+    }
   }
 }
 
@@ -171,13 +246,13 @@ struct alignas(16) DkdvStage {
   using Sh = DkdvShape<D, VAR>;
   using Tile = DTile<T, Sh::QB, D, Sh::WAVES>;
   static constexpr int NQ = (VAR == PW) ? 2 : 1;
-  T q[NQ][Tile::ELEMS];       // Q (piecewise: Q1, Q2)
   T dout[Tile::ELEMS];
+  T q[NQ][Tile::ELEMS];       // Q (piecewise: Q1, Q2)
   float stats[2 * Sh::QB];    // LSE of the block's rows, then their Delta
 };
 
 template <typename T, int D, int VAR>
-struct alignas(16) DkdvSmem {
+struct alignas(256) DkdvSmem {
   using Sh = DkdvShape<D, VAR>;
   using VTile = DTile<T, 32, D, 1, false>;  // natural key order
   DkdvStage<T, D, VAR> st[Sh::NS];
@@ -201,6 +276,7 @@ void attn_dkdv_kernel(const BwdParams p) {
   using V8 = typename Vec8<T>::type;
   using Sm = DkdvSmem<T, D, VAR>;
   using St = DkdvStage<T, D, VAR>;
+  using Tile = typename St::Tile;
   using VTile = typename Sm::VTile;
   using Dma = DmaTile<T, QB, D, kWaves>;
   constexpr int KK = D / 16;   // 16-wide k steps over the head dim
@@ -209,6 +285,7 @@ void attn_dkdv_kernel(const BwdParams p) {
   constexpr int PT = QB / 16;  // 16-query operand slices per block
   constexpr bool kPw = VAR == PW;
   static_assert(sizeof(Sm) <= kLdsBytes, "LDS budget");
+  static_assert(NS == 3, "the ring loop is unrolled by three");
 
   __shared__ Sm smem;
 
@@ -264,12 +341,11 @@ void attn_dkdv_kernel(const BwdParams p) {
   dma.lane_offsets(wave, lane);
 
   // LSE / Delta rows of a block: 2 QB floats loaded with 4-byte direct loads,
-  // E of them per wave, so every wave issues exactly one such load.
+  // E of them per wave, so every wave issues exactly one such load.  A
+  // wave's E elements lie all in the LSE half or all in the Delta half (E
+  // divides QB), so the source array is the same for the whole wave.
   constexpr int E = 2 * QB / kWaves;
-  static_assert(64 % E == 0, "row statistics split");
-  // A wave's E elements lie all in the LSE half or all in the Delta half
-  // (E divides QB), so the source array is the same for the whole wave.
-  static_assert(QB % E == 0, "row statistics split");
+  static_assert(64 % E == 0 && QB % E == 0, "row statistics split");
   const int st_first = wave * E;
   const int st_ins = st_first / 64;
   const bool st_lane = lane >= st_first % 64 && lane < st_first % 64 + E;
@@ -321,6 +397,18 @@ void attn_dkdv_kernel(const BwdParams p) {
     wait_all_but(n_new);
   else
     wait_vmcnt0();
+  // The resident V tile is stored negated (each wave flips the sign bits of
+  // its own rows), so that the dP accumulator can start at +Delta:
+  // Delta + dO (-V)^t = -(dP - Delta), i.e. the pass computes -dS, and dK is
+  // stored with scale -sm_scale.
+  if (wave_valid) {
+    constexpr int kChunks = VTile::ELEMS * 2 / 16 / 64;
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      u32x4* c = reinterpret_cast<u32x4*>(smem.v[wave]) + i * 64 + lane;
+      *c = *c ^ 0x80008000u;
+    }
+  }
   lds_barrier();
 
   // Loop-invariant LDS byte offsets.  Row reads: row li, chunk 2 kk + h of a
@@ -328,28 +416,35 @@ void attn_dkdv_kernel(const BwdParams p) {
   uint32_t rofs[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) rofs[kk] = row_chunk_ofs<D>(li, 2 * kk + h);
-  const TrLane tl(lane);
-  uint32_t tofs[DT][2];
-  tr_offsets<D>(tl, tofs);
-  auto rd8 = [&](const T* tile, int st, int kk) -> V8 {
-    return *reinterpret_cast<const V8*>(reinterpret_cast<const char*>(tile) + rofs[kk] + st * 32 * D * 2);
+  TrAddr<D> tra;
+  tra.init(&smem, TrLane(lane));
+  const char* sbase = reinterpret_cast<const char*>(&smem);
+  auto rd8 = [&](int off, int kk) -> V8 {
+    return *reinterpret_cast<const V8*>(sbase + off + rofs[kk]);
   };
-  const T* vres = smem.v[wave];
-
-  // One query block for this wave; MASK selects the causal-diagonal path.
-  // Rows with LSE = -inf (no visible key) only occur in causal blocks whose
-  // every pair is masked, where P is set to 0 after the exponent.
+  const int voff = (int)(reinterpret_cast<const char*>(smem.v[wave]) - sbase);
   const float neg_inv_scale = -1.f / p.sm_scale;
-  auto block = [&](const St& cur, int i0, auto mask_tag) {
+
+  // One query block for this wave from stage S; MASK selects the
+  // causal-diagonal path.  Rows with LSE = -inf (no visible key) only occur
+  // in causal blocks whose every pair is masked, where P is set to 0 after
+  // the exponent.
+  auto block = [&](auto stage_c, int i0, auto mask_tag) {
+    constexpr int S = decltype(stage_c)::value;
     constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int kSt = (int)(__builtin_offsetof(Sm, st) + S * sizeof(St));
+    constexpr int kDo = kSt + (int)__builtin_offsetof(St, dout);
+    constexpr int kQ0 = kSt + (int)__builtin_offsetof(St, q);
+    constexpr int kQ1 = kQ0 + Tile::ELEMS * 2;
+    const St& cur = smem.st[S];
     bool an = true, af = false;
     if constexpr (kPw) pw_classify(i0, i0 + QB - 1, kw0, kw0 + 31, pshift, p.w, an, af);
     f32x16 s[ST], dp[ST], dsf[kPw ? ST : 1];
 #pragma unroll
     for (int st = 0; st < ST; ++st) {
       // The score accumulator starts at -LSE / sm_scale and the dP one at
-      // -Delta (this lane's 16 rows), so that scale2 * S is the exponent of P
-      // and dP - Delta comes out of the product.
+      // +Delta (this lane's 16 rows): scale2 * S is then the exponent of P
+      // and the second product gives -(dP - Delta).
       f32x16 sinit, dinit;
       {
         const f32x4* l4 = reinterpret_cast<const f32x4*>(cur.stats + 32 * st + 8 * h);
@@ -361,20 +456,21 @@ void attn_dkdv_kernel(const BwdParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             sinit[4 * g + e] = lv[e] * neg_inv_scale;
-            dinit[4 * g + e] = -dv[e];
+            dinit[4 * g + e] = dv[e];
           }
         }
       }
-      // scores S = Q K^t (rows: queries in swap23 order; column: this key)
+      const int so = st * 32 * D * 2;
       if constexpr (kPw) {
+        // scores S = Q K^t (rows: queries in swap23 order; column: this key)
         f32x16 s1 = sinit, s2 = sinit;
         if (!af) {
 #pragma unroll
-          for (int kk = 0; kk < KK; ++kk) s1 = mfma32x32x16(rd8(cur.q[0], st, kk), kf[kk], s1);
+          for (int kk = 0; kk < KK; ++kk) s1 = mfma32x32x16(rd8(kQ0 + so, kk), kf[kk], s1);
         }
         if (!an) {
 #pragma unroll
-          for (int kk = 0; kk < KK; ++kk) s2 = mfma32x32x16(rd8(cur.q[kPw ? 1 : 0], st, kk), k2f[kk], s2);
+          for (int kk = 0; kk < KK; ++kk) s2 = mfma32x32x16(rd8(kQ1 + so, kk), k2f[kk], s2);
         }
         if (an) {
           s[st] = s1;
@@ -387,15 +483,19 @@ void attn_dkdv_kernel(const BwdParams p) {
             s[st][r] = pw_near(row + pshift - kj, p.w) ? s1[r] : s2[r];
           }
         }
+        dp[st] = dinit;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) dp[st] = mfma32x32x16(rd8(kDo + so, kk), rd8(voff, kk), dp[st]);
       } else {
+        // S = Q K^t and Delta - dP = Delta + dO (-V)^t, interleaved
         s[st] = sinit;
+        dp[st] = dinit;
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) s[st] = mfma32x32x16(rd8(cur.q[0], st, kk), kf[kk], s[st]);
+        for (int kk = 0; kk < KK; ++kk) {
+          s[st] = mfma32x32x16(rd8(kQ0 + so, kk), kf[kk], s[st]);
+          dp[st] = mfma32x32x16(rd8(kDo + so, kk), rd8(voff, kk), dp[st]);
+        }
       }
-      // dP - Delta = dO V^t - Delta
-      dp[st] = dinit;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) dp[st] = mfma32x32x16(rd8(cur.dout, st, kk), rd8(vres, 0, kk), dp[st]);
       // causal mask: key kj is beyond row i0 + 32 st + perm_row(r, h)
       const int thr = kj - pshift - i0 - 32 * st - 8 * h;
 #pragma unroll
@@ -404,22 +504,22 @@ void attn_dkdv_kernel(const BwdParams p) {
         if constexpr (MASK) {
           if (thr > perm_row(r, 0)) pv = 0.f;
         }
-        const float ds = pv * dp[st][r];
+        const float nds = pv * dp[st][r];  // -dS
         s[st][r] = pv;
         if constexpr (kPw) {
           if (an) {
-            dp[st][r] = ds;
+            dp[st][r] = nds;
           } else if (af) {
             dp[st][r] = 0.f;
-            dsf[st][r] = ds;
+            dsf[st][r] = nds;
           } else {
             const int row = i0 + 32 * st + perm_row(r, h);
             const bool nr = pw_near(row + pshift - kj, p.w);
-            dp[st][r] = nr ? ds : 0.f;
-            dsf[st][r] = nr ? 0.f : ds;
+            dp[st][r] = nr ? nds : 0.f;
+            dsf[st][r] = nr ? 0.f : nds;
           }
         } else {
-          dp[st][r] = ds;
+          dp[st][r] = nds;
         }
       }
     }
@@ -430,46 +530,56 @@ void attn_dkdv_kernel(const BwdParams p) {
       dsb[t] = pack8<T>(dp[t >> 1], 8 * (t & 1));
       if constexpr (kPw) dsfb[t] = pack8<T>(dsf[t >> 1], 8 * (t & 1));
     }
-    // dV^t += dO^t P ;  dK^t += Q^t dS  (dK2^t += Q2^t dS_far)
-    accum_tr<T, D, PT>(dvt, lds_addr(cur.dout), tofs, pb);
-    if (!kPw || !af) accum_tr<T, D, PT>(dkt, lds_addr(cur.q[0]), tofs, dsb);
+    // dV^t += dO^t P ;  -dK^t += Q^t (-dS)  (-dK2^t += Q2^t (-dS_far))
     if constexpr (kPw) {
-      if (!an) accum_tr<T, D, PT>(dk2t, lds_addr(cur.q[kPw ? 1 : 0]), tofs, dsfb);
+      if (!af)
+        accum_tr2<T, D, PT, kDo, kQ0>(dvt, dkt, tra, pb, dsb);
+      else
+        accum_tr<T, D, PT, kDo>(dvt, tra, pb);
+      if (!an) accum_tr<T, D, PT, kQ1>(dk2t, tra, dsfb);
+    } else {
+      accum_tr2<T, D, PT, kDo, kQ0>(dvt, dkt, tra, pb, dsb);
     }
   };
 
   // Block qb is computed from stage qb % NS while block qb + NS - 1 is being
-  // loaded into the stage freed by block qb - 1.
-  int cur_stage = 0;
-  for (int qb = 0; qb < nq; ++qb) {
+  // loaded into the stage freed by block qb - 1.  The stage index is a
+  // compile-time constant in each of the three unrolled steps, so every LDS
+  // address is a per-lane register plus an immediate.
+  auto step = [&](auto stage_c, int qb) {
+    constexpr int S = decltype(stage_c)::value;
+    constexpr int LD = (S + NS - 1) % NS;
     const int ahead = qb + NS - 1;
-    int ld_stage = cur_stage + NS - 1;
-    if (ld_stage >= NS) ld_stage -= NS;
     const bool issued = ahead < nq;
-    if (issued) n_new = issue(smem.st[ld_stage], ahead);
+    if (issued) n_new = issue(smem.st[LD], ahead);
     const int i0 = q_begin + qb * QB;
     const bool active = wave_valid && (!CAUSAL || i0 + QB - 1 + pshift >= kw0);
     if (active) {
       if (CAUSAL && (kw0 + 31 > i0 + pshift))
-        block(smem.st[cur_stage], i0, std::true_type{});
+        block(stage_c, i0, std::true_type{});
       else
-        block(smem.st[cur_stage], i0, std::false_type{});
+        block(stage_c, i0, std::false_type{});
     }
     if (issued)
       wait_all_but(n_new);
     else
       wait_vmcnt0();
     lds_barrier();
-    cur_stage = (cur_stage + 1 == NS) ? 0 : cur_stage + 1;
+  };
+  for (int qb = 0; qb < nq; qb += NS) {
+    step(ic<0>{}, qb);
+    if (qb + 1 < nq) step(ic<1>{}, qb + 1);
+    if (qb + 2 < nq) step(ic<2>{}, qb + 2);
   }
 
   if (!wave_valid) return;
+  const float dk_scale = -p.sm_scale;
   const int64_t orow = kbase + (int64_t)kj * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
     store_acc_t<T>((T*)p.dv + orow, dvt[dt], 32 * dt, h, 1.f);
-    store_acc_t<T>((T*)p.dk + orow, dkt[dt], 32 * dt, h, p.sm_scale);
-    if constexpr (kPw) store_acc_t<T>((T*)p.dk2 + orow, dk2t[dt], 32 * dt, h, p.sm_scale);
+    store_acc_t<T>((T*)p.dk + orow, dkt[dt], 32 * dt, h, dk_scale);
+    if constexpr (kPw) store_acc_t<T>((T*)p.dk2 + orow, dk2t[dt], 32 * dt, h, dk_scale);
   }
 }
 
@@ -480,20 +590,19 @@ struct DqShape {
   static constexpr int NT = 64 * WAVES;
   static constexpr int BM = 32 * WAVES;  // queries per workgroup
   static constexpr int BN = 64;          // keys per streamed block
+  static constexpr int NS = 3;           // ring stages
 };
 
+// Ring of K (K1), K2 and V tiles, grouped by kind so that the transposing
+// reads of the K tiles have small immediate offsets.
 template <typename T, int D, int VAR>
-struct alignas(16) DqStage {
-  using Tile = DTile<T, DqShape<D, VAR>::BN, D, DqShape<D, VAR>::WAVES>;
+struct alignas(256) DqSmem {
+  using Sh = DqShape<D, VAR>;
+  using Tile = DTile<T, Sh::BN, D, Sh::WAVES>;
   static constexpr int NK = (VAR == PW) ? 2 : 1;
-  T k[NK][Tile::ELEMS];   // K (piecewise: K1, K2)
-  T v[Tile::ELEMS];
+  T k[NK][Sh::NS][Tile::ELEMS];  // K (piecewise: K1, K2)
+  T v[Sh::NS][Tile::ELEMS];
 };
-
-template <typename T, int D, int VAR>
-constexpr int dq_stages() {
-  return 3 * (int)sizeof(DqStage<T, D, VAR>) <= kLdsBytes ? 3 : 2;
-}
 
 template <int D, int VAR>
 constexpr int dq_waves_per_eu() {
@@ -508,17 +617,20 @@ void attn_dq_kernel(const BwdParams p) {
   constexpr int kWaves = Sh::WAVES;
   constexpr int BM = Sh::BM;
   constexpr int BN = Sh::BN;
-  constexpr int NS = dq_stages<T, D, VAR>();
+  constexpr int NS = Sh::NS;
   using V8 = typename Vec8<T>::type;
-  using St = DqStage<T, D, VAR>;
+  using Sm = DqSmem<T, D, VAR>;
+  using Tile = typename Sm::Tile;
   using Dma = DmaTile<T, BN, D, kWaves>;
   constexpr int KK = D / 16;
   constexpr int DT = D / 32;
   constexpr int ST = BN / 32;
   constexpr int PT = BN / 16;
   constexpr bool kPw = VAR == PW;
+  static_assert(sizeof(Sm) <= kLdsBytes, "LDS budget");
+  static_assert(NS == 3, "the ring loop is unrolled by three");
 
-  __shared__ St smem[NS];
+  __shared__ Sm smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -569,25 +681,27 @@ void attn_dq_kernel(const BwdParams p) {
   if (CAUSAL) n_end = min(p.N, wg_last_row + pshift + 1);
   const int nkb = n_end > 0 ? (n_end + BN - 1) / BN : 0;
 
-  auto issue = [&](St& st, int jb) -> int {
+  // Issue the direct loads of key block jb into ring stage S; returns the
+  // number of load instructions this wave issued.
+  auto issue = [&](int S, int jb) -> int {
     const int64_t off = (int64_t)jb * BN * D;
     int n = Dma::PER_WAVE;
     if constexpr (kPw) {
       bool an, af;
       pw_classify(m0, wg_last_row, jb * BN, jb * BN + BN - 1, pshift, p.w, an, af);
       if (!af) {
-        dma.load(gk + off, st.k[0], wave);
+        dma.load(gk + off, smem.k[0][S], wave);
         n += Dma::PER_WAVE;
       }
       if (!an) {
-        dma.load(gk2 + off, st.k[kPw ? 1 : 0], wave);
+        dma.load(gk2 + off, smem.k[kPw ? 1 : 0][S], wave);
         n += Dma::PER_WAVE;
       }
     } else {
-      dma.load(gk + off, st.k[0], wave);
+      dma.load(gk + off, smem.k[0][S], wave);
       n += Dma::PER_WAVE;
     }
-    dma.load(gv + off, st.v, wave);
+    dma.load(gv + off, smem.v[S], wave);
     return n;
   };
   auto wait_all_but = [&](int n) {
@@ -603,8 +717,8 @@ void attn_dq_kernel(const BwdParams p) {
   int n_new = 0;
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
-    if (j < nkb) n_new = issue(smem[j], j);
-  if (NS == 3 && nkb > 1)
+    if (j < nkb) n_new = issue(j, j);
+  if (nkb > 1)
     wait_all_but(n_new);
   else
     wait_vmcnt0();
@@ -613,32 +727,39 @@ void attn_dq_kernel(const BwdParams p) {
   uint32_t rofs[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) rofs[kk] = row_chunk_ofs<D>(li, 2 * kk + h);
-  const TrLane tl(lane);
-  uint32_t tofs[DT][2];
-  tr_offsets<D>(tl, tofs);
-  auto rd8 = [&](const T* tile, int st, int kk) -> V8 {
-    return *reinterpret_cast<const V8*>(reinterpret_cast<const char*>(tile) + rofs[kk] + st * 32 * D * 2);
+  TrAddr<D> tra;
+  tra.init(&smem, TrLane(lane));
+  const char* sbase = reinterpret_cast<const char*>(&smem);
+  auto rd8 = [&](int off, int kk) -> V8 {
+    return *reinterpret_cast<const V8*>(sbase + off + rofs[kk]);
   };
 
-  // One key block for this wave; MASK selects the causal-diagonal path.
-  auto block = [&](const St& cur, int n0, auto mask_tag) {
+  // One key block for this wave from stage S; MASK selects the
+  // causal-diagonal path.
+  auto block = [&](auto stage_c, int n0, auto mask_tag) {
+    constexpr int S = decltype(stage_c)::value;
     constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int kK0 = (int)(__builtin_offsetof(Sm, k) + S * Tile::ELEMS * 2);
+    constexpr int kK1 = kK0 + NS * Tile::ELEMS * 2;
+    constexpr int kV = (int)(__builtin_offsetof(Sm, v) + S * Tile::ELEMS * 2);
     bool an = true, af = false;
     if constexpr (kPw) pw_classify(row0, row0 + 31, n0, n0 + BN - 1, pshift, p.w, an, af);
     V8 dsb[PT], dsfb[kPw ? PT : 1];
 #pragma unroll
     for (int st = 0; st < ST; ++st) {
-      // S^t = K Q^t (rows: keys in swap23 order; column: this query)
-      f32x16 s;
+      const int so = st * 32 * D * 2;
+      // S^t = K Q^t (rows: keys in swap23 order; column: this query) and
+      // dP^t = V dO^t
+      f32x16 s, dp = zero16();
       if constexpr (kPw) {
         f32x16 s1 = zero16(), s2 = zero16();
         if (!af) {
 #pragma unroll
-          for (int kk = 0; kk < KK; ++kk) s1 = mfma32x32x16(rd8(cur.k[0], st, kk), qf[kk], s1);
+          for (int kk = 0; kk < KK; ++kk) s1 = mfma32x32x16(rd8(kK0 + so, kk), qf[kk], s1);
         }
         if (!an) {
 #pragma unroll
-          for (int kk = 0; kk < KK; ++kk) s2 = mfma32x32x16(rd8(cur.k[kPw ? 1 : 0], st, kk), q2f[kk], s2);
+          for (int kk = 0; kk < KK; ++kk) s2 = mfma32x32x16(rd8(kK1 + so, kk), q2f[kk], s2);
         }
         if (an) {
           s = s1;
@@ -651,15 +772,16 @@ void attn_dq_kernel(const BwdParams p) {
             s[r] = pw_near(qi + pshift - key, p.w) ? s1[r] : s2[r];
           }
         }
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) dp = mfma32x32x16(rd8(kV + so, kk), dof[kk], dp);
       } else {
         s = zero16();
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) s = mfma32x32x16(rd8(cur.k[0], st, kk), qf[kk], s);
+        for (int kk = 0; kk < KK; ++kk) {
+          s = mfma32x32x16(rd8(kK0 + so, kk), qf[kk], s);
+          dp = mfma32x32x16(rd8(kV + so, kk), dof[kk], dp);
+        }
       }
-      // dP^t = V dO^t
-      f32x16 dp = zero16();
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) dp = mfma32x32x16(rd8(cur.v, st, kk), dof[kk], dp);
       f32x16 dsf;
       // causal mask: key n0 + 32 st + perm_row(r, h) is beyond this query
       const int thr = qi + pshift - n0 - 32 * st - 8 * h;
@@ -694,33 +816,36 @@ void attn_dq_kernel(const BwdParams p) {
       }
     }
     // dQ^t += K^t dS^t  (dQ2^t += K2^t dS_far^t)
-    if (!kPw || !af) accum_tr<T, D, PT>(dqt, lds_addr(cur.k[0]), tofs, dsb);
+    if (!kPw || !af) accum_tr<T, D, PT, kK0>(dqt, tra, dsb);
     if constexpr (kPw) {
-      if (!an) accum_tr<T, D, PT>(dq2t, lds_addr(cur.k[kPw ? 1 : 0]), tofs, dsfb);
+      if (!an) accum_tr<T, D, PT, kK1>(dq2t, tra, dsfb);
     }
   };
 
-  int cur_stage = 0;
-  for (int jb = 0; jb < nkb; ++jb) {
+  auto step = [&](auto stage_c, int jb) {
+    constexpr int S = decltype(stage_c)::value;
+    constexpr int LD = (S + NS - 1) % NS;
     const int ahead = jb + NS - 1;
-    int ld_stage = cur_stage + NS - 1;
-    if (ld_stage >= NS) ld_stage -= NS;
     const bool issued = ahead < nkb;
-    if (issued) n_new = issue(smem[ld_stage], ahead);
+    if (issued) n_new = issue(LD, ahead);
     const int n0 = jb * BN;
     const bool active = wave_valid && (!CAUSAL || n0 <= row0 + 31 + pshift);
     if (active) {
       if (CAUSAL && (n0 + BN - 1 > row0 + pshift))
-        block(smem[cur_stage], n0, std::true_type{});
+        block(stage_c, n0, std::true_type{});
       else
-        block(smem[cur_stage], n0, std::false_type{});
+        block(stage_c, n0, std::false_type{});
     }
-    if (NS == 3 && issued)
+    if (issued)
       wait_all_but(n_new);
     else
       wait_vmcnt0();
     lds_barrier();
-    cur_stage = (cur_stage + 1 == NS) ? 0 : cur_stage + 1;
+  };
+  for (int jb = 0; jb < nkb; jb += NS) {
+    step(ic<0>{}, jb);
+    if (jb + 1 < nkb) step(ic<1>{}, jb + 1);
+    if (jb + 2 < nkb) step(ic<2>{}, jb + 2);
   }
 
   if (!wave_valid) return;
