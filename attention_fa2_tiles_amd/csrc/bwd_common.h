@@ -1,0 +1,172 @@
+// Pieces of the attention backward kernels: launch parameters, the
+// piecewise distance rule, and the LDS addressing and accumulation helpers
+// for transposing operand reads.
+// Everything here has internal linkage in each translation unit.
+#pragma once
+
+#include <type_traits>
+
+#include "common.h"
+
+namespace fa {
+namespace {
+
+constexpr int kBwdLdsBytes = 160 * 1024;
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* q2;
+  const void* k2;
+  const void* dout;
+  const float* lse;
+  const float* delta;
+  void* dq;
+  void* dk;
+  void* dv;
+  void* dq2;
+  void* dk2;
+  int BH, M, N, nblk;
+  float scale2;
+  float sm_scale;
+  int w;
+};
+
+// LSE in log2 units; a row that saw no key (LSE = -inf) gets +inf so that
+// exp2(s - lse2) is exactly 0 for it.
+__device__ __forceinline__ float lse_to_log2(float lse) {
+  return lse == kNegInf ? __builtin_huge_valf() : lse * kLog2e;
+}
+
+__device__ __forceinline__ bool pw_near(int dist, int w) { return dist <= w && dist >= -w; }
+
+// Block classification for the piecewise rule, rows [r_lo, r_hi] x keys
+// [c_lo, c_hi]: every pair near, every pair far, or mixed.
+__device__ __forceinline__ void pw_classify(int r_lo, int r_hi, int c_lo, int c_hi, int pshift, int w,
+                                            bool& all_near, bool& all_far) {
+  const int dmax = r_hi + pshift - c_lo;
+  const int dmin = r_lo + pshift - c_hi;
+  all_near = (dmax <= w) && (dmin >= -w);
+  all_far = (w < 0) || (dmin > w) || (dmax < -w);
+}
+
+// 16-byte row reads of a DTile: row m, chunk c, as a byte offset.
+template <int D>
+__device__ __forceinline__ uint32_t row_chunk_ofs(int m, int c) {
+  return (uint32_t)((m * D + ((c ^ swz<D>(m)) * 8)) * 2);
+}
+
+// Byte offsets of the transposing reads (TrOps::issue_at) of d-tile dt,
+// halves s = 0, 1, key/query group 0 of a swap23 DTile.
+template <int D>
+__device__ __forceinline__ void tr_offsets(const TrLane& tl, uint32_t (&ofs)[D / 32][2]) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const int m = swap23(8 * tl.hh + 4 * s2 + tl.r);
+      const int d = 32 * dt + tl.dcol;
+      ofs[dt][s2] = (uint32_t)((m * D + (((d >> 3) ^ swz<D>(m)) * 8) + (d & 7)) * 2);
+    }
+  }
+}
+
+template <int V>
+using ic = std::integral_constant<int, V>;
+
+// Per-lane LDS addresses of the transposing reads: allocation base + the
+// lane's offsets (tr_offsets).
+template <int D>
+struct TrAddr {
+  uint32_t lo[D / 32][2];
+  __device__ __forceinline__ void init(const void* alloc, const TrLane& tl) {
+    uint32_t ofs[D / 32][2];
+    tr_offsets<D>(tl, ofs);
+    const uint32_t b = lds_addr(alloc);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      lo[dt][0] = b + ofs[dt][0];
+      lo[dt][1] = b + ofs[dt][1];
+    }
+  }
+};
+
+template <int D, int NOPS, int OFF>
+constexpr bool tr_fits() {
+  return OFF + (NOPS - 1) * 16 * D * 2 <= 65535;
+}
+
+// Issue the transposing reads of d-tile dt of the tile at byte offset OFF
+// inside the LDS allocation (tiles beyond the 16-bit immediate use the
+// addresses plus 32 KiB).
+template <typename T, int D, int NOPS, int OFF>
+__device__ __forceinline__ void tr_issue(TrOps<T, NOPS>& x, const TrAddr<D>& a, int dt) {
+  if constexpr (tr_fits<D, NOPS, OFF>()) {
+    x.template issue_imm<D, OFF>(a.lo[dt]);
+  } else {
+    static_assert(tr_fits<D, NOPS, OFF - 32768>(), "tile beyond the 96 KiB reach of the hi addresses");
+    const uint32_t hi[2] = {a.lo[dt][0] + 32768u, a.lo[dt][1] + 32768u};
+    x.template issue_imm<D, OFF - 32768>(hi);
+  }
+}
+
+// acc[dt] += X^t B over the d-tiles of the tile X at byte offset OFF of the
+// LDS allocation (transposing reads; the reads of d-tile dt + 1 are in
+// flight during the products of d-tile dt).
+template <typename T, int D, int NOPS, int OFF>
+__device__ __forceinline__ void accum_tr(f32x16 (&acc)[D / 32], const TrAddr<D>& a,
+                                         const typename Vec8<T>::type (&b)[NOPS]) {
+  constexpr int DT = D / 32;
+  TrOps<T, NOPS> xa, xb;
+  tr_issue<T, D, NOPS, OFF>(xa, a, 0);
+  xa.wait();
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    TrOps<T, NOPS>& cx = (dt & 1) ? xb : xa;
+    TrOps<T, NOPS>& nx = (dt & 1) ? xa : xb;
+    if (dt + 1 < DT) tr_issue<T, D, NOPS, OFF>(nx, a, dt + 1);
+#pragma unroll
+    for (int t = 0; t < NOPS; ++t) acc[dt] = mfma32x32x16(cx.op[t], b[t], acc[dt]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (dt + 1 < DT) nx.wait();
+  }
+}
+
+// Two such accumulations over the same d-tiles, interleaved (four products
+// per batch of reads): accA += XA^t bA, accB += XB^t bB.
+template <typename T, int D, int NOPS, int OFFA, int OFFB>
+__device__ __forceinline__ void accum_tr2(f32x16 (&accA)[D / 32], f32x16 (&accB)[D / 32], const TrAddr<D>& a,
+                                          const typename Vec8<T>::type (&bA)[NOPS],
+                                          const typename Vec8<T>::type (&bB)[NOPS]) {
+  constexpr int DT = D / 32;
+  TrOps<T, NOPS> xa, xb, ya, yb;
+  tr_issue<T, D, NOPS, OFFA>(xa, a, 0);
+  tr_issue<T, D, NOPS, OFFB>(ya, a, 0);
+  xa.wait();
+  ya.wait();
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    TrOps<T, NOPS>& cx = (dt & 1) ? xb : xa;
+    TrOps<T, NOPS>& nx = (dt & 1) ? xa : xb;
+    TrOps<T, NOPS>& cy = (dt & 1) ? yb : ya;
+    TrOps<T, NOPS>& ny = (dt & 1) ? ya : yb;
+    if (dt + 1 < DT) {
+      tr_issue<T, D, NOPS, OFFA>(nx, a, dt + 1);
+      tr_issue<T, D, NOPS, OFFB>(ny, a, dt + 1);
+    }
+#pragma unroll
+    for (int t = 0; t < NOPS; ++t) {
+      accA[dt] = mfma32x32x16(cx.op[t], bA[t], accA[dt]);
+      accB[dt] = mfma32x32x16(cy.op[t], bB[t], accB[dt]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (dt + 1 < DT) {
+      nx.wait();
+      ny.wait();
+    }
+  }
+}
+
+}  // namespace
+}  // namespace fa
