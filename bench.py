@@ -127,8 +127,10 @@ def source_digest(paths):
 
 KERNEL_SOURCES = {
     "fwd": ["attention_fa2_tiles_amd/csrc/attn_fwd.hip", "attention_fa2_tiles_amd/csrc/common.h"],
-    "dkdv": ["attention_fa2_tiles_amd/csrc/attn_bwd.hip", "attention_fa2_tiles_amd/csrc/common.h"],
-    "dq": ["attention_fa2_tiles_amd/csrc/attn_bwd.hip", "attention_fa2_tiles_amd/csrc/common.h"],
+    "dkdv": ["attention_fa2_tiles_amd/csrc/attn_bwd.hip", "attention_fa2_tiles_amd/csrc/bwd_common.h",
+             "attention_fa2_tiles_amd/csrc/common.h"],
+    "dq": ["attention_fa2_tiles_amd/csrc/attn_bwd.hip", "attention_fa2_tiles_amd/csrc/bwd_common.h",
+           "attention_fa2_tiles_amd/csrc/common.h"],
     "delta": ["attention_fa2_tiles_amd/csrc/attn_bwd.hip"],
     "merge_fwd": ["attention_fa2_tiles_amd/csrc/merge.hip", "attention_fa2_tiles_amd/csrc/common.h"],
     "merge_bwd": ["attention_fa2_tiles_amd/csrc/merge.hip", "attention_fa2_tiles_amd/csrc/common.h"],
