@@ -273,8 +273,8 @@ void attn_dkdv_kernel(const BwdParams p) {
 
   // One query block for this wave from stage S; MASK selects the
   // causal-diagonal path.  Rows with LSE = -inf (no visible key) only occur
-  // in causal blocks whose every pair is masked, where P is set to 0 after
-  // the exponent.
+  // in causal blocks whose every pair is masked, where P is 0 (plain: the
+  // score starts at -inf; piecewise: P is set to 0 after the exponent).
   auto block = [&](auto stage_c, int i0, auto mask_tag) {
     constexpr int S = decltype(stage_c)::value;
     constexpr bool MASK = decltype(mask_tag)::value;
@@ -333,15 +333,24 @@ void attn_dkdv_kernel(const BwdParams p) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) dp[st] = mfma32x32x16(rd8(kDo + so, kk), rd8(voff, kk), dp[st]);
       } else {
-        // S = Q K^t and Delta - dP = Delta + dO (-V)^t, interleaved
+        // S = Q K^t and Delta - dP = Delta + dO (-V)^t, interleaved; on a
+        // causal diagonal block a pair whose key kj lies beyond its row
+        // i0 + 32 st + perm_row(r, h) starts at -inf, so that P = 0 there
         s[st] = sinit;
         dp[st] = dinit;
+        if constexpr (MASK) {
+          const int thr = kj - pshift - i0 - 32 * st - 8 * h;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (thr > perm_row(r, 0)) s[st][r] = kNegInf;
+        }
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           s[st] = mfma32x32x16(rd8(kQ0 + so, kk), kf[kk], s[st]);
           dp[st] = mfma32x32x16(rd8(kDo + so, kk), rd8(voff, kk), dp[st]);
         }
       }
+      if constexpr (!kPw) continue;  // plain: P / dS are formed during the accumulation below
       // causal mask: key kj is beyond row i0 + 32 st + perm_row(r, h)
       const int thr = kj - pshift - i0 - 32 * st - 8 * h;
 #pragma unroll
@@ -370,21 +379,69 @@ void attn_dkdv_kernel(const BwdParams p) {
       }
     }
     V8 pb[PT], dsb[PT], dsfb[kPw ? PT : 1];
-#pragma unroll
-    for (int t = 0; t < PT; ++t) {
-      pb[t] = pack8<T>(s[t >> 1], 8 * (t & 1));
-      dsb[t] = pack8<T>(dp[t >> 1], 8 * (t & 1));
-      if constexpr (kPw) dsfb[t] = pack8<T>(dsf[t >> 1], 8 * (t & 1));
-    }
-    // dV^t += dO^t P ;  -dK^t += Q^t (-dS)  (-dK2^t += Q2^t (-dS_far))
     if constexpr (kPw) {
+#pragma unroll
+      for (int t = 0; t < PT; ++t) {
+        pb[t] = pack8<T>(s[t >> 1], 8 * (t & 1));
+        dsb[t] = pack8<T>(dp[t >> 1], 8 * (t & 1));
+        dsfb[t] = pack8<T>(dsf[t >> 1], 8 * (t & 1));
+      }
+      // dV^t += dO^t P ;  -dK^t += Q^t (-dS_near) ;  -dK2^t += Q2^t (-dS_far)
       if (!af)
         accum_tr2<T, D, PT, kDo, kQ0>(dvt, dkt, tra, pb, dsb);
       else
         accum_tr<T, D, PT, kDo>(dvt, tra, pb);
       if (!an) accum_tr<T, D, PT, kQ1>(dk2t, tra, dsfb);
     } else {
-      accum_tr2<T, D, PT, kDo, kQ0>(dvt, dkt, tra, pb, dsb);
+      // P and -dS of operand slot t (8 rows of the score tile): exponent,
+      // product with Delta - dP, packing.  Element e of slot t is formed right after
+      // the e-th product of the accumulation of slot t - 1: a wave's vector
+      // work overlaps matrix work best when it sits between its own products
+      // (with two waves per SIMD); slot 0 has nothing before it to hide under.
+      constexpr int kPer = 8 / (2 * DT) > 0 ? 8 / (2 * DT) : 1;  // elements per product
+      static_assert(8 % (2 * DT) == 0 || 2 * DT % 8 == 0, "slot split");
+      auto element = [&](auto tc, auto ec) {
+        constexpr int t = decltype(tc)::value, e = decltype(ec)::value;
+        constexpr int st = t >> 1, r = 8 * (t & 1) + e;
+        const float pv = exp2_fast(s[st][r] * p.scale2);
+        dp[st][r] = pv * dp[st][r];  // -dS
+        s[st][r] = pv;
+        if constexpr (e == 7) {
+          pb[t] = pack8<T>(s[st], 8 * (t & 1));
+          dsb[t] = pack8<T>(dp[st], 8 * (t & 1));
+        }
+      };
+      static_for<8>([&](auto ec) { element(ic<0>{}, ec); });
+      // dV^t += dO^t P ;  -dK^t += Q^t (-dS), slot by slot, d-tile by d-tile;
+      // the two transposing operands of step k + 1 are read during step k.
+      TrOps<T, 1> xo[2], yo[2];
+      auto rd = [&](auto kc) {
+        constexpr int k = decltype(kc)::value, t = k / DT, dt = k % DT;
+        tr_issue<T, D, 1, kDo + t * 16 * D * 2>(xo[k & 1], tra, dt);
+        tr_issue<T, D, 1, kQ0 + t * 16 * D * 2>(yo[k & 1], tra, dt);
+      };
+      rd(ic<0>{});
+      static_for<PT * DT>([&](auto kc) {
+        constexpr int k = decltype(kc)::value, t = k / DT, dt = k % DT;
+        if constexpr (k + 1 < PT * DT) {
+          rd(ic<k + 1>{});
+          asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(xo[k & 1].op[0]), "+v"(yo[k & 1].op[0]));
+        } else {
+          asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(xo[k & 1].op[0]), "+v"(yo[k & 1].op[0]));
+        }
+        // elements of slot t + 1 placed after this step's two products
+        constexpr int e0 = 2 * dt * kPer;
+        dvt[dt] = mfma32x32x16(xo[k & 1].op[0], pb[t], dvt[dt]);
+        if constexpr (t + 1 < PT) {
+          static_for<kPer>([&](auto uc) { element(ic<t + 1>{}, ic<e0 + decltype(uc)::value>{}); });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        dkt[dt] = mfma32x32x16(yo[k & 1].op[0], dsb[t], dkt[dt]);
+        if constexpr (t + 1 < PT) {
+          static_for<kPer>([&](auto uc) { element(ic<t + 1>{}, ic<e0 + kPer + decltype(uc)::value>{}); });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
     }
   };
 
