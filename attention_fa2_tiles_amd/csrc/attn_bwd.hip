@@ -648,6 +648,79 @@ void attn_dq_kernel(const BwdParams p) {
     bool an = true, af = false;
     if constexpr (kPw) pw_classify(row0, row0 + 31, n0, n0 + BN - 1, pshift, p.w, an, af);
     V8 dsb[PT], dsfb[kPw ? PT : 1];
+    if constexpr (!kPw) {
+      // Plain: the vector work of each score tile is spread between matrix
+      // products that do not depend on it (a wave's vector work overlaps
+      // matrix work best when it sits between its own products, with two
+      // waves per SIMD): tile 0's P / dS between tile 1's score products,
+      // tile 1's between the dQ products of tile 0.  On a causal diagonal
+      // block a pair whose key n0 + 32 st + perm_row(r, h) lies beyond this
+      // query starts at -inf, so that P = 0 there.
+      static_assert(ST == 2 && PT == 4, "two score tiles of 32 keys");
+      f32x16 s[ST], dp[ST];
+#pragma unroll
+      for (int st = 0; st < ST; ++st) {
+        s[st] = zero16();
+        dp[st] = zero16();
+        if constexpr (MASK) {
+          const int thr = qi + pshift - n0 - 32 * st - 8 * h;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (perm_row(r, 0) > thr) s[st][r] = kNegInf;
+        }
+      }
+      // element r of tile st: P, dS = P (dP - Delta), packed per 8 rows
+      auto element = [&](auto stc, auto rc) {
+        constexpr int st = decltype(stc)::value, r = decltype(rc)::value;
+        const float pv = exp2_fast(fmaf(s[st][r], p.scale2, -lse2));
+        dp[st][r] = pv * (dp[st][r] - dl);
+        if constexpr (r % 8 == 7) dsb[2 * st + r / 8] = pack8<T>(dp[st], r - 7);
+      };
+      // S^t = K Q^t (rows: keys in swap23 order; column: this query) and
+      // dP^t = V dO^t of tile st; after product pair kk, between(kk)
+      auto products = [&](auto stc, auto&& between) {
+        constexpr int st = decltype(stc)::value;
+        constexpr int so = st * 32 * D * 2;
+        static_for<KK>([&](auto kc) {
+          constexpr int kk = decltype(kc)::value;
+          s[st] = mfma32x32x16(rd8(kK0 + so, kk), qf[kk], s[st]);
+          dp[st] = mfma32x32x16(rd8(kV + so, kk), dof[kk], dp[st]);
+          between(kc);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      };
+      products(ic<0>{}, [](auto) {});
+      constexpr int kPerKK = 16 / KK;  // tile-0 elements per product pair
+      products(ic<1>{}, [&](auto kc) {
+        constexpr int kk = decltype(kc)::value;
+        static_for<kPerKK>([&](auto uc) { element(ic<0>{}, ic<kk * kPerKK + decltype(uc)::value>{}); });
+      });
+      // dQ^t += K^t dS^t slot by slot, d-tile by d-tile; the transposing
+      // operand of step k + 1 is read during step k; tile 1's elements sit
+      // between the products of slots 0 and 1.
+      TrOps<T, 1> ko[2];
+      auto rd = [&](auto kc) {
+        constexpr int k = decltype(kc)::value, t = k / DT, dt = k % DT;
+        tr_issue<T, D, 1, kK0 + t * 16 * D * 2>(ko[k & 1], tra, dt);
+      };
+      constexpr int kPerStep = 16 / (2 * DT);  // tile-1 elements per product of slots 0, 1
+      rd(ic<0>{});
+      static_for<PT * DT>([&](auto kc) {
+        constexpr int k = decltype(kc)::value, t = k / DT, dt = k % DT;
+        if constexpr (k + 1 < PT * DT) {
+          rd(ic<k + 1>{});
+          asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(ko[k & 1].op[0]));
+        } else {
+          asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(ko[k & 1].op[0]));
+        }
+        dqt[dt] = mfma32x32x16(ko[k & 1].op[0], dsb[t], dqt[dt]);
+        if constexpr (t < 2) {
+          static_for<kPerStep>([&](auto uc) { element(ic<1>{}, ic<k * kPerStep + decltype(uc)::value>{}); });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+      return;
+    }
 #pragma unroll
     for (int st = 0; st < ST; ++st) {
       const int so = st * 32 * D * 2;
