@@ -47,7 +47,6 @@ int check_attn_shape(int B, int H, int M, int N, int D) {
   if (bh > (1 << 24) || M > (1 << 24) || N > (1 << 24)) return FA_ERR_SHAPE;
   if (bh * (int64_t)(M > N ? M : N) * D > ((int64_t)1 << 46)) return FA_ERR_SHAPE;
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
-  if (M % 64 != 0 || N % 64 != 0) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 

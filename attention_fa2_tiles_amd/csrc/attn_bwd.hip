@@ -110,7 +110,9 @@ constexpr int dkdv_waves_per_eu() {
   return DkdvShape<D, VAR>::WAVES / 4;
 }
 
-template <typename T, int D, int VAR, bool CAUSAL>
+// RAGGED: M or N is not a multiple of 64 (the tail handling is compiled only
+// into these instantiations).
+template <typename T, int D, int VAR, bool CAUSAL, bool RAGGED>
 __global__ __launch_bounds__((DkdvShape<D, VAR>::NT))
 __attribute__((amdgpu_waves_per_eu(dkdv_waves_per_eu<D, VAR>(), dkdv_waves_per_eu<D, VAR>())))
 void attn_dkdv_kernel(const BwdParams p) {
@@ -154,11 +156,16 @@ void attn_dkdv_kernel(const BwdParams p) {
   const int64_t lbase = (int64_t)bh * p.M;
 
   // Resident operands: this wave's 32 rows of V in LDS, K (K1, K2) columns
-  // in registers (lane li feeds key kj).
+  // in registers (lane li feeds key kj).  Keys past the last one read the
+  // last key; their columns are not stored.
   V8 kf[KK], k2f[kPw ? KK : 1];
   if (wave_valid) {
-    VTile::load(smem.v[wave], (const T*)p.v + kbase + (int64_t)kw0 * D, 0, lane);
-    const int64_t off = kbase + (int64_t)kj * D + 8 * h;
+    const T* vsrc = (const T*)p.v + kbase + (int64_t)kw0 * D;
+    if (!RAGGED || p.N - kw0 >= 32)
+      VTile::load(smem.v[wave], vsrc, 0, lane);
+    else
+      VTile::load_lim(smem.v[wave], vsrc, 0, lane, p.N - kw0);
+    const int64_t off = kbase + (int64_t)(RAGGED ? min(kj, p.N - 1) : kj) * D + 8 * h;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       kf[kk] = *reinterpret_cast<const V8*>((const T*)p.k + off + 16 * kk);
@@ -195,32 +202,45 @@ void attn_dkdv_kernel(const BwdParams p) {
   const int st_first = wave * E;
   const int st_ins = st_first / 64;
   const bool st_lane = lane >= st_first % 64 && lane < st_first % 64 + E;
-  const float* st_src = (st_first < QB ? p.lse + lbase + st_ins * 64 : p.delta + lbase + (st_ins * 64 - QB));
+  const float* st_src = (st_first < QB ? p.lse : p.delta) + lbase;
+  const int st_row = lane + (st_first < QB ? st_ins * 64 : st_ins * 64 - QB);  // row within a block
 
   // Issue the direct loads of query block qb into stage st; returns the
   // number of vector-memory instructions this wave issued.
+  auto tload = [&](const T* g, T* lds, int nr) {
+    if constexpr (RAGGED)
+      dma.load_rows(g, lds, wave, lane, nr);
+    else
+      dma.load(g, lds, wave);
+  };
   auto issue = [&](St& st, int qb) -> int {
     const int i0 = q_begin + qb * QB;
     const int64_t off = (int64_t)i0 * D;
     int n = Dma::PER_WAVE + 1;
+    const int nr = p.M - i0;  // rows of this block that exist
     if constexpr (kPw) {
       bool an, af;
       pw_classify(i0, i0 + QB - 1, n0, wg_key_hi, pshift, p.w, an, af);
       if (!af) {
-        dma.load(gq + off, st.q[0], wave);
+        tload(gq + off, st.q[0], nr);
         n += Dma::PER_WAVE;
       }
       if (!an) {
-        dma.load(gq2 + off, st.q[kPw ? 1 : 0], wave);
+        tload(gq2 + off, st.q[kPw ? 1 : 0], nr);
         n += Dma::PER_WAVE;
       }
     } else {
-      dma.load(gq + off, st.q[0], wave);
+      tload(gq + off, st.q[0], nr);
       n += Dma::PER_WAVE;
     }
-    dma.load(gdo + off, st.dout, wave);
+    tload(gdo + off, st.dout, nr);
+    // (a row past the last one gets LSE = +inf, so P = 0 for all of it, and
+    // Delta = 0; its Q and dO rows load as zeros)
+    const float* st_ptr = (!RAGGED || i0 + st_row < p.M)
+                              ? st_src + (i0 + st_row)
+                              : (st_first < QB ? &kPosInfF : reinterpret_cast<const float*>(kZero16));
     if (st_lane)
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(st_src + (i0 + lane)),
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)st_ptr,
                                        (void __attribute__((address_space(3)))*)(st.stats + st_ins * 64), 4, 0,
                                        0);
     return n;
@@ -475,7 +495,7 @@ void attn_dkdv_kernel(const BwdParams p) {
     if (qb + 2 < nq) step(ic<2>{}, qb + 2);
   }
 
-  if (!wave_valid) return;
+  if (!wave_valid || (RAGGED && kj >= p.N)) return;  // keys past the last one
   const float dk_scale = -p.sm_scale;
   const int64_t orow = kbase + (int64_t)kj * D;
 #pragma unroll
@@ -512,7 +532,7 @@ constexpr int dq_waves_per_eu() {
   return DqShape<D, VAR>::WAVES / 4;
 }
 
-template <typename T, int D, int VAR, bool CAUSAL>
+template <typename T, int D, int VAR, bool CAUSAL, bool RAGGED>
 __global__ __launch_bounds__((DqShape<D, VAR>::NT))
 __attribute__((amdgpu_waves_per_eu(dq_waves_per_eu<D, VAR>(), dq_waves_per_eu<D, VAR>())))
 void attn_dq_kernel(const BwdParams p) {
@@ -558,18 +578,20 @@ void attn_dq_kernel(const BwdParams p) {
   dma.lane_offsets(wave, lane);
 
   // Query-side operands stay in registers for the whole pass.
+  // (lanes past the last query row read that row; their results are not stored)
   V8 qf[KK], q2f[kPw ? KK : 1], dof[KK];
   float lse2 = __builtin_huge_valf(), dl = 0.f;
+  const int qr = RAGGED ? min(qi, p.M - 1) : qi;
   if (wave_valid) {
-    const int64_t off = qbase + (int64_t)qi * D + 8 * h;
+    const int64_t off = qbase + (int64_t)qr * D + 8 * h;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       qf[kk] = *reinterpret_cast<const V8*>((const T*)p.q + off + 16 * kk);
       dof[kk] = *reinterpret_cast<const V8*>((const T*)p.dout + off + 16 * kk);
       if constexpr (kPw) q2f[kk] = *reinterpret_cast<const V8*>((const T*)p.q2 + off + 16 * kk);
     }
-    lse2 = lse_to_log2(p.lse[(int64_t)bh * p.M + qi]);
-    dl = p.delta[(int64_t)bh * p.M + qi];
+    lse2 = lse_to_log2(p.lse[(int64_t)bh * p.M + qr]);
+    dl = p.delta[(int64_t)bh * p.M + qr];
   }
 
   f32x16 dqt[DT], dq2t[kPw ? DT : 1];
@@ -586,25 +608,32 @@ void attn_dq_kernel(const BwdParams p) {
 
   // Issue the direct loads of key block jb into ring stage S; returns the
   // number of load instructions this wave issued.
+  auto tload = [&](const T* g, T* lds, int nr) {
+    if constexpr (RAGGED)
+      dma.load_rows(g, lds, wave, lane, nr);
+    else
+      dma.load(g, lds, wave);
+  };
   auto issue = [&](int S, int jb) -> int {
     const int64_t off = (int64_t)jb * BN * D;
+    const int nr = p.N - jb * BN;  // rows of this block that exist
     int n = Dma::PER_WAVE;
     if constexpr (kPw) {
       bool an, af;
       pw_classify(m0, wg_last_row, jb * BN, jb * BN + BN - 1, pshift, p.w, an, af);
       if (!af) {
-        dma.load(gk + off, smem.k[0][S], wave);
+        tload(gk + off, smem.k[0][S], nr);
         n += Dma::PER_WAVE;
       }
       if (!an) {
-        dma.load(gk2 + off, smem.k[kPw ? 1 : 0][S], wave);
+        tload(gk2 + off, smem.k[kPw ? 1 : 0][S], nr);
         n += Dma::PER_WAVE;
       }
     } else {
-      dma.load(gk + off, smem.k[0][S], wave);
+      tload(gk + off, smem.k[0][S], nr);
       n += Dma::PER_WAVE;
     }
-    dma.load(gv + off, smem.v[S], wave);
+    tload(gv + off, smem.v[S], nr);
     return n;
   };
   auto wait_all_but = [&](int n) {
@@ -669,10 +698,15 @@ void attn_dq_kernel(const BwdParams p) {
             if (perm_row(r, 0) > thr) s[st][r] = kNegInf;
         }
       }
-      // element r of tile st: P, dS = P (dP - Delta), packed per 8 rows
+      // element r of tile st: P, dS = P (dP - Delta), packed per 8 rows.  The
+      // exponent is at most 0 for every key that exists (LSE bounds each of
+      // its row's scores); with ragged lengths it is clamped there, so that a
+      // zero-filled key past the last one (S = 0) cannot overflow P when LSE
+      // is very negative (its dS then meets a zero K row).
       auto element = [&](auto stc, auto rc) {
         constexpr int st = decltype(stc)::value, r = decltype(rc)::value;
-        const float pv = exp2_fast(fmaf(s[st][r], p.scale2, -lse2));
+        const float x = fmaf(s[st][r], p.scale2, -lse2);
+        const float pv = exp2_fast(RAGGED ? fminf(x, 0.f) : x);
         dp[st][r] = pv * (dp[st][r] - dl);
         if constexpr (r % 8 == 7) dsb[2 * st + r / 8] = pack8<T>(dp[st], r - 7);
       };
@@ -763,7 +797,9 @@ void attn_dq_kernel(const BwdParams p) {
       const int thr = qi + pshift - n0 - 32 * st - 8 * h;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pv = exp2_fast(fmaf(s[r], p.scale2, -lse2));
+        // (clamped as in the plain path: a zero-filled key past the last one)
+        const float x = fmaf(s[r], p.scale2, -lse2);
+        float pv = exp2_fast(RAGGED ? fminf(x, 0.f) : x);
         if constexpr (MASK) {
           if (perm_row(r, 0) > thr) pv = 0.f;
         }
@@ -824,7 +860,7 @@ void attn_dq_kernel(const BwdParams p) {
     if (jb + 2 < nkb) step(ic<2>{}, jb + 2);
   }
 
-  if (!wave_valid) return;
+  if (!wave_valid || (RAGGED && qi >= p.M)) return;  // lanes past the last query row
   const int64_t orow = qbase + (int64_t)qi * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
@@ -864,10 +900,15 @@ hipError_t dkdv_t(const BwdArgs& a, hipStream_t s) {
   BwdParams p = make_params(a);
   p.nblk = (a.N + Sh::KB - 1) / Sh::KB;
   dim3 grid(p.nblk * p.BH), block(Sh::NT);
-  if (a.causal)
-    hipLaunchKernelGGL((attn_dkdv_kernel<T, D, VAR, true>), grid, block, 0, s, p);
+  const bool ragged = a.M % 64 != 0 || a.N % 64 != 0;
+  if (a.causal && ragged)
+    hipLaunchKernelGGL((attn_dkdv_kernel<T, D, VAR, true, true>), grid, block, 0, s, p);
+  else if (a.causal)
+    hipLaunchKernelGGL((attn_dkdv_kernel<T, D, VAR, true, false>), grid, block, 0, s, p);
+  else if (ragged)
+    hipLaunchKernelGGL((attn_dkdv_kernel<T, D, VAR, false, true>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((attn_dkdv_kernel<T, D, VAR, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((attn_dkdv_kernel<T, D, VAR, false, false>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
@@ -877,10 +918,15 @@ hipError_t dq_t(const BwdArgs& a, hipStream_t s) {
   BwdParams p = make_params(a);
   p.nblk = (a.M + Sh::BM - 1) / Sh::BM;
   dim3 grid(p.nblk * p.BH), block(Sh::NT);
-  if (a.causal)
-    hipLaunchKernelGGL((attn_dq_kernel<T, D, VAR, true>), grid, block, 0, s, p);
+  const bool ragged = a.M % 64 != 0 || a.N % 64 != 0;
+  if (a.causal && ragged)
+    hipLaunchKernelGGL((attn_dq_kernel<T, D, VAR, true, true>), grid, block, 0, s, p);
+  else if (a.causal)
+    hipLaunchKernelGGL((attn_dq_kernel<T, D, VAR, true, false>), grid, block, 0, s, p);
+  else if (ragged)
+    hipLaunchKernelGGL((attn_dq_kernel<T, D, VAR, false, true>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((attn_dq_kernel<T, D, VAR, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((attn_dq_kernel<T, D, VAR, false, false>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 

@@ -82,7 +82,9 @@ constexpr int fwd_waves_per_eu() {
   return FwdShape<VAR, D>::WAVES / 4;
 }
 
-template <typename T, int D, int VAR, bool CAUSAL>
+// RAGGED: M or N is not a multiple of 64 (the tail handling is compiled only
+// into these instantiations, so the common case runs none of it).
+template <typename T, int D, int VAR, bool CAUSAL, bool RAGGED>
 __global__ __launch_bounds__((FwdShape<VAR, D>::NT))
 __attribute__((amdgpu_waves_per_eu(fwd_waves_per_eu<VAR, D>(), fwd_waves_per_eu<VAR, D>())))
 void attn_fwd_kernel(const FwdParams p) {
@@ -132,20 +134,27 @@ void attn_fwd_kernel(const FwdParams p) {
   const int wg_last_row = min(p.M, m0 + kBM) - 1;
   if (CAUSAL) n_end = min(p.N, wg_last_row + pshift + 1);
   const int nblk = n_end > 0 ? (n_end + kBN - 1) / kBN : 0;
+  // Non-causal with a partial last key block: that block is visited first,
+  // in a peeled iteration, so that the loop never needs the mask (causal:
+  // the diagonal mask already hides every key past the last one).
+  const bool tail_first = RAGGED && !CAUSAL && p.N % kBN != 0;
+  auto key_block = [&](int jb) { return tail_first ? (jb == 0 ? nblk - 1 : jb - 1) : jb; };
 
   // Query-side operands stay in registers for the whole pass.
+  // (lanes past the last query row read that row; their results are not stored)
   V8 qf[KK], q2f[kPw ? KK : 1], tqf[kJvp ? KK : 1];
+  const int qr = RAGGED ? min(qi, p.M - 1) : qi;
   if (wave_valid) {
-    const T* qrow = (const T*)p.q + qbase + (int64_t)qi * D + 8 * h;
+    const T* qrow = (const T*)p.q + qbase + (int64_t)qr * D + 8 * h;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const V8*>(qrow + 16 * kk);
     if constexpr (kPw) {
-      const T* q2row = (const T*)p.q2 + qbase + (int64_t)qi * D + 8 * h;
+      const T* q2row = (const T*)p.q2 + qbase + (int64_t)qr * D + 8 * h;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) q2f[kk] = *reinterpret_cast<const V8*>(q2row + 16 * kk);
     }
     if constexpr (kJvp) {
-      const T* tqrow = (const T*)p.tq + qbase + (int64_t)qi * D + 8 * h;
+      const T* tqrow = (const T*)p.tq + qbase + (int64_t)qr * D + 8 * h;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) tqf[kk] = *reinterpret_cast<const V8*>(tqrow + 16 * kk);
     }
@@ -192,27 +201,35 @@ void attn_fwd_kernel(const FwdParams p) {
   // Issue the direct loads of K/V block jb into stage st (completion:
   // vmcnt); returns the number of load instructions this wave issued.
   constexpr int kTileLoads = DmaTile<T, kBN, D, kWaves>::PER_WAVE;
+  auto tload = [&](const T* g, T* lds, int nr) {
+    if constexpr (RAGGED)
+      dma.load_rows(g, lds, wave, lane, nr);
+    else
+      dma.load(g, lds, wave);
+  };
   auto issue = [&](St& st, int jb) -> int {
-    const int64_t off = (int64_t)jb * kBN * D;
+    const int kb = key_block(jb);
+    const int64_t off = (int64_t)kb * kBN * D;
+    const int nr = p.N - kb * kBN;  // rows of this block that exist
     int n = kTileLoads * St::NV;
     if constexpr (kPw) {
       bool an, af;
-      pw_class(m0, wg_last_row, jb * kBN, an, af);
+      pw_class(m0, wg_last_row, kb * kBN, an, af);
       if (!af) {
-        dma.load(gk + off, st.k[0], wave);
+        tload(gk + off, st.k[0], nr);
         n += kTileLoads;
       }
       if (!an) {
-        dma.load(gk2 + off, st.k[1], wave);
+        tload(gk2 + off, st.k[1], nr);
         n += kTileLoads;
       }
     } else {
-      dma.load(gk + off, st.k[0], wave);
-      if constexpr (kJvp) dma.load(gk2 + off, st.k[1], wave);
+      tload(gk + off, st.k[0], nr);
+      if constexpr (kJvp) tload(gk2 + off, st.k[1], nr);
       n += kTileLoads * St::NK;
     }
-    dma.load(gv + off, st.v[0], wave);
-    if constexpr (kJvp) dma.load(gv2 + off, st.v[1], wave);
+    tload(gv + off, st.v[0], nr);
+    if constexpr (kJvp) tload(gv2 + off, st.v[1], nr);
     return n;
   };
   // Wait until every load but the newest n (one block's) has landed; loads
@@ -317,8 +334,9 @@ void attn_fwd_kernel(const FwdParams p) {
     if constexpr (MASK) {
 #pragma unroll
       for (int st = 0; st < ST; ++st) {
-        // key n0 + 32 st + perm_row(r, h) is beyond this query
-        const int thr = qi + pshift - n0 - 32 * st - 8 * h;
+        // key n0 + 32 st + perm_row(r, h) is beyond this query (causal) or
+        // beyond the last key
+        const int thr = (CAUSAL ? (RAGGED ? min(qi + pshift, p.N - 1) : qi + pshift) : p.N - 1) - n0 - 32 * st - 8 * h;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           if (perm_row(r, 0) > thr) s[st][r] = kNegInf;
@@ -423,16 +441,16 @@ void attn_fwd_kernel(const FwdParams p) {
   // wave waits until its loads of block jb + 1 have landed, leaving those of
   // the newest block in flight (loads complete in issue order).
   int cur_stage = 0;
-  for (int jb = 0; jb < nblk; ++jb) {
+  auto iteration = [&](int jb, auto tail_tag) {
     const int ahead = jb + NS - 1;
     int ld_stage = cur_stage + NS - 1;
     if (ld_stage >= NS) ld_stage -= NS;
     const bool issued = ahead < nblk;
     if (issued) n_new = issue(smem[ld_stage], ahead);
-    const int n0 = jb * kBN;
+    const int n0 = key_block(jb) * kBN;
     const bool active = wave_valid && (!CAUSAL || n0 <= row0 + 31 + pshift);
     if (active) {
-      if (CAUSAL && (n0 + kBN - 1 > row0 + pshift))
+      if (decltype(tail_tag)::value || (CAUSAL && (n0 + kBN - 1 > row0 + pshift)))
         block(smem[cur_stage], n0, std::true_type{});
       else
         block(smem[cur_stage], n0, std::false_type{});
@@ -443,7 +461,15 @@ void attn_fwd_kernel(const FwdParams p) {
       wait_vmcnt0();
     lds_barrier();
     cur_stage = (cur_stage + 1 == NS) ? 0 : cur_stage + 1;
+  };
+  int jb0 = 0;
+  if constexpr (RAGGED) {
+    if (tail_first && nblk > 0) {
+      iteration(0, std::true_type{});
+      jb0 = 1;
+    }
   }
+  for (int jb = jb0; jb < nblk; ++jb) iteration(jb, std::false_type{});
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----------------------
   // Waves whose rows lie beyond M (last query block of a head) store nothing.
@@ -451,6 +477,7 @@ void attn_fwd_kernel(const FwdParams p) {
   const float l = halves_sum(l_i);
   const bool has = l > 0.f;
   const float inv = has ? 1.f / l : 0.f;
+  if (RAGGED && qi >= p.M) return;  // lanes past the last query row
   T* orow = (T*)p.o + qbase + (int64_t)qi * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) store_acc_t<T>(orow, acc[dt], 32 * dt, h, inv);
@@ -492,7 +519,7 @@ struct alignas(256) PipeSmem {
   T v[kPipeNS][Tile::ELEMS];
 };
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, bool RAGGED>
 __global__ __launch_bounds__(64 * kPipeWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_pipe_kernel(const FwdParams p) {
   constexpr int kWaves = kPipeWaves;
@@ -544,10 +571,21 @@ void attn_fwd_pipe_kernel(const FwdParams p) {
   const int wg_last_row = min(p.M, m0 + kBM) - 1;
   if (CAUSAL) n_end = min(p.N, wg_last_row + pshift + 1);
   const int nblk = n_end > 0 ? (n_end + kBN - 1) / kBN : 0;
+  // A partial last key block.  Non-causal: it is visited first (its mask is
+  // applied in the prologue, never in the loop).  Causal: its tile is the
+  // 64 keys ending at key N - 1 (all of them exist, so the loads need no
+  // per-lane tail code); the keys it shares with the block before are masked
+  // from below, and the diagonal mask hides every key past the last one.
+  const bool tail_first = RAGGED && !CAUSAL && p.N % kBN != 0;
+  auto key_block = [&](int jb) { return tail_first ? (jb == 0 ? nblk - 1 : jb - 1) : jb; };
+  auto tile_start = [&](int kb) {
+    return (RAGGED && CAUSAL && kb * kBN + kBN > p.N && p.N >= kBN) ? p.N - kBN : kb * kBN;
+  };
 
+  // (lanes past the last query row read that row; their results are not stored)
   V8 qf[KK];
   if (wave_valid) {
-    const T* qrow = (const T*)p.q + qbase + (int64_t)qi * D + 8 * h;
+    const T* qrow = (const T*)p.q + qbase + (int64_t)(RAGGED ? min(qi, p.M - 1) : qi) * D + 8 * h;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const V8*>(qrow + 16 * kk);
   }
@@ -579,11 +617,21 @@ void attn_fwd_pipe_kernel(const FwdParams p) {
     }
   }
 
-  auto issue = [&](int jb) {
+  // (CHK: the tile may lack rows: only in the prologue, since in the loop
+  // every tile lies inside the keys)
+  auto issue = [&](int jb, auto chk) {
     const int st = jb % NS;
-    const int64_t off = (int64_t)jb * kBN * D;
-    dma.load(gk + off, smem.k[st], wave);
-    dma.load(gv + off, smem.v[st], wave);
+    const int kb = key_block(jb);
+    const int t0 = tile_start(kb);
+    const int64_t off = (int64_t)t0 * D;
+    if constexpr (RAGGED && decltype(chk)::value) {
+      const int nr = p.N - t0;  // rows of this tile that exist
+      dma.load_rows(gk + off, smem.k[st], wave, lane, nr);
+      dma.load_rows(gv + off, smem.v[st], wave, lane, nr);
+    } else {
+      dma.load(gk + off, smem.k[st], wave);
+      dma.load(gv + off, smem.v[st], wave);
+    }
   };
   constexpr int kLoads = 2 * Dma::PER_WAVE;
   auto active = [&](int jb) { return wave_valid && (!CAUSAL || jb * kBN <= row0 + 31 + pshift); };
@@ -623,14 +671,18 @@ void attn_fwd_pipe_kernel(const FwdParams p) {
     });
   };
 
-  // Causal mask of a block's raw scores (keys beyond this query -> -inf).
-  auto apply_mask = [&](f32x16 (&sc)[ST], int n0) {
+  // Mask of the raw scores of key block kb (tile from key t0): keys beyond
+  // this query (causal) or beyond the last key (non-causal), and keys of the
+  // block before (a causal tail tile starts before kb * kBN) -> -inf.
+  auto apply_mask = [&](f32x16 (&sc)[ST], int kb) {
+    const int t0 = tile_start(kb);
 #pragma unroll
     for (int st = 0; st < ST; ++st) {
-      const int thr = qi + pshift - n0 - 32 * st - 8 * h;
+      const int thr = (CAUSAL ? qi + pshift : p.N - 1) - t0 - 32 * st - 8 * h;
+      const int lo = kb * kBN - t0 - 32 * st - 8 * h;
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (perm_row(r, 0) > thr) sc[st][r] = kNegInf;
+        if (perm_row(r, 0) > thr || (RAGGED && CAUSAL && perm_row(r, 0) < lo)) sc[st][r] = kNegInf;
     }
   };
 
@@ -694,7 +746,7 @@ void attn_fwd_pipe_kernel(const FwdParams p) {
   wait_vmcnt0();
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
-    if (j < nblk) issue(j);
+    if (j < nblk) issue(j, std::true_type{});
   if (nblk > NS - 2)
     wait_vmcnt<kLoads>();
   else
@@ -709,7 +761,7 @@ void attn_fwd_pipe_kernel(const FwdParams p) {
   }
   if (nblk > 0 && active(0)) {
     scores(std::integral_constant<int, 0>{}, sa, [](auto) {});
-    if (needs_mask(0)) apply_mask(sa, 0);
+    if (tail_first || needs_mask(0)) apply_mask(sa, key_block(0));
     float mx = kNegInf;
 #pragma unroll
     for (int st = 0; st < ST; ++st)
@@ -723,7 +775,7 @@ void attn_fwd_pipe_kernel(const FwdParams p) {
   auto step = [&](auto stage_c, int jb, f32x16 (&sc)[ST], f32x16 (&sn)[ST]) {
     constexpr int S = decltype(stage_c)::value;
     constexpr int SN = (S + 1) % NS;
-    if (jb + NS - 1 < nblk) issue(jb + NS - 1);
+    if (jb + NS - 1 < nblk) issue(jb + NS - 1, std::false_type{});
     const bool a_c = active(jb);
     const bool a_n = jb + 1 < nblk && active(jb + 1);
     const float neg_m = (m_i == kNegInf) ? 0.f : -m_i;
@@ -735,7 +787,7 @@ void attn_fwd_pipe_kernel(const FwdParams p) {
         static_for<NR>([&](auto ic) { exp_step(sc, neg_m, ic); });
       V8 pb[PT];
       pack_sum(sc, pb);
-      if (a_n && needs_mask(jb + 1)) apply_mask(sn, (jb + 1) * kBN);
+      if (a_n && needs_mask(jb + 1)) apply_mask(sn, jb + 1);
       // P V of block jb || row max of block jb + 1 (taken whether or not
       // that block is active; only used when it is)
       float mx[2] = {kNegInf, kNegInf};
@@ -767,6 +819,7 @@ void attn_fwd_pipe_kernel(const FwdParams p) {
   const float l = halves_sum(l_i);
   const bool has = l > 0.f;
   const float inv = has ? 1.f / l : 0.f;
+  if (RAGGED && qi >= p.M) return;  // lanes past the last query row
   T* orow = (T*)p.o + qbase + (int64_t)qi * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) store_acc_t<T>(orow, acc[dt], 32 * dt, h, inv);
@@ -796,17 +849,26 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
   p.sm_scale = a.sm_scale;
   p.w = a.w;
   dim3 grid(p.nmb * p.BH), block(FwdShape<VAR, D>::NT);
+  const bool ragged = a.M % 64 != 0 || a.N % 64 != 0;
   if constexpr (VAR == PLAIN) {
     static_assert(FwdShape<PLAIN, D>::NT == 64 * kPipeWaves, "same launch shape");
-    if (a.causal)
-      hipLaunchKernelGGL((attn_fwd_pipe_kernel<T, D, true>), grid, block, 0, s, p);
+    if (a.causal && ragged)
+      hipLaunchKernelGGL((attn_fwd_pipe_kernel<T, D, true, true>), grid, block, 0, s, p);
+    else if (a.causal)
+      hipLaunchKernelGGL((attn_fwd_pipe_kernel<T, D, true, false>), grid, block, 0, s, p);
+    else if (ragged)
+      hipLaunchKernelGGL((attn_fwd_pipe_kernel<T, D, false, true>), grid, block, 0, s, p);
     else
-      hipLaunchKernelGGL((attn_fwd_pipe_kernel<T, D, false>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((attn_fwd_pipe_kernel<T, D, false, false>), grid, block, 0, s, p);
   } else {
-    if (a.causal)
-      hipLaunchKernelGGL((attn_fwd_kernel<T, D, VAR, true>), grid, block, 0, s, p);
+    if (a.causal && ragged)
+      hipLaunchKernelGGL((attn_fwd_kernel<T, D, VAR, true, true>), grid, block, 0, s, p);
+    else if (a.causal)
+      hipLaunchKernelGGL((attn_fwd_kernel<T, D, VAR, true, false>), grid, block, 0, s, p);
+    else if (ragged)
+      hipLaunchKernelGGL((attn_fwd_kernel<T, D, VAR, false, true>), grid, block, 0, s, p);
     else
-      hipLaunchKernelGGL((attn_fwd_kernel<T, D, VAR, false>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((attn_fwd_kernel<T, D, VAR, false, false>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }

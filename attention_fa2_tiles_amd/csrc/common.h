@@ -267,6 +267,11 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ constexpr int tile_row(int m, bool perm) { return perm ? swap23(m) : m; }
 
+// 16 zero bytes (source of the lanes of a direct tile load whose row lies
+// past the end of the tensor) and a +inf (the LSE of such a row).
+static __device__ __attribute__((aligned(16))) uint32_t kZero16[4] = {0u, 0u, 0u, 0u};
+static __device__ float kPosInfF = __builtin_huge_valf();
+
 template <typename T, int R, int D, int NW, bool PERM = true>
 struct DTile {
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
@@ -287,6 +292,24 @@ struct DTile {
       const T* src = g + tile_row(m, PERM) * D + ((slot ^ swz<D>(m)) * 8);
       __builtin_amdgcn_global_load_lds(
           (const void __attribute__((address_space(1)))*)src,
+          (void __attribute__((address_space(3)))*)(lds + ins * 512), 16, 0, 0);
+    }
+  }
+
+  // As load, for a tile of which only rows 0 .. nrows-1 exist in memory:
+  // the rows beyond are filled with zeros (a lane whose source row lies
+  // beyond reads 16 zero bytes of kZero16 instead).  Same instruction count
+  // as load.
+  __device__ static __forceinline__ void load_lim(T* lds, const T* g, int wave, int lane, int nrows) {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int ins = wave * PER_WAVE + j;
+      const int p = ins * 64 + lane;
+      const int m = p / CPR, slot = p % CPR;
+      const int src = tile_row(m, PERM);
+      const T* src_ptr = src < nrows ? g + src * D + ((slot ^ swz<D>(m)) * 8) : reinterpret_cast<const T*>(kZero16);
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)src_ptr,
           (void __attribute__((address_space(3)))*)(lds + ins * 512), 16, 0, 0);
     }
   }
@@ -325,6 +348,14 @@ struct DmaTile {
           (const void __attribute__((address_space(1)))*)(reinterpret_cast<const char*>(g) + voff[j]),
           (void __attribute__((address_space(3)))*)(lds + ins * 512), 16, 0, 0);
     }
+  }
+  // As load, when only rows 0 .. nrows-1 of the tile exist (see
+  // DTile::load_lim); nrows >= R is the same as load.
+  __device__ __forceinline__ void load_rows(const T* g, T* lds, int wave, int lane, int nrows) const {
+    if (nrows >= R)
+      load(g, lds, wave);
+    else
+      Tile::load_lim(lds, g, wave, lane, nrows);
   }
 };
 

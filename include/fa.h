@@ -37,8 +37,9 @@
  *   16 bytes; fp32 per-row vectors (lse, delta, l0, gl, gl0, gq) and the
  *   attention backward's workspace 4 bytes; the merge backward's workspace
  *   16 bytes.
- * - Supported attention shapes: B, H >= 1; M, N multiples of 64; D in
- *   {64, 128} (FA_ERR_UNSUPPORTED otherwise).
+ * - Supported attention shapes: B, H, M, N >= 1 (any lengths; the kernels
+ *   mask the last partial tile); D in {64, 128} (FA_ERR_UNSUPPORTED
+ *   otherwise).
  *
  * Citations name the page and the function or passage whose computation the
  * entry point performs:

@@ -78,8 +78,6 @@ def fwd_args(**kw):
     (dict(M=-64), -2),
     (dict(D=96), -6),
     (dict(D=32), -6),
-    (dict(M=100), -6),
-    (dict(N=130), -6),
     (dict(causal=2), -6),
     (dict(sm_scale=-1.0), -6),
     (dict(sm_scale=float("nan")), -6),

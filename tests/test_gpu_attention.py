@@ -2,8 +2,9 @@
 
 Small shapes are compared element by element on every output; they span
 several tiles in both directions, a half-filled last query block, M != N
-(bottom-right causal alignment, including query rows that see no key), both
-head dims and all three dtypes.  The full-size workloads (causal bf16
+(bottom-right causal alignment, including query rows that see no key),
+lengths that are not tile multiples (down to a single score), both head dims
+and all three dtypes, with guard regions around every output.  The full-size workloads (causal bf16
 B4 H16 2048 D128 and non-causal bf16 B1 H32 8192 D128) run in the same launch
 configuration the benchmark times and are compared on whole sampled heads.
 """
@@ -61,10 +62,28 @@ def compare(wl, t, got, heads=None, with_bwd=True):
         check_lse(f"{tag}.lse", got["lse"][b, h], lse[0, 0], wl.dtype)
         if with_bwd:
             dq, dk, dv = oracle.attn_bwd(f["q"], f["k"], f["v"], f["do"], wl.causal, c)
-            check_grad(f"{tag}.dq", got["dq"][b, h], dq[0, 0], wl.dtype)
-            check_grad(f"{tag}.dk", got["dk"][b, h], dk[0, 0], wl.dtype)
+            terms = lambda: summand_scales(f, wl.causal, c)
+            check_grad(f"{tag}.dq", got["dq"][b, h], dq[0, 0], wl.dtype, zero_scale=lambda: terms()[0])
+            check_grad(f"{tag}.dk", got["dk"][b, h], dk[0, 0], wl.dtype, zero_scale=lambda: terms()[1])
             check_grad(f"{tag}.dv", got["dv"][b, h], dv[0, 0], wl.dtype)
     del sel
+
+
+def summand_scales(f, causal, c):
+    """Largest summands of dQ = c (P o dP) K and dK = c (P o dP)^t Q before
+    the Delta term cancels them (used only when a reference gradient is all
+    zeros); a tolerance scale, not a second reference."""
+    q, k, v, do = (f[n][0, 0] for n in ("q", "k", "v", "do"))
+    M, N = q.shape[0], k.shape[0]
+    s = c * q @ k.T
+    if causal:
+        s = np.where(np.arange(N)[None, :] > np.arange(M)[:, None] + (N - M), -np.inf, s)
+    mx = s.max(axis=1, keepdims=True)
+    e = np.exp(np.where(np.isfinite(mx), s - mx, -np.inf))
+    den = e.sum(axis=1, keepdims=True)
+    pm = np.where(den > 0, e / np.where(den > 0, den, 1.0), 0.0)
+    t = np.abs(pm * (do @ v.T))
+    return c * (t @ np.abs(k)).max(), c * (t.T @ np.abs(q)).max()
 
 
 SMALL = [
@@ -80,6 +99,18 @@ SMALL = [
     (F32, 1, 2, 128, 128, 64, False),
     (F32, 1, 2, 192, 128, 128, True),
     (F32, 1, 1, 64, 192, 64, True),
+    # lengths that are not tile multiples: partial last query / key tiles
+    (BF16, 2, 3, 200, 200, 128, True),
+    (BF16, 2, 3, 200, 200, 128, False),
+    (F16, 1, 2, 77, 150, 64, True),       # M < N, both ragged
+    (F16, 1, 2, 150, 77, 64, False),      # M > N
+    (F16, 1, 2, 150, 77, 128, True),      # M > N causal: rows that see no key
+    (BF16, 1, 2, 37, 29, 128, True),      # both below one tile
+    (BF16, 1, 2, 29, 37, 64, False),
+    (F16, 1, 1, 1, 1, 64, False),         # a single score
+    (BF16, 1, 2, 300, 1000, 128, True),   # causal key tail past a full tile
+    (BF16, 1, 1, 64, 65, 128, False),     # one key past a tile
+    (F32, 1, 2, 100, 130, 64, True),
 ]
 
 

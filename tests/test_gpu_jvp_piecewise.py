@@ -49,6 +49,8 @@ JVP_SMALL = [
     (F16, 1, 2, 256, 128, 128, True),
     (F32, 1, 2, 128, 128, 64, False),
     (F32, 1, 2, 128, 192, 128, True),
+    (F16, 1, 2, 100, 150, 64, True),      # ragged lengths
+    (BF16, 1, 2, 150, 100, 128, False),
 ]
 
 
@@ -134,6 +136,8 @@ PW_SMALL = [
     (F16, 1, 2, 256, 256, 64, True, 0),        # only the diagonal is near
     (F32, 1, 2, 128, 128, 64, True, 20),
     (F32, 1, 2, 128, 192, 128, False, 50),
+    (F16, 1, 2, 200, 170, 64, True, 50),       # ragged lengths
+    (BF16, 1, 2, 130, 250, 128, False, 60),
 ]
 
 

@@ -83,8 +83,12 @@ def check_lse(name, got, ref, dtype):
     return 0.0
 
 
-def check_grad(name, got, ref, dtype):
-    """Gradients and tangents."""
+def check_grad(name, got, ref, dtype, zero_scale=None):
+    """Gradients and tangents.  A reference that is exactly zero everywhere
+    (a cancellation, e.g. dK with a single key, where dP - Delta = 0) has no
+    scale of its own: zero_scale (a callable) then gives the magnitude of the
+    summands that cancel, and the bar is GRAD_REL times that; without it the
+    result must be exactly zero."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
@@ -96,8 +100,12 @@ def check_grad(name, got, ref, dtype):
         return err
     scale = np.abs(ref).max() if ref.size else 0.0
     if scale == 0.0:
-        assert err == 0.0, f"{name}: expected exact zeros, max abs {err:.3e}"
-        return 0.0
+        if zero_scale is None:
+            assert err == 0.0, f"{name}: expected exact zeros, max abs {err:.3e}"
+            return 0.0
+        zs = zero_scale()
+        assert err <= GRAD_REL * zs, f"{name}: max abs err {err:.3e} > {GRAD_REL} x {zs:.3e} (cancelled summands)"
+        return err / zs if zs else 0.0
     rel = err / scale
     assert rel <= GRAD_REL, f"{name}: max abs err {err:.3e} = {rel:.3e} x max|ref| > {GRAD_REL}"
     return rel
