@@ -108,8 +108,8 @@ def attn_fwd(q, k, v, causal, sm_scale):
     return o, lse
 
 
-def attn_bwd(q, k, v, do, causal, sm_scale):
-    """Attention backward: returns (dQ, dK, dV) for the loss <dO, O>.
+def attn_bwd(q, k, v, do, causal, sm_scale, dlse=None):
+    """Attention backward: returns (dQ, dK, dV) for the loss <dO, O> + <dLSE, LSE>.
 
     The analytic vector-Jacobian product that the gist's backward computes by
     recomputation (``_attn_bwd_preprocess`` for Delta, ``_attn_bwd_dkdv`` and
@@ -120,7 +120,13 @@ def attn_bwd(q, k, v, do, causal, sm_scale):
         dS = P * (dP - Delta)
         dQ = sm_scale * dS K,   dK = sm_scale * dS^T Q.
     Masking is the same for causal and non-causal; the non-causal case visits
-    every block (the correction proposed in the gist's comment thread)."""
+    every block (the correction proposed in the gist's comment thread).
+
+    ``dlse`` ([B, H, M], optional, zeros when None) is the gradient reaching
+    the log-sum-exp output, as the residual merge's backward hands to its
+    LSE inputs.  The gist's backward has no such input; by the chain rule,
+    dLSE_i / dS_ij = P_ij, so it adds P * dLSE to dS:
+        dS = P * (dP - (Delta - dLSE))."""
     B, H, M, D = q.shape
     N = k.shape[2]
     A = allowed_mask(M, N, causal)
@@ -135,6 +141,8 @@ def attn_bwd(q, k, v, do, causal, sm_scale):
             dv[b, h] = P.T @ dO
             dP = dO @ v[b, h].T
             delta = (O * dO).sum(axis=1)
+            if dlse is not None:
+                delta = delta - dlse[b, h]
             dS = P * (dP - delta[:, None])
             dq[b, h] = sm_scale * (dS @ k[b, h])
             dk[b, h] = sm_scale * (dS.T @ q[b, h])
@@ -142,7 +150,7 @@ def attn_bwd(q, k, v, do, causal, sm_scale):
 
 
 def attn_fwd_jvp(q, k, v, tq, tk, tv, causal, sm_scale):
-    """Forward-mode JVP of attention: returns (O, LSE, tO).
+    """Forward-mode JVP of attention: returns (O, LSE, tO, tLSE).
 
     The directional derivative of O along (tQ, tK, tV), as the gist's fused
     forward accumulates it (the ``ENABLE_JVP`` branch of ``_attn_fwd_inner``
@@ -150,13 +158,17 @@ def attn_fwd_jvp(q, k, v, tq, tk, tv, causal, sm_scale):
     arXiv 2410.11081):
         Sdot = sm_scale * (tQ K^T + Q tK^T), zero on masked entries
         mu_i = sum_j P_ij Sdot_ij
-        tO   = (P * Sdot) V - mu O + P tV."""
+        tO   = (P * Sdot) V - mu O + P tV.
+    The gist returns no tangent for LSE; since dLSE_i / dS_ij = P_ij it is
+        tLSE = mu
+    (natural log units; 0 for a row with no visible key)."""
     B, H, M, D = q.shape
     N = k.shape[2]
     A = allowed_mask(M, N, causal)
     o = np.zeros_like(q)
     lse = np.zeros((B, H, M))
     to = np.zeros_like(q)
+    tlse = np.zeros((B, H, M))
     for b in range(B):
         for h in range(H):
             P, lse[b, h] = _softmax_rows(_scores(q[b, h], k[b, h], sm_scale), A)
@@ -167,7 +179,8 @@ def attn_fwd_jvp(q, k, v, tq, tk, tv, causal, sm_scale):
             mu = PS.sum(axis=1)
             o[b, h] = O
             to[b, h] = PS @ v[b, h] - mu[:, None] * O + P @ tv[b, h]
-    return o, lse, to
+            tlse[b, h] = mu
+    return o, lse, to, tlse
 
 
 def _pw_scores(q1, k1, q2, k2, near, sm_scale):
@@ -195,14 +208,15 @@ def pw_fwd(q1, k1, q2, k2, v, causal, sm_scale, w):
     return o, lse
 
 
-def pw_bwd(q1, k1, q2, k2, v, do, causal, sm_scale, w):
+def pw_bwd(q1, k1, q2, k2, v, do, causal, sm_scale, w, dlse=None):
     """Piecewise attention backward: returns (dq1, dk1, dq2, dk2, dv).
 
     FlagAttention ``piecewise.py`` (``_bwd_kv_kernel``, ``_bwd_q_kernel``):
     dS is formed as in ``attn_bwd`` and split by the near mask; the near part
     flows to (q1, k1) and the far part to (q2, k2):
         dq1 = c (dS*near) k1,   dk1 = c (dS*near)^T q1,
-        dq2 = c (dS*far)  k2,   dk2 = c (dS*far)^T  q2,   dv = P^T dO."""
+        dq2 = c (dS*far)  k2,   dk2 = c (dS*far)^T  q2,   dv = P^T dO.
+    ``dlse`` enters dS as in ``attn_bwd``."""
     B, H, M, D = q1.shape
     N = k1.shape[2]
     A = allowed_mask(M, N, causal)
@@ -222,6 +236,8 @@ def pw_bwd(q1, k1, q2, k2, v, do, causal, sm_scale, w):
             dv[b, h] = P.T @ dO
             dP = dO @ v[b, h].T
             delta = (O * dO).sum(axis=1)
+            if dlse is not None:
+                delta = delta - dlse[b, h]
             dS = P * (dP - delta[:, None])
             dSn = np.where(near, dS, 0.0)
             dSf = np.where(far, dS, 0.0)

@@ -32,7 +32,7 @@ def cases():
         c = 0.6
         o, lse = oracle.attn_fwd(t["q"], t["k"], t["v"], causal, c)
         dq, dk, dv = oracle.attn_bwd(t["q"], t["k"], t["v"], t["do"], causal, c)
-        _, _, to = oracle.attn_fwd_jvp(t["q"], t["k"], t["v"], t["tq"], t["tk"], t["tv"], causal, c)
+        _, _, to, _ = oracle.attn_fwd_jvp(t["q"], t["k"], t["v"], t["tq"], t["tk"], t["tv"], causal, c)
         po, plse = oracle.pw_fwd(t["q"], t["k"], t["q2"], t["k2"], t["v"], causal, c, 2)
         pg = oracle.pw_bwd(t["q"], t["k"], t["q2"], t["k2"], t["v"], t["do"], causal, c, 2)
         tag = "causal" if causal else "full"

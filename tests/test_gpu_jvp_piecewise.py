@@ -35,7 +35,7 @@ def compare_jvp(wl, t, got, heads=None):
     pairs = [(b, h) for b in range(wl.B) for h in range(wl.H)] if heads is None else heads
     for (b, h) in pairs:
         f = [t[n].f64[b:b + 1, h:h + 1] for n in JVP_NAMES]
-        o, lse, to = oracle.attn_fwd_jvp(*f, wl.causal, wl.scale())
+        o, lse, to, tlse = oracle.attn_fwd_jvp(*f, wl.causal, wl.scale())
         tag = f"{wl.name}[b={b},h={h}]"
         check_output(f"{tag}.o", got["o"][b, h], o[0, 0], wl.dtype)
         check_lse(f"{tag}.lse", got["lse"][b, h], lse[0, 0], wl.dtype)

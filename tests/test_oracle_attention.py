@@ -221,6 +221,52 @@ def test_bwd_invariants():
     np.testing.assert_allclose(dq[:, :, 0], 0.0, atol=1e-15)
 
 
+def _loss_lse(q, k, v, do, g, causal, c):
+    o, lse = oa.attn_fwd(q, k, v, causal, c)
+    return float((o * do).sum() + (lse * g).sum())
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("M,N", [(5, 5), (3, 5)])
+def test_bwd_lse_gradient_finite_differences(causal, M, N):
+    """A gradient reaching LSE (loss <dO, O> + <g, LSE>) against central
+    differences of the forward."""
+    D, c = 3, 0.7
+    q, k, v, do = rand(1, 1, M, D), rand(1, 1, N, D), rand(1, 1, N, D), rand(1, 1, M, D)
+    g = rand(1, 1, M)
+    dq, dk, dv = oa.attn_bwd(q, k, v, do, causal, c, dlse=g)
+    gq = _fd_grad(lambda x: _loss_lse(x, k, v, do, g, causal, c), q)
+    gk = _fd_grad(lambda x: _loss_lse(q, x, v, do, g, causal, c), k)
+    gv = _fd_grad(lambda x: _loss_lse(q, k, x, do, g, causal, c), v)
+    for a, b in ((dq, gq), (dk, gk), (dv, gv)):
+        np.testing.assert_allclose(a, b, atol=1e-8 * max(1.0, np.abs(b).max()), rtol=0)
+
+
+def test_bwd_lse_gradient_closed_forms():
+    M = N = 7
+    D, c = 4, 0.6
+    q, k, v = rand(1, 2, M, D), rand(1, 2, N, D), rand(1, 2, N, D)
+    g = rand(1, 2, M)
+    zero_do = np.zeros_like(q)
+    for causal in (False, True):
+        dq, dk, dv = oa.attn_bwd(q, k, v, zero_do, causal, c, dlse=g)
+        np.testing.assert_allclose(dv, 0.0, atol=0)  # LSE does not depend on V
+        # moving every key by u moves LSE_i by c q_i . u, so sum_j dK_j = c sum_i g_i q_i
+        np.testing.assert_allclose(dk.sum(axis=2), c * np.einsum("bhm,bhmd->bhd", g, q), atol=1e-12)
+        # scaling Q by (1 + t) scales every score, dLSE_i/dt = sum_j P_ij S_ij
+        P, _ = oa.attn_probs(q, k, causal, c)
+        S = c * np.einsum("bhmd,bhnd->bhmn", q, k)
+        lhs = float((dq * q).sum())
+        rhs = float((g * (P * np.where(P > 0, S, 0.0)).sum(axis=3)).sum())
+        assert abs(lhs - rhs) < 1e-12 * max(1.0, abs(rhs))
+    # g = 0 is the plain backward
+    do = rand(1, 2, M, D)
+    a = oa.attn_bwd(q, k, v, do, True, c, dlse=np.zeros((1, 2, M)))
+    b = oa.attn_bwd(q, k, v, do, True, c)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
 # --------------------------------------------------------------------- JVP --
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -229,15 +275,27 @@ def test_jvp_vs_torch_func_jvp(causal):
     D = 8
     args = [rand(1, 3, M, D), rand(1, 3, N, D), rand(1, 3, N, D)]
     tans = [rand(1, 3, M, D), rand(1, 3, N, D), rand(1, 3, N, D)]
-    o, lse, to = oa.attn_fwd_jvp(*args, *tans, causal, 0.25)
+    o, lse, to, tlse = oa.attn_fwd_jvp(*args, *tans, causal, 0.25)
 
     def f(a, b, c):
         return _sdpa(a, b, c, causal, 0.25, M, N)
+
+    def f_lse(a, b):
+        # torch's logsumexp of the masked scaled scores (independent of P)
+        s = 0.25 * (a @ b.transpose(-1, -2))
+        if causal:
+            i = torch.arange(M)[:, None]
+            j = torch.arange(N)[None, :]
+            s = s.masked_fill(j > i + (N - M), -math.inf)
+        return torch.logsumexp(s, dim=-1)
 
     with sdpa_kernel(SDPBackend.MATH):
         p, t = torch.func.jvp(f, tuple(_t(a) for a in args), tuple(_t(a) for a in tans))
     np.testing.assert_allclose(o, p.numpy(), atol=1e-12, rtol=0)
     np.testing.assert_allclose(to, t.numpy(), atol=1e-12, rtol=0)
+    pl, tl = torch.func.jvp(f_lse, (_t(args[0]), _t(args[1])), (_t(tans[0]), _t(tans[1])))
+    np.testing.assert_allclose(lse, pl.numpy(), atol=1e-12, rtol=0)
+    np.testing.assert_allclose(tlse, tl.numpy(), atol=1e-12, rtol=0)
     o2, lse2 = oa.attn_fwd(*args, causal, 0.25)
     np.testing.assert_allclose(o, o2, atol=1e-14, rtol=0)
     np.testing.assert_allclose(lse, lse2, atol=1e-14, rtol=0)
@@ -248,11 +306,12 @@ def test_jvp_directional_fd_and_adjoint(causal):
     M, N, D, c = 6, 6, 4, 0.9
     q, k, v = rand(1, 1, M, D), rand(1, 1, N, D), rand(1, 1, N, D)
     tq, tk, tv = rand(1, 1, M, D), rand(1, 1, N, D), rand(1, 1, N, D)
-    _, _, to = oa.attn_fwd_jvp(q, k, v, tq, tk, tv, causal, c)
+    _, _, to, tlse = oa.attn_fwd_jvp(q, k, v, tq, tk, tv, causal, c)
     h = 1e-6
-    op, _ = oa.attn_fwd(q + h * tq, k + h * tk, v + h * tv, causal, c)
-    om, _ = oa.attn_fwd(q - h * tq, k - h * tk, v - h * tv, causal, c)
+    op, lp = oa.attn_fwd(q + h * tq, k + h * tk, v + h * tv, causal, c)
+    om, lm = oa.attn_fwd(q - h * tq, k - h * tk, v - h * tv, causal, c)
     np.testing.assert_allclose(to, (op - om) / (2 * h), atol=1e-8, rtol=0)
+    np.testing.assert_allclose(tlse, (lp - lm) / (2 * h), atol=1e-8, rtol=0)
     # <dO, tO> = <dQ, tQ> + <dK, tK> + <dV, tV> ties the JVP to the VJP
     do = rand(1, 1, M, D)
     dq, dk, dv = oa.attn_bwd(q, k, v, do, causal, c)
@@ -267,12 +326,21 @@ def test_jvp_special_cases():
     q, k, v = rand(1, 2, M, D), rand(1, 2, N, D), rand(1, 2, N, D)
     z_q, z_k = np.zeros_like(q), np.zeros_like(k)
     for causal in (False, True):
-        o, _, to = oa.attn_fwd_jvp(q, k, v, z_q, z_k, v, causal, 0.5)
+        o, _, to, tlse = oa.attn_fwd_jvp(q, k, v, z_q, z_k, v, causal, 0.5)
         np.testing.assert_allclose(to, o, atol=1e-14)  # O is linear in V
+        np.testing.assert_allclose(tlse, 0.0, atol=0)  # LSE does not depend on V
         u = rand(D)
         tk = np.broadcast_to(u, k.shape).copy()  # every key moves by u
-        _, _, to = oa.attn_fwd_jvp(q, k, v, z_q, tk, z_k, causal, 0.5)
+        _, _, to, tlse = oa.attn_fwd_jvp(q, k, v, z_q, tk, z_k, causal, 0.5)
         np.testing.assert_allclose(to, 0.0, atol=1e-13)
+        # every score of row i moves by 0.5 q_i . u, so LSE_i moves by as much
+        np.testing.assert_allclose(tlse, 0.5 * (q @ u), atol=1e-13)
         vc = np.broadcast_to(rand(D), v.shape).copy()  # constant V, no V tangent
-        _, _, to = oa.attn_fwd_jvp(q, k, vc, rand(*q.shape), rand(*k.shape), z_k, causal, 0.5)
+        _, _, to, _ = oa.attn_fwd_jvp(q, k, vc, rand(*q.shape), rand(*k.shape), z_k, causal, 0.5)
         np.testing.assert_allclose(to, 0.0, atol=1e-13)
+    # causal with M > N: rows with no visible key have a zero LSE tangent
+    q3 = rand(1, 1, 9, D)
+    k3, v3 = rand(1, 1, 4, D), rand(1, 1, 4, D)
+    _, lse, _, tlse = oa.attn_fwd_jvp(q3, k3, v3, rand(*q3.shape), rand(*k3.shape), rand(*v3.shape), True, 0.5)
+    assert np.all(np.isneginf(lse[..., :5])) and np.all(tlse[..., :5] == 0.0)
+    assert np.all(tlse[..., 5:] != 0.0)

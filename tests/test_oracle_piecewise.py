@@ -111,18 +111,21 @@ def _fd_grad(f, x, h=1e-6):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_bwd_finite_differences(causal):
+@pytest.mark.parametrize("with_lse", [False, True])
+def test_bwd_finite_differences(causal, with_lse):
+    """Loss <dO, O> (+ <g, LSE> when with_lse) against central differences."""
     M = N = 6
     D, c, w = 3, 0.7, 2
     q1, k1, q2, k2, v, do = (rand(1, 1, M, D) for _ in range(6))
-    grads = oa.pw_bwd(q1, k1, q2, k2, v, do, causal, c, w)
+    gl = rand(1, 1, M) if with_lse else np.zeros((1, 1, M))
+    grads = oa.pw_bwd(q1, k1, q2, k2, v, do, causal, c, w, dlse=gl if with_lse else None)
     args = [q1, k1, q2, k2, v]
 
     def loss_with(idx, x):
         a = list(args)
         a[idx] = x
-        o, _ = oa.pw_fwd(*a, causal, c, w)
-        return float((o * do).sum())
+        o, lse = oa.pw_fwd(*a, causal, c, w)
+        return float((o * do).sum() + (lse * gl).sum())
 
     for idx, g in enumerate(grads):
         fd = _fd_grad(lambda x: loss_with(idx, x), args[idx])
