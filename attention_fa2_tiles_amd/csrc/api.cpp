@@ -31,6 +31,13 @@ int check_tensors(std::initializer_list<const void*> ps) {
   return FA_OK;
 }
 
+// Optional fp32 per-row vectors (NULL allowed).
+int check_opt_scalars(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p && !aligned(p, 4)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
 // fp32 per-row vectors (LSE, Delta, l0, gl0, gq).
 int check_scalars(std::initializer_list<const void*> ps) {
   for (const void* p : ps)
@@ -72,10 +79,10 @@ int run_fwd(FwdArgs& a, hipStream_t s) {
   return hip_status(a.dtype == FA_F32 ? fa::launch_attn_fwd_f32(a, s) : fa::launch_attn_fwd(a, s));
 }
 
-int run_bwd_steps(BwdArgs& a, const void* o, float* delta, hipStream_t s, bool do_delta, bool do_dkdv,
-                  bool do_dq) {
+int run_bwd_steps(BwdArgs& a, const void* o, const float* dlse, float* delta, hipStream_t s, bool do_delta,
+                  bool do_dkdv, bool do_dq) {
   if (do_delta) {
-    FA_TRY(hip_status(fa::launch_attn_delta(a.dtype, o, a.dout, delta, (int64_t)a.B * a.H * a.M, a.D, s)));
+    FA_TRY(hip_status(fa::launch_attn_delta(a.dtype, o, a.dout, dlse, delta, (int64_t)a.B * a.H * a.M, a.D, s)));
   }
   a.delta = delta;
   if (do_dkdv) {
@@ -145,13 +152,15 @@ size_t fa_bwd_workspace_size(int B, int H, int M, int N, int D, int dtype) {
 }
 
 static int bwd_common(int dtype, int variant, const void* q, const void* k, const void* q2, const void* k2,
-                      const void* v, const void* o, const void* dout, const float* lse, void* dq, void* dk,
+                      const void* v, const void* o, const void* dout, const float* lse, const float* dlse,
+                      void* dq, void* dk,
                       void* dq2, void* dk2, void* dv, void* workspace, size_t workspace_bytes, int B, int H,
                       int M, int N, int D, int causal, float sm_scale, int w, void* stream) {
   FA_TRY(check_dtype(dtype));
   FA_TRY(check_tensors({q, k, v, o, dout, dq, dk, dv}));
   if (variant == fa::PW) FA_TRY(check_tensors({q2, k2, dq2, dk2}));
   FA_TRY(check_scalars({lse}));
+  FA_TRY(check_opt_scalars({dlse}));
   FA_TRY(check_attn_shape(B, H, M, N, D));
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
   float scale;
@@ -181,23 +190,25 @@ static int bwd_common(int dtype, int variant, const void* q, const void* k, cons
   a.causal = causal;
   a.sm_scale = scale;
   a.w = w;
-  return run_bwd_steps(a, o, (float*)workspace, (hipStream_t)stream, true, true, true);
+  return run_bwd_steps(a, o, dlse, (float*)workspace, (hipStream_t)stream, true, true, true);
 }
 
 int fa_bwd(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,
-           const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H,
-           int M, int N, int D, int causal, float sm_scale, void* stream) {
-  return bwd_common(dtype, fa::PLAIN, q, k, nullptr, nullptr, v, o, dout, lse, dq, dk, nullptr, nullptr, dv,
+           const float* lse, const float* dlse, void* dq, void* dk, void* dv, void* workspace,
+           size_t workspace_bytes, int B, int H, int M, int N, int D, int causal, float sm_scale, void* stream) {
+  return bwd_common(dtype, fa::PLAIN, q, k, nullptr, nullptr, v, o, dout, lse, dlse, dq, dk, nullptr, nullptr, dv,
                     workspace, workspace_bytes, B, H, M, N, D, causal, sm_scale, 0, stream);
 }
 
-int fa_bwd_delta(int dtype, const void* o, const void* dout, float* delta, int B, int H, int M, int D,
-                 void* stream) {
+int fa_bwd_delta(int dtype, const void* o, const void* dout, const float* dlse, float* delta, int B, int H, int M,
+                 int D, void* stream) {
   FA_TRY(check_dtype(dtype));
   FA_TRY(check_tensors({o, dout}));
   FA_TRY(check_scalars({delta}));
+  FA_TRY(check_opt_scalars({dlse}));
   FA_TRY(check_attn_shape(B, H, M, M, D));
-  return hip_status(fa::launch_attn_delta(dtype, o, dout, delta, (int64_t)B * H * M, D, (hipStream_t)stream));
+  return hip_status(
+      fa::launch_attn_delta(dtype, o, dout, dlse, delta, (int64_t)B * H * M, D, (hipStream_t)stream));
 }
 
 static int bwd_pass(bool dkdv, int dtype, const void* q, const void* k, const void* v, const void* dout,
@@ -231,7 +242,7 @@ static int bwd_pass(bool dkdv, int dtype, const void* q, const void* k, const vo
   a.D = D;
   a.causal = causal;
   a.sm_scale = scale;
-  return run_bwd_steps(a, nullptr, (float*)delta, (hipStream_t)stream, false, dkdv, !dkdv);
+  return run_bwd_steps(a, nullptr, nullptr, (float*)delta, (hipStream_t)stream, false, dkdv, !dkdv);
 }
 
 int fa_bwd_dkdv(int dtype, const void* q, const void* k, const void* v, const void* dout, const float* lse,
@@ -249,11 +260,12 @@ int fa_bwd_dq(int dtype, const void* q, const void* k, const void* v, const void
 }
 
 int fa_fwd_jvp(int dtype, const void* q, const void* k, const void* v, const void* tq, const void* tk,
-               const void* tv, void* o, float* lse, void* to, int B, int H, int M, int N, int D, int causal,
-               float sm_scale, void* stream) {
+               const void* tv, void* o, float* lse, void* to, float* tlse, int B, int H, int M, int N, int D,
+               int causal, float sm_scale, void* stream) {
   FA_TRY(check_dtype(dtype));
   FA_TRY(check_tensors({q, k, v, tq, tk, tv, o, to}));
   FA_TRY(check_scalars({lse}));
+  FA_TRY(check_opt_scalars({tlse}));
   FA_TRY(check_attn_shape(B, H, M, N, D));
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
   float scale;
@@ -270,6 +282,7 @@ int fa_fwd_jvp(int dtype, const void* q, const void* k, const void* v, const voi
   a.o = o;
   a.lse = lse;
   a.to = to;
+  a.tlse = tlse;
   a.B = B;
   a.H = H;
   a.M = M;
@@ -315,10 +328,10 @@ size_t pw_bwd_workspace_size(int B, int H, int M, int N, int D, int dtype) {
 }
 
 int pw_bwd(int dtype, const void* q1, const void* k1, const void* q2, const void* k2, const void* v, const void* o,
-           const void* dout, const float* lse, void* dq1, void* dk1, void* dq2, void* dk2, void* dv,
-           void* workspace, size_t workspace_bytes, int B, int H, int M, int N, int D, int causal, float sm_scale,
-           int w, void* stream) {
-  return bwd_common(dtype, fa::PW, q1, k1, q2, k2, v, o, dout, lse, dq1, dk1, dq2, dk2, dv, workspace,
+           const void* dout, const float* lse, const float* dlse, void* dq1, void* dk1, void* dq2, void* dk2,
+           void* dv, void* workspace, size_t workspace_bytes, int B, int H, int M, int N, int D, int causal,
+           float sm_scale, int w, void* stream) {
+  return bwd_common(dtype, fa::PW, q1, k1, q2, k2, v, o, dout, lse, dlse, dq1, dk1, dq2, dk2, dv, workspace,
                     workspace_bytes, B, H, M, N, D, causal, sm_scale, w, stream);
 }
 

@@ -46,7 +46,8 @@ struct Row8 {
 
 template <typename T, int D>
 __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o, const T* __restrict__ dout,
-                                                    float* __restrict__ delta, int64_t rows) {
+                                                    const float* __restrict__ dlse, float* __restrict__ delta,
+                                                    int64_t rows) {
   constexpr int TPR = D / 8;      // threads per row
   constexpr int RPB = 256 / TPR;  // rows per block
   const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
@@ -60,18 +61,20 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o, con
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
-  if (row < rows && c == 0) delta[row] = sum;
+  // A gradient reaching LSE adds P * dLSE to dS, i.e. it lowers Delta.
+  if (row < rows && c == 0) delta[row] = dlse ? sum - dlse[row] : sum;
 }
 
 template <typename T>
-hipError_t launch_delta_t(const void* o, const void* dout, float* delta, int64_t rows, int D,
-                          hipStream_t s) {
+hipError_t launch_delta_t(const void* o, const void* dout, const float* dlse, float* delta, int64_t rows,
+                          int D, hipStream_t s) {
   const int64_t rpb = 256 / (D / 8);
   dim3 grid((unsigned)((rows + rpb - 1) / rpb)), block(256);
   if (D == 64)
-    hipLaunchKernelGGL((delta_kernel<T, 64>), grid, block, 0, s, (const T*)o, (const T*)dout, delta, rows);
+    hipLaunchKernelGGL((delta_kernel<T, 64>), grid, block, 0, s, (const T*)o, (const T*)dout, dlse, delta, rows);
   else if (D == 128)
-    hipLaunchKernelGGL((delta_kernel<T, 128>), grid, block, 0, s, (const T*)o, (const T*)dout, delta, rows);
+    hipLaunchKernelGGL((delta_kernel<T, 128>), grid, block, 0, s, (const T*)o, (const T*)dout, dlse, delta,
+                       rows);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -946,11 +949,11 @@ hipError_t dispatch(const BwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_attn_delta(int dtype, const void* o, const void* dout, float* delta, int64_t rows, int D,
-                             hipStream_t s) {
-  if (dtype == 0) return launch_delta_t<float>(o, dout, delta, rows, D, s);
-  if (dtype == 1) return launch_delta_t<_Float16>(o, dout, delta, rows, D, s);
-  if (dtype == 2) return launch_delta_t<__bf16>(o, dout, delta, rows, D, s);
+hipError_t launch_attn_delta(int dtype, const void* o, const void* dout, const float* dlse, float* delta,
+                             int64_t rows, int D, hipStream_t s) {
+  if (dtype == 0) return launch_delta_t<float>(o, dout, dlse, delta, rows, D, s);
+  if (dtype == 1) return launch_delta_t<_Float16>(o, dout, dlse, delta, rows, D, s);
+  if (dtype == 2) return launch_delta_t<__bf16>(o, dout, dlse, delta, rows, D, s);
   return hipErrorInvalidValue;
 }
 

@@ -88,6 +88,8 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a, float scale, in
     const float c = mu * inv;
 #pragma unroll
     for (int e = 0; e < E; ++e) TO[lane + 64 * e] = (accg[e] - c * acc[e]) * inv;
+    // LSE tangent: sum_j P_ij Sdot_ij (0 for a row with no visible key)
+    if (lane == 0 && a.tlse) a.tlse[row] = c;
   }
 }
 

@@ -55,6 +55,7 @@ struct FwdParams {
   void* o;
   float* lse;
   void* to;
+  float* tlse;     // may be NULL
   int BH, M, N, nmb;
   float scale2;    // sm_scale * log2(e)
   float sm_scale;
@@ -493,6 +494,8 @@ void attn_fwd_kernel(const FwdParams p) {
       for (int r = 0; r < 16; ++r) t[r] = (accg[dt][r] - c * acc[dt][r]) * inv;
       store_acc_t<T>(torow, t, 32 * dt, h, 1.f);
     }
+    // LSE tangent: sum_j P_ij Sdot_ij (0 for a row with no visible key)
+    if (h == 0 && p.tlse) p.tlse[(int64_t)bh * p.M + qi] = c;
   }
 }
 
@@ -840,6 +843,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
   p.o = a.o;
   p.lse = a.lse;
   p.to = a.to;
+  p.tlse = a.tlse;
   p.BH = a.B * a.H;
   p.M = a.M;
   p.N = a.N;

@@ -23,6 +23,7 @@ struct FwdArgs {
   void* o;
   float* lse;
   void* to;                // JVP only
+  float* tlse;             // JVP only, may be NULL
   int B, H, M, N, D;
   int causal;
   float sm_scale;          // resolved (> 0)
@@ -71,7 +72,8 @@ struct MergeArgs {
 };
 
 hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t s);
-hipError_t launch_attn_delta(int dtype, const void* o, const void* dout, float* delta,
+// delta = rowsum(o * dout) - dlse (dlse may be NULL: zeros)
+hipError_t launch_attn_delta(int dtype, const void* o, const void* dout, const float* dlse, float* delta,
                              int64_t rows, int D, hipStream_t s);
 hipError_t launch_attn_dkdv(const BwdArgs& a, hipStream_t s);
 hipError_t launch_attn_dq(const BwdArgs& a, hipStream_t s);

@@ -41,14 +41,14 @@ _SIGNATURES = {
     "fa_version": ([], _I),
     "fa_fwd": ([_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P], _I),
     "fa_bwd_workspace_size": ([_I, _I, _I, _I, _I, _I], _Z),
-    "fa_bwd": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _I, _F, _P], _I),
-    "fa_bwd_delta": ([_I, _P, _P, _P, _I, _I, _I, _I, _P], _I),
+    "fa_bwd": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _I, _F, _P], _I),
+    "fa_bwd_delta": ([_I, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "fa_bwd_dkdv": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P], _I),
     "fa_bwd_dq": ([_I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P], _I),
-    "fa_fwd_jvp": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P], _I),
+    "fa_fwd_jvp": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P], _I),
     "pw_fwd": ([_I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P], _I),
     "pw_bwd_workspace_size": ([_I, _I, _I, _I, _I, _I], _Z),
-    "pw_bwd": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
+    "pw_bwd": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
                 _I, _I, _I, _I, _I, _I, _F, _I, _P], _I),
     "resmerge_fwd": ([_I, _P, _P, _P, _P, _P, _P, _I, _I, _F, _P], _I),
     "resmerge_bwd_workspace_size": ([_I, _I], _Z),
@@ -125,15 +125,15 @@ def fa_bwd_workspace_size(B, H, M, N, D, dtype):
     return load().fa_bwd_workspace_size(B, H, M, N, D, dtype)
 
 
-def fa_bwd(dtype, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes,
+def fa_bwd(dtype, q, k, v, o, dout, lse, dlse, dq, dk, dv, workspace, workspace_bytes,
            B, H, M, N, D, causal, sm_scale, stream=None):
     _check("fa_bwd", load().fa_bwd(dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
-                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace_bytes,
+                                   _ptr(dlse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace_bytes,
                                    B, H, M, N, D, int(causal), sm_scale, _stream(stream)))
 
 
-def fa_bwd_delta(dtype, o, dout, delta, B, H, M, D, stream=None):
-    _check("fa_bwd_delta", load().fa_bwd_delta(dtype, _ptr(o), _ptr(dout), _ptr(delta), B, H, M, D,
+def fa_bwd_delta(dtype, o, dout, dlse, delta, B, H, M, D, stream=None):
+    _check("fa_bwd_delta", load().fa_bwd_delta(dtype, _ptr(o), _ptr(dout), _ptr(dlse), _ptr(delta), B, H, M, D,
                                                _stream(stream)))
 
 
@@ -149,9 +149,9 @@ def fa_bwd_dq(dtype, q, k, v, dout, lse, delta, dq, B, H, M, N, D, causal, sm_sc
                                          _stream(stream)))
 
 
-def fa_fwd_jvp(dtype, q, k, v, tq, tk, tv, o, lse, to, B, H, M, N, D, causal, sm_scale, stream=None):
+def fa_fwd_jvp(dtype, q, k, v, tq, tk, tv, o, lse, to, tlse, B, H, M, N, D, causal, sm_scale, stream=None):
     _check("fa_fwd_jvp", load().fa_fwd_jvp(dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv),
-                                           _ptr(o), _ptr(lse), _ptr(to), B, H, M, N, D, int(causal),
+                                           _ptr(o), _ptr(lse), _ptr(to), _ptr(tlse), B, H, M, N, D, int(causal),
                                            sm_scale, _stream(stream)))
 
 
@@ -164,10 +164,10 @@ def pw_bwd_workspace_size(B, H, M, N, D, dtype):
     return load().pw_bwd_workspace_size(B, H, M, N, D, dtype)
 
 
-def pw_bwd(dtype, q1, k1, q2, k2, v, o, dout, lse, dq1, dk1, dq2, dk2, dv, workspace, workspace_bytes,
+def pw_bwd(dtype, q1, k1, q2, k2, v, o, dout, lse, dlse, dq1, dk1, dq2, dk2, dv, workspace, workspace_bytes,
            B, H, M, N, D, causal, sm_scale, w, stream=None):
     _check("pw_bwd", load().pw_bwd(dtype, _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(v), _ptr(o), _ptr(dout),
-                                   _ptr(lse), _ptr(dq1), _ptr(dk1), _ptr(dq2), _ptr(dk2), _ptr(dv),
+                                   _ptr(lse), _ptr(dlse), _ptr(dq1), _ptr(dk1), _ptr(dq2), _ptr(dk2), _ptr(dv),
                                    _ptr(workspace), workspace_bytes, B, H, M, N, D, int(causal), sm_scale, w,
                                    _stream(stream)))
 

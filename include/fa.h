@@ -91,9 +91,13 @@ int fa_fwd(int dtype, const void* q, const void* k, const void* v, void* o, floa
  * Attention backward [tutorial: _attn_bwd_preprocess, _attn_bwd_dkdv,
  * _attn_bwd_dq, with the non-causal block range from the comment thread;
  * piecewise: _bwd_preprocess, _bwd_kv_kernel, _bwd_q_kernel].
- * Gradients of <dout, O> with O = fa_fwd(q, k, v); o and lse must be the
- * outputs of fa_fwd on the same inputs.  Three launches on `stream`:
- *   Delta_i = sum_d o_id dout_id                    (fa_bwd_delta)
+ * Gradients of <dout, O> + <dlse, LSE> with (O, LSE) = fa_fwd(q, k, v); o
+ * and lse must be the outputs of fa_fwd on the same inputs.  dlse [B,H,M]
+ * fp32 is the gradient reaching the LSE output (e.g. resmerge_bwd's gl0);
+ * NULL means zeros and gives the pages' backward.  The pages' backward has
+ * no such input: by the chain rule dLSE_i/dS_ij = P_ij, so it enters as
+ * dS = P (dP - (Delta - dlse)).  Three launches on `stream`:
+ *   Delta_i = sum_d o_id dout_id - dlse_i           (fa_bwd_delta)
  *   dK, dV  with K/V resident, looping over queries  (fa_bwd_dkdv)
  *   dQ      with Q resident, looping over keys       (fa_bwd_dq)
  * workspace: device buffer of at least fa_bwd_workspace_size() bytes (it
@@ -101,13 +105,14 @@ int fa_fwd(int dtype, const void* q, const void* k, const void* v, void* o, floa
  */
 size_t fa_bwd_workspace_size(int B, int H, int M, int N, int D, int dtype);
 int fa_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
-           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+           const void* dout, const float* lse, const float* dlse, void* dq, void* dk, void* dv,
            void* workspace, size_t workspace_bytes,
            int B, int H, int M, int N, int D, int causal, float sm_scale, void* stream);
 
 /* The three steps of fa_bwd, exposed separately so each can be timed. */
-/* delta [B,H,M] fp32 <- rowsum(o * dout)  [tutorial: _attn_bwd_preprocess] */
-int fa_bwd_delta(int dtype, const void* o, const void* dout, float* delta,
+/* delta [B,H,M] fp32 <- rowsum(o * dout) - dlse (dlse may be NULL)
+ * [tutorial: _attn_bwd_preprocess] */
+int fa_bwd_delta(int dtype, const void* o, const void* dout, const float* dlse, float* delta,
                  int B, int H, int M, int D, void* stream);
 /* dk, dv [B,H,N,D] from q, k, v, dout, lse and delta  [tutorial: _attn_bwd_dkdv] */
 int fa_bwd_dkdv(int dtype, const void* q, const void* k, const void* v, const void* dout,
@@ -125,11 +130,13 @@ int fa_bwd_dq(int dtype, const void* q, const void* k, const void* v, const void
  *   to = d/dt O(q + t*tq, k + t*tk, v + t*tv) at t = 0          [B,H,M,D]
  * computed in the same pass: with Sdot = sm_scale (tq K^T + Q tk^T),
  *   to = (P*Sdot) V - rowsum(P*Sdot) O + P tv.
- * tq is q-like, tk and tv are k-like.
+ * tq is q-like, tk and tv are k-like.  tlse [B,H,M] fp32 (may be NULL)
+ * receives the tangent of lse, rowsum(P*Sdot) (dLSE_i/dS_ij = P_ij; the
+ * pages return no LSE tangent); 0 for a row with no visible key.
  */
 int fa_fwd_jvp(int dtype, const void* q, const void* k, const void* v,
                const void* tq, const void* tk, const void* tv,
-               void* o, float* lse, void* to,
+               void* o, float* lse, void* to, float* tlse,
                int B, int H, int M, int N, int D, int causal, float sm_scale, void* stream);
 
 /*
@@ -147,12 +154,13 @@ int pw_fwd(int dtype, const void* q1, const void* k1, const void* q2, const void
  * Piecewise attention backward [piecewise: _bwd_preprocess, _bwd_kv_kernel,
  * _bwd_q_kernel].  dS is split by the same distance rule: the near part
  * yields dq1, dk1, the far part dq2, dk2; dv = P^T dout.  o and lse must come
- * from pw_fwd on the same inputs.  workspace as for fa_bwd
+ * from pw_fwd on the same inputs; dlse (may be NULL) as for fa_bwd.
+ * workspace as for fa_bwd
  * (pw_bwd_workspace_size() bytes, holds Delta).
  */
 size_t pw_bwd_workspace_size(int B, int H, int M, int N, int D, int dtype);
 int pw_bwd(int dtype, const void* q1, const void* k1, const void* q2, const void* k2,
-           const void* v, const void* o, const void* dout, const float* lse,
+           const void* v, const void* o, const void* dout, const float* lse, const float* dlse,
            void* dq1, void* dk1, void* dq2, void* dk2, void* dv,
            void* workspace, size_t workspace_bytes,
            int B, int H, int M, int N, int D, int causal, float sm_scale, int w, void* stream);

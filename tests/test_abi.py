@@ -89,20 +89,25 @@ def test_fa_fwd_rejects(kw, code):
 
 
 def test_bwd_rejects_small_workspace():
-    args = [2, P[0], P[1], P[2], P[3], P[5], P[4], P[6], P[7], P[8], P[9], 2 * 128 * 4 - 4,
+    args = [2, P[0], P[1], P[2], P[3], P[5], P[4], None, P[6], P[7], P[8], P[9], 2 * 128 * 4 - 4,
             1, 2, 128, 128, 64, 1, 0.0, None]
     assert status(lib.fa_bwd, *args) == -5
-    args[10] = None
-    args[11] = 1 << 20
+    args[11] = None
+    args[12] = 1 << 20
     assert status(lib.fa_bwd, *args) == -5
-    args = [2, P[0], P[1], P[2], P[3], P[5], P[4], None, P[7], P[8], P[9], 1 << 20,
+    args = [2, P[0], P[1], P[2], P[3], P[5], P[4], None, None, P[7], P[8], P[9], 1 << 20,
             1, 2, 128, 128, 64, 1, 0.0, None]
     assert status(lib.fa_bwd, *args) == -1
+    # an optional LSE gradient must still be 4-byte aligned
+    args = [2, P[0], P[1], P[2], P[3], P[5], P[4], P[4] + 2, P[6], P[7], P[8], P[9], 1 << 20,
+            1, 2, 128, 128, 64, 1, 0.0, None]
+    assert status(lib.fa_bwd, *args) == -4
 
 
 def test_step_entry_points_reject():
-    assert status(lib.fa_bwd_delta, 1, P[0], P[1], None, 1, 1, 64, 64) == -1
-    assert status(lib.fa_bwd_delta, 1, P[0], P[1], P[2], 1, 1, 64, 48) == -6
+    assert status(lib.fa_bwd_delta, 1, P[0], P[1], None, None, 1, 1, 64, 64) == -1
+    assert status(lib.fa_bwd_delta, 1, P[0], P[1], None, P[2], 1, 1, 64, 48) == -6
+    assert status(lib.fa_bwd_delta, 1, P[0], P[1], P[3] + 1, P[2], 1, 1, 64, 64) == -4
     assert status(lib.fa_bwd_dkdv, 2, P[0], P[1], P[2], P[3], P[4], P[5], P[6], None,
                   1, 1, 64, 64, 64, 0, 0.0) == -1
     assert status(lib.fa_bwd_dq, 2, P[0], P[1], P[2], P[3], P[4], P[5], P[6],
@@ -110,11 +115,13 @@ def test_step_entry_points_reject():
 
 
 def test_jvp_and_pw_reject():
-    assert status(lib.fa_fwd_jvp, 1, P[0], P[1], P[2], None, P[4], P[5], P[6], P[7], P[8],
+    assert status(lib.fa_fwd_jvp, 1, P[0], P[1], P[2], None, P[4], P[5], P[6], P[7], P[8], None,
                   1, 1, 64, 64, 64, 0, 0.0) == -1
+    assert status(lib.fa_fwd_jvp, 1, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], P[9] + 2,
+                  1, 1, 64, 64, 64, 0, 0.0) == -4
     assert status(lib.pw_fwd, 1, P[0], P[1], P[2], P[3], P[4], P[5], P[6],
                   1, 1, 64, 64, 256, 1, 0.0, 10) == -6
-    assert status(lib.pw_bwd, 1, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], P[9], P[10],
+    assert status(lib.pw_bwd, 1, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], None, P[8], P[9], P[10],
                   P[11], P[12], P[13], 0, 1, 1, 64, 64, 64, 1, 0.0, 10) == -5
 
 

@@ -14,14 +14,14 @@ import pytest
 
 import oracle
 from attention_fa2_tiles_amd import lib
-from attention_fa2_tiles_amd.inputs import BF16, F16, F32, WORKLOADS, AttnWorkload, attn_inputs
+from attention_fa2_tiles_amd.inputs import BF16, F16, F32, WORKLOADS, AttnWorkload, attn_inputs, draw
 from gpu_util import check_guards, dev, empty_f32, filled, guarded, guarded_f32, host, log, need_gpu
 from tolerance import check_fp32_abs, check_grad, check_lse, check_output
 
 pytestmark = pytest.mark.gpu
 
 
-def run_fwd_bwd(wl, t, with_bwd=True, steps=False, guard=False):
+def run_fwd_bwd(wl, t, with_bwd=True, steps=False, guard=False, dlse=None):
     torch = need_gpu()
     q, k, v, do = (dev(t[n]) for n in ("q", "k", "v", "do"))
     B, H, M, N, D = wl.B, wl.H, wl.M, wl.N, wl.D
@@ -34,13 +34,13 @@ def run_fwd_bwd(wl, t, with_bwd=True, steps=False, guard=False):
         dq, dk, dv = (alloc(x.shape, wl.dtype) for x in (q, k, v))
         if steps:
             delta = guarded_f32((B, H, M)) if guard else empty_f32((B, H, M))
-            lib.fa_bwd_delta(wl.dtype, o, do, delta, B, H, M, D)
+            lib.fa_bwd_delta(wl.dtype, o, do, dlse, delta, B, H, M, D)
             lib.fa_bwd_dkdv(wl.dtype, q, k, v, do, lse, delta, dk, dv, B, H, M, N, D, wl.causal, wl.sm_scale)
             lib.fa_bwd_dq(wl.dtype, q, k, v, do, lse, delta, dq, B, H, M, N, D, wl.causal, wl.sm_scale)
         else:
             ws_bytes = lib.fa_bwd_workspace_size(B, H, M, N, D, wl.dtype)
             ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-            lib.fa_bwd(wl.dtype, q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, H, M, N, D,
+            lib.fa_bwd(wl.dtype, q, k, v, o, do, lse, dlse, dq, dk, dv, ws, ws_bytes, B, H, M, N, D,
                        wl.causal, wl.sm_scale)
         out.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
@@ -50,7 +50,7 @@ def run_fwd_bwd(wl, t, with_bwd=True, steps=False, guard=False):
     return res
 
 
-def compare(wl, t, got, heads=None, with_bwd=True):
+def compare(wl, t, got, heads=None, with_bwd=True, dlse=None):
     sel = (slice(None), slice(None)) if heads is None else None
     c = wl.scale()
     pairs = [(b, h) for b in range(wl.B) for h in range(wl.H)] if heads is None else heads
@@ -61,7 +61,8 @@ def compare(wl, t, got, heads=None, with_bwd=True):
         check_output(f"{tag}.o", got["o"][b, h], o[0, 0], wl.dtype)
         check_lse(f"{tag}.lse", got["lse"][b, h], lse[0, 0], wl.dtype)
         if with_bwd:
-            dq, dk, dv = oracle.attn_bwd(f["q"], f["k"], f["v"], f["do"], wl.causal, c)
+            g = None if dlse is None else dlse[b:b + 1, h:h + 1]
+            dq, dk, dv = oracle.attn_bwd(f["q"], f["k"], f["v"], f["do"], wl.causal, c, dlse=g)
             terms = lambda: summand_scales(f, wl.causal, c)
             check_grad(f"{tag}.dq", got["dq"][b, h], dq[0, 0], wl.dtype, zero_scale=lambda: terms()[0])
             check_grad(f"{tag}.dk", got["dk"][b, h], dk[0, 0], wl.dtype, zero_scale=lambda: terms()[1])
@@ -122,6 +123,28 @@ def test_small_parity(case):
     t = attn_inputs(wl)
     got = run_fwd_bwd(wl, t, guard=True)
     compare(wl, t, got)
+
+
+LSE_GRAD = [
+    (BF16, 1, 2, 256, 256, 128, True),
+    (F16, 1, 2, 150, 77, 64, True),       # rows that see no key get a gradient too
+    (BF16, 1, 2, 200, 130, 64, False),
+    (F32, 1, 2, 128, 192, 64, False),
+]
+
+
+@pytest.mark.parametrize("steps", [False, True], ids=["fused", "steps"])
+@pytest.mark.parametrize("case", LSE_GRAD, ids=lambda c: "-".join(map(str, c)))
+def test_lse_gradient(case, steps):
+    """A gradient reaching LSE (dlse) on top of dO, through fa_bwd and through
+    its three steps."""
+    dtype, B, H, M, N, D, causal = case
+    wl = AttnWorkload("dlse", dtype, B, H, M, N, D, causal, seed=21 + M + N)
+    log(f"fa lse-gradient parity {case} steps={steps}")
+    t = attn_inputs(wl)
+    g = draw(wl.seed + 1, [("dlse", (B, H, M), 1.0, F32)])["dlse"]
+    got = run_fwd_bwd(wl, t, steps=steps, guard=True, dlse=dev(g))
+    compare(wl, t, got, dlse=g.f64)
 
 
 def test_steps_equal_fused_bwd():

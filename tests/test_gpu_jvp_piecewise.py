@@ -1,11 +1,12 @@
-"""GPU parity: fa_fwd_jvp, pw_fwd and pw_bwd against the fp64 oracle."""
+"""GPU parity: fa_fwd_jvp (O, LSE and both tangents), pw_fwd and pw_bwd (with
+and without a gradient reaching LSE) against the fp64 oracle."""
 
 import numpy as np
 import pytest
 
 import oracle
 from attention_fa2_tiles_amd import lib
-from attention_fa2_tiles_amd.inputs import BF16, F16, F32, PIECEWISE_W, WORKLOADS, AttnWorkload, attn_inputs
+from attention_fa2_tiles_amd.inputs import BF16, F16, F32, PIECEWISE_W, WORKLOADS, AttnWorkload, attn_inputs, draw
 from gpu_util import check_guards, dev, empty_f32, filled, guarded, guarded_f32, host, log, need_gpu
 from tolerance import check_grad, check_lse, check_output
 
@@ -24,9 +25,10 @@ def run_jvp(wl, t):
     o = guarded((B, H, M, D), wl.dtype)
     to = guarded((B, H, M, D), wl.dtype)
     lse = guarded_f32((B, H, M))
-    lib.fa_fwd_jvp(wl.dtype, q, k, v, tq, tk, tv, o, lse, to, B, H, M, N, D, wl.causal, wl.sm_scale)
+    tlse = guarded_f32((B, H, M))
+    lib.fa_fwd_jvp(wl.dtype, q, k, v, tq, tk, tv, o, lse, to, tlse, B, H, M, N, D, wl.causal, wl.sm_scale)
     torch.cuda.synchronize()
-    res = {"o": host(o), "lse": host(lse), "to": host(to)}
+    res = {"o": host(o), "lse": host(lse), "to": host(to), "tlse": host(tlse)}
     check_guards()
     return res
 
@@ -40,6 +42,7 @@ def compare_jvp(wl, t, got, heads=None):
         check_output(f"{tag}.o", got["o"][b, h], o[0, 0], wl.dtype)
         check_lse(f"{tag}.lse", got["lse"][b, h], lse[0, 0], wl.dtype)
         check_grad(f"{tag}.to", got["to"][b, h], to[0, 0], wl.dtype)
+        check_grad(f"{tag}.tlse", got["tlse"][b, h], tlse[0, 0], wl.dtype)
 
 
 JVP_SMALL = [
@@ -88,7 +91,7 @@ def test_jvp_full_size(name):
 
 # ------------------------------------------------------------ piecewise ----
 
-def run_pw(wl, t, w, with_bwd=True):
+def run_pw(wl, t, w, with_bwd=True, dlse=None):
     torch = need_gpu()
     q1, k1, q2, k2, v, do = (dev(t[n]) for n in PW_NAMES)
     B, H, M, N, D = wl.B, wl.H, wl.M, wl.N, wl.D
@@ -101,7 +104,7 @@ def run_pw(wl, t, w, with_bwd=True):
                  (("dq1", q1), ("dk1", k1), ("dq2", q2), ("dk2", k2), ("dv", v))}
         nb = lib.pw_bwd_workspace_size(B, H, M, N, D, wl.dtype)
         ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
-        lib.pw_bwd(wl.dtype, q1, k1, q2, k2, v, o, do, lse, grads["dq1"], grads["dk1"], grads["dq2"],
+        lib.pw_bwd(wl.dtype, q1, k1, q2, k2, v, o, do, lse, dlse, grads["dq1"], grads["dk1"], grads["dq2"],
                    grads["dk2"], grads["dv"], ws, nb, B, H, M, N, D, wl.causal, wl.sm_scale, w)
         out.update(grads)
     torch.cuda.synchronize()
@@ -110,7 +113,7 @@ def run_pw(wl, t, w, with_bwd=True):
     return res
 
 
-def compare_pw(wl, t, got, w, heads=None, with_bwd=True):
+def compare_pw(wl, t, got, w, heads=None, with_bwd=True, dlse=None):
     pairs = [(b, h) for b in range(wl.B) for h in range(wl.H)] if heads is None else heads
     c = wl.scale()
     for (b, h) in pairs:
@@ -120,7 +123,8 @@ def compare_pw(wl, t, got, w, heads=None, with_bwd=True):
         check_output(f"{tag}.o", got["o"][b, h], o[0, 0], wl.dtype)
         check_lse(f"{tag}.lse", got["lse"][b, h], lse[0, 0], wl.dtype)
         if with_bwd:
-            ref = oracle.pw_bwd(*f, wl.causal, c, w)
+            g = None if dlse is None else dlse[b:b + 1, h:h + 1]
+            ref = oracle.pw_bwd(*f, wl.causal, c, w, dlse=g)
             for n, r in zip(("dq1", "dk1", "dq2", "dk2", "dv"), ref):
                 check_grad(f"{tag}.{n}", got[n][b, h], r[0, 0], wl.dtype)
 
@@ -148,6 +152,17 @@ def test_pw_small(case):
     log(f"pw small parity {case}")
     t = attn_inputs(wl, PW_NAMES)
     compare_pw(wl, t, run_pw(wl, t, w), w)
+
+
+@pytest.mark.parametrize("case", [(F16, 1, 2, 256, 256, 64, True, 100), (BF16, 1, 2, 130, 250, 128, False, 60),
+                                  (F32, 1, 2, 128, 128, 64, True, 20)], ids=lambda c: "-".join(map(str, c)))
+def test_pw_lse_gradient(case):
+    dtype, B, H, M, N, D, causal, w = case
+    wl = AttnWorkload("pw_dlse", dtype, B, H, M, N, D, causal, seed=41 + M)
+    log(f"pw lse-gradient parity {case}")
+    t = attn_inputs(wl, PW_NAMES)
+    g = draw(wl.seed + 1, [("dlse", (B, H, M), 1.0, F32)])["dlse"]
+    compare_pw(wl, t, run_pw(wl, t, w, dlse=dev(g)), w, dlse=g.f64)
 
 
 def test_pw_full_size():
