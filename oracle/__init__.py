@@ -17,7 +17,8 @@ attention.py
     comment thread) and FlagAttention ``src/flag_attn/piecewise.py``.
 merge.py
     ``merge_fwd`` and ``merge_bwd`` for the block-residual two-way
-    online-softmax merge.  Source: flash_attn_res 0.1.11,
+    online-softmax merge; ``lse_merge_fwd`` and ``lse_merge_bwd``, its N-way
+    form with given logits (the merge of attention partials).  Source: flash_attn_res 0.1.11,
     ``slop/backward_phase_2.txt`` (``reference_forward`` and the phase-2 merge
     backward kernel).
 
@@ -37,4 +38,4 @@ from .attention import (  # noqa: F401
     pw_fwd,
     pw_bwd,
 )
-from .merge import merge_fwd, merge_bwd  # noqa: F401
+from .merge import merge_fwd, merge_bwd, lse_merge_fwd, lse_merge_bwd  # noqa: F401

@@ -69,3 +69,43 @@ def merge_bwd(x, q, y0, l0, gy, gl, eps):
     gx = beta[:, None] * gy + gl1[:, None] * dl1_dx
     gq = ((gl1 * rho)[:, None] * x).sum(axis=0)
     return gx, gq, gy0, gl0
+
+
+# ------------------------------------------------- N-way (y, lse) merge ----
+#
+# The same online-softmax combine with S inputs whose logits are given rather
+# than computed from x: the merge of attention partials over key splits
+# (split-KV, ring partials).  The residual merge above is its S = 2 case with
+# (y_0, l_0) = (y0, l0) and (y_1, l_1) = (x, rho x . q).  Shapes: ys [S, rows,
+# D], lses [S, rows]; a row whose S logits are all -inf merges to y = 0 and
+# lse = -inf (the convention of an attention row with no visible key).
+
+def lse_merge_fwd(ys, lses):
+    """Returns (y [rows, D], lse [rows]):
+        lse = log sum_s exp(lse_s),   y = sum_s exp(lse_s - lse) y_s."""
+    m = lses.max(axis=0)
+    has = np.isfinite(m)
+    m_safe = np.where(has, m, 0.0)
+    e = np.exp(lses - m_safe[None, :])          # exp(-inf) == 0
+    Z = e.sum(axis=0)
+    Z_safe = np.where(has, Z, 1.0)
+    w = e / Z_safe[None, :]
+    y = (w[:, :, None] * ys).sum(axis=0)
+    lse = np.where(has, m_safe + np.log(Z_safe), -np.inf)
+    return y, lse
+
+
+def lse_merge_bwd(ys, lses, gy, gl):
+    """VJP of ``lse_merge_fwd`` for <gy, y> + <gl, lse>; returns
+    (gys [S, rows, D], glses [S, rows]).  With w_s = exp(lse_s - lse):
+        d lse / d lse_s = w_s,   d y / d lse_s = w_s (y_s - y),   d y / d y_s = w_s,
+    so  gys_s = w_s gy  and  glses_s = w_s (gl + gy . (y_s - y)).
+    ``gl=None`` means zeros."""
+    y, lse = lse_merge_fwd(ys, lses)
+    if gl is None:
+        gl = np.zeros_like(lse)
+    has = np.isfinite(lse)
+    w = np.where(has[None, :], np.exp(lses - np.where(has, lse, 0.0)[None, :]), 0.0)
+    gys = w[:, :, None] * gy[None, :, :]
+    glses = w * (gl[None, :] + (gy[None, :, :] * (ys - y[None, :, :])).sum(axis=-1))
+    return gys, glses

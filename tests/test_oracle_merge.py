@@ -7,6 +7,10 @@
   low l1 returns y0.
 * A small hand-derived example (values written out in the test).
 * Central finite differences for gx, gq, gy0 and gl0.
+* N-way merge: attention over all keys equals the merge of attention over
+  key splits (against the attention oracle); the S = 2 case with the
+  logit rho x . q is the residual merge; -inf inputs and rows; finite
+  differences.
 """
 
 import math
@@ -113,3 +117,99 @@ def test_bwd_finite_differences(with_gl):
     for i, g in enumerate((gx, gq, gy0, gl0)):
         ref = fd(i, [x, q, y0, l0][i])
         np.testing.assert_allclose(g, ref, atol=1e-8 * max(1.0, np.abs(ref).max()), rtol=0)
+
+
+# ------------------------------------------------------ N-way lse merge ----
+
+def test_lse_merge_equals_attention_over_all_keys():
+    """Attention over all keys equals the merge of attention over disjoint key
+    splits (the identity split-KV attention rests on); the attention oracle is
+    an independent computation of the left side."""
+    from oracle import attention as oa
+    B, H, M, D, c = 1, 2, 7, 5, 0.6
+    splits = [3, 1, 6, 4]
+    N = sum(splits)
+    q, k, v = rand(B, H, M, D), rand(B, H, N, D), rand(B, H, N, D)
+    o_all, lse_all = oa.attn_fwd(q, k, v, False, c)
+    ys, lses, j = [], [], 0
+    for n in splits:
+        o_s, l_s = oa.attn_fwd(q, k[:, :, j:j + n], v[:, :, j:j + n], False, c)
+        ys.append(o_s.reshape(-1, D))
+        lses.append(l_s.reshape(-1))
+        j += n
+    y, lse = om.lse_merge_fwd(np.stack(ys), np.stack(lses))
+    np.testing.assert_allclose(y, o_all.reshape(-1, D), atol=1e-13, rtol=0)
+    np.testing.assert_allclose(lse, lse_all.reshape(-1), atol=1e-13, rtol=0)
+
+
+def test_lse_merge_is_the_residual_merge_with_given_logit():
+    rows, D, eps = 6, 8, 1e-6
+    x, q, y0, l0 = rand(rows, D), rand(D) / 3, rand(rows, D), rand(rows)
+    gy, gl = rand(rows, D), rand(rows)
+    y_r, lse_r = om.merge_fwd(x, q, y0, l0, eps)
+    l1 = (x @ q) / np.sqrt((x * x).mean(axis=1) + eps)
+    ys, lses = np.stack([y0, x]), np.stack([l0, l1])
+    y, lse = om.lse_merge_fwd(ys, lses)
+    np.testing.assert_allclose(y, y_r, atol=1e-14, rtol=0)
+    np.testing.assert_allclose(lse, lse_r, atol=1e-14, rtol=0)
+    # the y0 and l0 gradients are the residual merge's gy0 and gl0
+    _, _, gy0, gl0 = om.merge_bwd(x, q, y0, l0, gy, gl, eps)
+    gys, glses = om.lse_merge_bwd(ys, lses, gy, gl)
+    np.testing.assert_allclose(gys[0], gy0, atol=1e-14, rtol=0)
+    np.testing.assert_allclose(glses[0], gl0, atol=1e-13, rtol=0)
+
+
+def test_lse_merge_special_cases():
+    S, rows, D = 3, 4, 5
+    ys, lses = rand(S, rows, D), rand(S, rows)
+    # one input: identity
+    y, lse = om.lse_merge_fwd(ys[:1], lses[:1])
+    np.testing.assert_array_equal(y, ys[0])
+    np.testing.assert_array_equal(lse, lses[0])
+    # an input at -inf contributes nothing and gets zero gradients
+    l2 = lses.copy()
+    l2[1] = -np.inf
+    y, lse = om.lse_merge_fwd(ys, l2)
+    y_ref, lse_ref = om.lse_merge_fwd(ys[[0, 2]], lses[[0, 2]])
+    np.testing.assert_allclose(y, y_ref, atol=1e-15)
+    np.testing.assert_allclose(lse, lse_ref, atol=1e-15)
+    gys, glses = om.lse_merge_bwd(ys, l2, rand(rows, D), rand(rows))
+    assert np.all(gys[1] == 0) and np.all(glses[1] == 0)
+    # a row with every input at -inf: y = 0, lse = -inf, zero gradients
+    l3 = lses.copy()
+    l3[:, 2] = -np.inf
+    y, lse = om.lse_merge_fwd(ys, l3)
+    assert np.all(y[2] == 0) and np.isneginf(lse[2]) and np.all(np.isfinite(lse[[0, 1, 3]]))
+    gys, glses = om.lse_merge_bwd(ys, l3, rand(rows, D), rand(rows))
+    assert np.all(gys[:, 2] == 0) and np.all(glses[:, 2] == 0)
+    # equal logits average; lse = l + log S
+    le = np.broadcast_to(lses[:1], lses.shape).copy()
+    y, lse = om.lse_merge_fwd(ys, le)
+    np.testing.assert_allclose(y, ys.mean(axis=0), atol=1e-15)
+    np.testing.assert_allclose(lse, lses[0] + math.log(S), atol=1e-15)
+
+
+@pytest.mark.parametrize("with_gl", [True, False])
+def test_lse_merge_bwd_finite_differences(with_gl):
+    S, rows, D = 3, 2, 4
+    ys, lses, gy = rand(S, rows, D), rand(S, rows), rand(rows, D)
+    gl = rand(rows) if with_gl else None
+
+    def loss(ys_, lses_):
+        y, lse = om.lse_merge_fwd(ys_, lses_)
+        return float((y * gy).sum() + (0.0 if gl is None else (lse * gl).sum()))
+
+    def fd(a, f, h=1e-6):
+        g = np.zeros_like(a)
+        it = np.nditer(a, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            ap, am = a.copy(), a.copy()
+            ap[idx] += h
+            am[idx] -= h
+            g[idx] = (f(ap) - f(am)) / (2 * h)
+        return g
+
+    gys, glses = om.lse_merge_bwd(ys, lses, gy, gl)
+    np.testing.assert_allclose(gys, fd(ys, lambda a: loss(a, lses)), atol=1e-8, rtol=0)
+    np.testing.assert_allclose(glses, fd(lses, lambda a: loss(ys, a)), atol=1e-8, rtol=0)
