@@ -370,11 +370,12 @@ size_t resmerge_bwd_workspace_size(int rows, int D) {
 
 int resmerge_bwd(int dtype, const void* x, const void* q, const void* y0, const float* l0, const void* gy,
                  const float* gl, void* gx, float* gq, void* gy0, float* gl0, void* workspace,
-                 size_t workspace_bytes, int rows, int D, float eps, void* stream) {
+                 size_t workspace_bytes, int rows, int D, float eps, int accumulate, void* stream) {
   FA_TRY(check_tensors({x, q, y0, gy, gx, gy0}));
   FA_TRY(check_scalars({l0, gq, gl0}));
   if (gl && !aligned(gl, 4)) return FA_ERR_ALIGN;
   FA_TRY(check_merge(dtype, rows, D, eps));
+  if (accumulate != 0 && accumulate != 1) return FA_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < resmerge_bwd_workspace_size(rows, D)) return FA_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return FA_ERR_ALIGN;
   MergeArgs a = {};
@@ -393,7 +394,53 @@ int resmerge_bwd(int dtype, const void* x, const void* q, const void* y0, const 
   a.rows = rows;
   a.D = D;
   a.eps = eps;
+  a.accumulate = accumulate;
   return hip_status(fa::launch_merge_bwd(a, (hipStream_t)stream));
+}
+
+static int check_lse_merge(int dtype, int S, int rows, int D) {
+  FA_TRY(check_dtype(dtype));
+  if (S <= 0 || rows <= 0 || D <= 0) return FA_ERR_SHAPE;
+  if (S > (1 << 16) || (int64_t)S * rows * D > ((int64_t)1 << 40)) return FA_ERR_SHAPE;
+  if (D % 8 != 0 || D > 4096) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+int lse_merge_fwd(int dtype, const void* ys, const float* lses, void* y, float* lse, int S, int rows, int D,
+                  void* stream) {
+  FA_TRY(check_tensors({ys, y}));
+  FA_TRY(check_scalars({lses, lse}));
+  FA_TRY(check_lse_merge(dtype, S, rows, D));
+  fa::LseMergeArgs a = {};
+  a.dtype = dtype;
+  a.ys = ys;
+  a.lses = lses;
+  a.y = y;
+  a.lse = lse;
+  a.S = S;
+  a.rows = rows;
+  a.D = D;
+  return hip_status(fa::launch_lse_merge_fwd(a, (hipStream_t)stream));
+}
+
+int lse_merge_bwd(int dtype, const void* ys, const float* lses, const void* gy, const float* gl, void* gys,
+                  float* glses, int S, int rows, int D, void* stream) {
+  FA_TRY(check_tensors({ys, gy, gys}));
+  FA_TRY(check_scalars({lses, glses}));
+  FA_TRY(check_opt_scalars({gl}));
+  FA_TRY(check_lse_merge(dtype, S, rows, D));
+  fa::LseMergeArgs a = {};
+  a.dtype = dtype;
+  a.ys = ys;
+  a.lses = lses;
+  a.gy = gy;
+  a.gl = gl;
+  a.gys = gys;
+  a.glses = glses;
+  a.S = S;
+  a.rows = rows;
+  a.D = D;
+  return hip_status(fa::launch_lse_merge_bwd(a, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -69,6 +69,22 @@ struct MergeArgs {
   float* partial;          // bwd workspace
   int rows, D;
   float eps;
+  int accumulate;          // bwd: add gx, gq into the outputs instead of overwriting
+};
+
+struct LseMergeArgs {
+  int dtype;
+  const void* ys;          // [S, rows, D]
+  const float* lses;       // [S, rows]
+  void* y;                 // fwd [rows, D]
+  float* lse;              // fwd [rows]
+  const void* gy;          // bwd [rows, D]
+  const float* gl;         // bwd [rows] (may be null)
+  void* gys;               // bwd [S, rows, D]
+  float* glses;            // bwd [S, rows]
+  int S;
+  int64_t rows;
+  int D;
 };
 
 hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t s);
@@ -86,5 +102,8 @@ hipError_t launch_attn_dq_f32(const BwdArgs& a, hipStream_t s);
 hipError_t launch_merge_fwd(const MergeArgs& a, hipStream_t s);
 int merge_bwd_partial_rows(int rows, int D);   // number of gq partial vectors
 hipError_t launch_merge_bwd(const MergeArgs& a, hipStream_t s);
+
+hipError_t launch_lse_merge_fwd(const LseMergeArgs& a, hipStream_t s);
+hipError_t launch_lse_merge_bwd(const LseMergeArgs& a, hipStream_t s);
 
 }  // namespace fa

@@ -280,6 +280,12 @@ __global__ __launch_bounds__(kTeamWG) void merge_bwd_kernel(MergeArgs a) {
         gx[i] = mx.beta * gf[i] + cq * qf[j][i] + cx * xf[i];
         gq[j][i] += cg * xf[i];
       }
+      if (a.accumulate) {  // add into the caller's gradient (one rounding)
+        float old[E];
+        chunk_f32<T>(gxc[tm.t + j * 64 * WPR], old);
+#pragma unroll
+        for (int i = 0; i < E; ++i) gx[i] += old[i];
+      }
       gxc[tm.t + j * 64 * WPR] = f32_chunk<T>(gx);
       gyc[tm.t + j * 64 * WPR] = f32_chunk<T>(gy0);
     }
@@ -407,6 +413,12 @@ __global__ __launch_bounds__(kNTM) void merge_bwd_generic(MergeArgs a) {
         gx[i] = mx.beta * gf[i] + cq * qf[i] + cx * xf[i];
         part[c * 8 + i] += cg * xf[i];
       }
+      if (a.accumulate) {
+        float old[8];
+        to_f32(gxc[c], old);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) gx[i] += old[i];
+      }
       gxc[c] = from_f32<T>(gx);
       gyc[c] = from_f32<T>(gy0);
     }
@@ -444,13 +456,13 @@ __global__ __launch_bounds__(256) void gq_reduce_slices(const float* __restrict_
 }
 
 __global__ __launch_bounds__(256) void gq_reduce_final(const float* __restrict__ slices, float* __restrict__ gq,
-                                                       int D) {
+                                                       int D, int accumulate) {
   const int d = blockIdx.x * 256 + threadIdx.x;
   if (d >= D) return;
   float t = 0.f;
 #pragma unroll
   for (int sl = 0; sl < kRedSlices; ++sl) t += slices[(int64_t)sl * D + d];
-  gq[d] = t;
+  gq[d] = accumulate ? gq[d] + t : t;
 }
 
 int grid_for(int rows) {
@@ -576,7 +588,7 @@ hipError_t bwd_t(const MergeArgs& a, hipStream_t s) {
   float* slices = a.partial + (int64_t)np * a.D;
   hipLaunchKernelGGL(gq_reduce_slices, dim3((a.D + 127) / 128, kRedSlices), dim3(256), 0, s, a.partial, slices, np,
                      a.D);
-  hipLaunchKernelGGL(gq_reduce_final, dim3((a.D + 255) / 256), dim3(256), 0, s, slices, a.gq, a.D);
+  hipLaunchKernelGGL(gq_reduce_final, dim3((a.D + 255) / 256), dim3(256), 0, s, slices, a.gq, a.D, a.accumulate);
   return hipGetLastError();
 }
 

@@ -146,6 +146,29 @@ class MergeWorkload:
         return es * (5 * self.rows * self.D + self.D) + 12 * self.rows + 4 * self.D
 
 
+@dataclass(frozen=True)
+class LseMergeWorkload:
+    """S attention partials (o, lse) of rows = B*H*M query rows, head dim D."""
+    name: str
+    dtype: int
+    S: int
+    rows: int
+    D: int
+    seed: int
+
+    def fwd_bytes(self):
+        """Algorithmic HBM bytes of one N-way merge forward: read ys
+        (S x rows x D) and lses (S x rows, fp32); write y (rows x D) and lse."""
+        es = 4 if self.dtype == F32 else 2
+        return es * (self.S + 1) * self.rows * self.D + 4 * (self.S + 1) * self.rows
+
+    def bwd_bytes(self):
+        """Algorithmic HBM bytes of one N-way merge backward: read ys, lses,
+        gy, gl; write gys (S x rows x D) and glses (S x rows)."""
+        es = 4 if self.dtype == F32 else 2
+        return es * (2 * self.S + 1) * self.rows * self.D + 4 * (2 * self.S + 1) * self.rows
+
+
 WORKLOADS = {
     "tiny_f32": AttnWorkload("tiny_f32", F32, 1, 2, 128, 128, 64, False, 1, 0.125),
     "causal_bf16_b4h16_s2048_d128": AttnWorkload(
@@ -163,6 +186,10 @@ PIECEWISE_W = 1024
 
 MERGE_WORKLOAD = MergeWorkload("merge_bf16_rows32768_d4096", BF16, 8 * 4096, 4096, 1e-6, 5)
 
+# Split-KV combine of the causal headline shape (B4 H16 2048 query rows,
+# D128) over 4 key splits.
+LSE_MERGE_WORKLOAD = LseMergeWorkload("lse_merge_bf16_s4_rows131072_d128", BF16, 4, 4 * 16 * 2048, 128, 6)
+
 
 def attn_inputs(wl, names=("q", "k", "v", "do"), seed=None):
     """Seeded attention tensors: q-like [B,H,M,D] and k-like [B,H,N,D]."""
@@ -170,6 +197,18 @@ def attn_inputs(wl, names=("q", "k", "v", "do"), seed=None):
     kshape = (wl.B, wl.H, wl.N, wl.D)
     qlike = {"q", "do", "tq", "q1", "q2"}
     specs = [(n, qshape if n in qlike else kshape, 1.0, wl.dtype) for n in names]
+    return draw(wl.seed if seed is None else seed, specs)
+
+
+def lse_merge_inputs(wl, seed=None):
+    """Seeded N-way merge tensors: ys, lses (N(0, 4): partials of different
+    weight), gy, gl."""
+    specs = [
+        ("ys", (wl.S, wl.rows, wl.D), 1.0, wl.dtype),
+        ("lses", (wl.S, wl.rows), 2.0, F32),
+        ("gy", (wl.rows, wl.D), 1.0, wl.dtype),
+        ("gl", (wl.rows,), 1.0, F32),
+    ]
     return draw(wl.seed if seed is None else seed, specs)
 
 

@@ -52,7 +52,9 @@ _SIGNATURES = {
                 _I, _I, _I, _I, _I, _I, _F, _I, _P], _I),
     "resmerge_fwd": ([_I, _P, _P, _P, _P, _P, _P, _I, _I, _F, _P], _I),
     "resmerge_bwd_workspace_size": ([_I, _I], _Z),
-    "resmerge_bwd": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _F, _P], _I),
+    "resmerge_bwd": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _F, _I, _P], _I),
+    "lse_merge_fwd": ([_I, _P, _P, _P, _P, _I, _I, _I, _P], _I),
+    "lse_merge_bwd": ([_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P], _I),
 }
 
 EXPORTS = tuple(_SIGNATURES)
@@ -182,7 +184,18 @@ def resmerge_bwd_workspace_size(rows, D):
 
 
 def resmerge_bwd(dtype, x, q, y0, l0, gy, gl, gx, gq, gy0, gl0, workspace, workspace_bytes, rows, D, eps,
-                 stream=None):
+                 accumulate=0, stream=None):
     _check("resmerge_bwd", load().resmerge_bwd(dtype, _ptr(x), _ptr(q), _ptr(y0), _ptr(l0), _ptr(gy), _ptr(gl),
                                                _ptr(gx), _ptr(gq), _ptr(gy0), _ptr(gl0), _ptr(workspace),
-                                               workspace_bytes, rows, D, eps, _stream(stream)))
+                                               workspace_bytes, rows, D, eps, int(accumulate),
+                                               _stream(stream)))
+
+
+def lse_merge_fwd(dtype, ys, lses, y, lse, S, rows, D, stream=None):
+    _check("lse_merge_fwd", load().lse_merge_fwd(dtype, _ptr(ys), _ptr(lses), _ptr(y), _ptr(lse), S, rows, D,
+                                                 _stream(stream)))
+
+
+def lse_merge_bwd(dtype, ys, lses, gy, gl, gys, glses, S, rows, D, stream=None):
+    _check("lse_merge_bwd", load().lse_merge_bwd(dtype, _ptr(ys), _ptr(lses), _ptr(gy), _ptr(gl), _ptr(gys),
+                                                 _ptr(glses), S, rows, D, _stream(stream)))

@@ -134,6 +134,8 @@ KERNEL_SOURCES = {
     "delta": ["attention_fa2_tiles_amd/csrc/attn_bwd.hip"],
     "merge_fwd": ["attention_fa2_tiles_amd/csrc/merge.hip", "attention_fa2_tiles_amd/csrc/common.h"],
     "merge_bwd": ["attention_fa2_tiles_amd/csrc/merge.hip", "attention_fa2_tiles_amd/csrc/common.h"],
+    "lse_merge_fwd": ["attention_fa2_tiles_amd/csrc/lse_merge.hip", "attention_fa2_tiles_amd/csrc/common.h"],
+    "lse_merge_bwd": ["attention_fa2_tiles_amd/csrc/lse_merge.hip", "attention_fa2_tiles_amd/csrc/common.h"],
 }
 MERGE_NAME = "merge_bf16_rows32768_d4096"
 
@@ -309,6 +311,31 @@ def bench_merge(torch, timer, iters):
             "bwd_traffic": measured_traffic(MERGE_NAME, "merge_bwd")}
 
 
+def bench_lse_merge(torch, timer, iters):
+    from attention_fa2_tiles_amd import lib
+    from attention_fa2_tiles_amd.inputs import LSE_MERGE_WORKLOAD, lse_merge_inputs
+    from gpu_util import dev, empty, empty_f32
+    wl = LSE_MERGE_WORKLOAD
+    progress(f"component {wl.name}")
+    t = lse_merge_inputs(wl)
+    ys, lses, gy, gl = (dev(t[n]) for n in ("ys", "lses", "gy", "gl"))
+    del t
+    S, R, D = wl.S, wl.rows, wl.D
+    y, lse = empty((R, D), wl.dtype), empty_f32((R,))
+    gys, glses = empty((S, R, D), wl.dtype), empty_f32((S, R))
+    fwd = lambda: lib.lse_merge_fwd(wl.dtype, ys, lses, y, lse, S, R, D)
+    bwd = lambda: lib.lse_merge_bwd(wl.dtype, ys, lses, gy, gl, gys, glses, S, R, D)
+    f_ms = timer.avg_ms(fwd, iters)
+    b_ms = timer.avg_ms(bwd, iters)
+    f_gb = wl.fwd_bytes() / (f_ms * 1e-3) / 1e9
+    b_gb = wl.bwd_bytes() / (b_ms * 1e-3) / 1e9
+    return {"fwd_ms": round(f_ms, 4), "fwd_GB/s": round(f_gb, 1), "fwd_frac_hbm": round(f_gb / PEAK_HBM_GBPS, 4),
+            "bwd_ms": round(b_ms, 4), "bwd_GB/s": round(b_gb, 1), "bwd_frac_hbm": round(b_gb / PEAK_HBM_GBPS, 4),
+            "fwd_bytes": wl.fwd_bytes(), "bwd_bytes": wl.bwd_bytes(),
+            "fwd_traffic": measured_traffic(wl.name, "lse_merge_fwd"),
+            "bwd_traffic": measured_traffic(wl.name, "lse_merge_bwd")}
+
+
 def cpu_baseline(target_s):
     """The fp64 oracle, as it stands, on whole heads of the headline workload."""
     import numpy as np
@@ -347,12 +374,13 @@ def cpu_baseline(target_s):
 
 
 def profile_mode(torch):
-    """Launch each kernel of the headline step and the residual merge a few
-    times, then copy 256 MiB device-to-device; rocprofv3 --pmc runs wrap this
-    to count HBM bytes per dispatch, and the copy's counter value per byte is
-    the calibration."""
+    """Launch each kernel of the headline step, the residual merge and the
+    N-way merge a few times, then copy 256 MiB device-to-device; rocprofv3
+    --pmc runs wrap this to count HBM bytes per dispatch, and the copy's
+    counter value per byte is the calibration."""
     from attention_fa2_tiles_amd import lib
-    from attention_fa2_tiles_amd.inputs import MERGE_WORKLOAD, WORKLOADS, merge_inputs
+    from attention_fa2_tiles_amd.inputs import (LSE_MERGE_WORKLOAD, MERGE_WORKLOAD, WORKLOADS, lse_merge_inputs,
+                                                merge_inputs)
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from gpu_util import dev, empty, empty_f32
     wl = WORKLOADS[HEADLINE]
@@ -384,6 +412,21 @@ def profile_mode(torch):
     torch.cuda.synchronize()
     progress("profiled merge bwd")
     del x, y0, q, l0, gy, gl, y, lse, gx, gy0, gq, gl0, ws
+    lw = LSE_MERGE_WORKLOAD
+    t = lse_merge_inputs(lw)
+    ys, lses, gy, gl = (dev(t[n]) for n in ("ys", "lses", "gy", "gl"))
+    del t
+    y, lse = empty((lw.rows, lw.D), lw.dtype), empty_f32((lw.rows,))
+    gys, glses = empty((lw.S, lw.rows, lw.D), lw.dtype), empty_f32((lw.S, lw.rows))
+    for _ in range(3):
+        lib.lse_merge_fwd(lw.dtype, ys, lses, y, lse, lw.S, lw.rows, lw.D)
+    torch.cuda.synchronize()
+    progress("profiled lse_merge fwd")
+    for _ in range(3):
+        lib.lse_merge_bwd(lw.dtype, ys, lses, gy, gl, gys, glses, lw.S, lw.rows, lw.D)
+    torch.cuda.synchronize()
+    progress("profiled lse_merge bwd")
+    del ys, lses, gy, gl, y, lse, gys, glses
     torch.cuda.empty_cache()
     # calibration: an elementwise copy (dst = -src) of COPY_BYTES, launched
     # over the whole device like the kernels above
@@ -444,6 +487,7 @@ def main():
         components["jvp_f16_b4h16_s1024_d64"] = bench_jvp(torch, timer, "jvp_f16_b4h16_s1024_d64", iters)
         components["piecewise_f16_b2h16_s4096_d64_w1024"] = bench_pw(torch, timer, iters)
         components["merge_bf16_rows32768_d4096"] = bench_merge(torch, timer, iters)
+        components["lse_merge_bf16_s4_rows131072_d128"] = bench_lse_merge(torch, timer, iters)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
 
     line = {

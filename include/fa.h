@@ -180,17 +180,46 @@ int resmerge_fwd(int dtype, const void* x, const void* q, const void* y0, const 
 /*
  * Merge backward [merge: the phase-2 merge backward kernel and its
  * launcher].  VJP of resmerge_fwd for <gy, y> + <gl, lse>; gl == NULL means
- * zeros.  Outputs (all overwritten): gx, gy0 [rows, D] dtype; gl0 [rows]
- * fp32; gq [D] fp32 = sum over rows, reduced in a fixed order (no float
- * atomics, so repeated calls are bitwise identical).  workspace: at least
- * resmerge_bwd_workspace_size(rows, D) bytes of device scratch (per-block
- * partial sums of gq).
+ * zeros.  Outputs: gx, gy0 [rows, D] dtype; gl0 [rows] fp32; gq [D] fp32 =
+ * sum over rows, reduced in a fixed order (no float atomics, so repeated
+ * calls are bitwise identical).  accumulate = 0: every output is
+ * overwritten.  accumulate = 1: the gradient is added to what gx and gq
+ * hold (gx rounded once after the fp32 sum), as the page's kernel adds into
+ * the caller's grad_intrablock_partial_sum and grad_pseudo_query buffers;
+ * gy0 and gl0 are overwritten in both modes, as on the page.  Other values:
+ * FA_ERR_UNSUPPORTED.  workspace: at least resmerge_bwd_workspace_size(rows,
+ * D) bytes of device scratch (per-block partial sums of gq).
  */
 size_t resmerge_bwd_workspace_size(int rows, int D);
 int resmerge_bwd(int dtype, const void* x, const void* q, const void* y0, const float* l0,
                  const void* gy, const float* gl, void* gx, float* gq, void* gy0, float* gl0,
                  void* workspace, size_t workspace_bytes, int rows, int D, float eps,
-                 void* stream);
+                 int accumulate, void* stream);
+
+/*
+ * N-way online-softmax merge of (y, lse) partials, forward [merge: the
+ * two-way combine of reference_forward with both logits given, for S
+ * inputs].  Combines attention outputs over disjoint key ranges (e.g. the
+ * o/lse pairs of fa_fwd on key splits) into attention over all of them.
+ * Per row r:
+ *   lse = log sum_s exp(lses[s, r]),   y = sum_s exp(lses[s, r] - lse) ys[s, r]
+ * ys [S, rows, D] dtype; lses [S, rows] fp32 (natural log, may hold -inf);
+ * y [rows, D] dtype; lse [rows] fp32.  A row whose logits are all -inf
+ * gets y = 0 and lse = -inf.  1 <= S <= 65536; D a multiple of 8, at most
+ * 4096 (FA_ERR_UNSUPPORTED otherwise).
+ */
+int lse_merge_fwd(int dtype, const void* ys, const float* lses, void* y, float* lse,
+                  int S, int rows, int D, void* stream);
+
+/*
+ * Its backward: the VJP of lse_merge_fwd for <gy, y> + <gl, lse> (gl may be
+ * NULL: zeros).  With w_s = exp(lses[s] - lse):
+ *   gys[s] = w_s gy   ([S, rows, D] dtype),
+ *   glses[s] = w_s (gl + gy . (ys[s] - y))   ([S, rows] fp32).
+ * Every output element is overwritten; no workspace.
+ */
+int lse_merge_bwd(int dtype, const void* ys, const float* lses, const void* gy, const float* gl,
+                  void* gys, float* glses, int S, int rows, int D, void* stream);
 
 #ifdef __cplusplus
 }

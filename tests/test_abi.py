@@ -20,7 +20,7 @@ if not os.path.exists(lib.LIB_PATH):
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(fa_\w+|pw_\w+|resmerge_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fa_\w+|pw_\w+|resmerge_\w+|lse_merge_\w+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol():
@@ -141,8 +141,24 @@ def test_merge_rejects():
     args[12] = need
     args[7] = None  # gx
     assert status(b, *args) == -1
+    args[7] = P[7]
+    assert status(b, *args, 2) == -6  # accumulate is 0 or 1
 
 
 def test_load_missing_library_raises():
     with pytest.raises(lib.FAError):
         lib.load("/nonexistent/libfa2tiles.so")
+
+
+def test_lse_merge_rejects():
+    f, b = lib.lse_merge_fwd, lib.lse_merge_bwd
+    assert status(f, 2, P[0], P[1], P[2], P[3], 0, 100, 128) == -2      # S = 0
+    assert status(f, 2, P[0], P[1], P[2], P[3], 4, 0, 128) == -2        # no rows
+    assert status(f, 2, P[0], P[1], P[2], P[3], 4, 100, 60) == -6       # D not a multiple of 8
+    assert status(f, 2, P[0], P[1], P[2], P[3], 4, 100, 8192) == -6     # D above 4096
+    assert status(f, 5, P[0], P[1], P[2], P[3], 4, 100, 128) == -3      # dtype
+    assert status(f, 2, None, P[1], P[2], P[3], 4, 100, 128) == -1
+    assert status(f, 2, P[0] + 8, P[1], P[2], P[3], 4, 100, 128) == -4  # ys not 16-byte aligned
+    assert status(b, 2, P[0], P[1], None, None, P[4], P[5], 4, 100, 128) == -1
+    assert status(b, 2, P[0], P[1], P[2], P[3] + 2, P[4], P[5], 4, 100, 128) == -4  # gl misaligned
+    assert status(b, 2, P[0], P[1], P[2], None, P[4], P[5], 4, 100, 12) == -6

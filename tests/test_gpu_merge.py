@@ -1,11 +1,12 @@
-"""GPU parity: resmerge_fwd / resmerge_bwd against the fp64 oracle."""
+"""GPU parity: resmerge_fwd / resmerge_bwd and lse_merge_fwd / lse_merge_bwd
+against the fp64 oracle."""
 
 import numpy as np
 import pytest
 
 import oracle
 from attention_fa2_tiles_amd import lib
-from attention_fa2_tiles_amd.inputs import BF16, F16, F32, MERGE_WORKLOAD, MergeWorkload, merge_inputs
+from attention_fa2_tiles_amd.inputs import BF16, F16, F32, MERGE_WORKLOAD, MergeWorkload, draw, merge_inputs
 from gpu_util import check_guards, dev, empty, empty_f32, filled, guarded, guarded_f32, host, log, need_gpu
 from tolerance import check_grad, check_lse, check_output
 
@@ -101,3 +102,114 @@ def test_merge_full_size():
     log("merge full-size")
     t = merge_inputs(wl)
     compare(wl, t, run_merge(wl, t))
+
+
+@pytest.mark.parametrize("case", [(BF16, 37, 4096, 1e-6), (F32, 50, 2048, 1e-6), (BF16, 33, 1000, 1e-6),
+                                  (F16, 300, 1024, 1e-6)], ids=lambda c: "-".join(map(str, c)))
+def test_merge_bwd_accumulate(case):
+    """accumulate = 1 adds gx and gq into what the buffers hold (the page's
+    atomic-add semantics); gy0 and gl0 are overwritten as in mode 0."""
+    torch = need_gpu()
+    dtype, R, D, eps = case
+    wl = MergeWorkload("merge_acc", dtype, R, D, eps, seed=81 + D)
+    log(f"merge accumulate {case}")
+    t = merge_inputs(wl)
+    prior = draw(wl.seed + 1, [("gx0", (R, D), 1.0, dtype), ("gq0", (D,), 1.0, F32)])
+    x, y0, q, gy, l0, gl = (dev(t[n]) for n in ("x", "y0", "q", "gy", "l0", "gl"))
+    gx, gy0 = guarded((R, D), dtype), guarded((R, D), dtype)
+    gq, gl0 = guarded_f32((D,)), guarded_f32((R,))
+    gx.copy_(dev(prior["gx0"]))
+    gq.copy_(dev(prior["gq0"]))
+    nb = lib.resmerge_bwd_workspace_size(R, D)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    lib.resmerge_bwd(dtype, x, q, y0, l0, gy, gl, gx, gq, gy0, gl0, ws, nb, R, D, eps, 1)
+    torch.cuda.synchronize()
+    got = {n: host(v) for n, v in (("gx", gx), ("gq", gq), ("gy0", gy0), ("gl0", gl0))}
+    check_guards()
+    f = {n: t[n].f64 for n in ("x", "q", "y0", "l0", "gy", "gl")}
+    rgx, rgq, rgy0, rgl0 = oracle.merge_bwd(f["x"], f["q"], f["y0"], f["l0"], f["gy"], f["gl"], eps)
+    tag = f"merge_acc{case}"
+    check_grad(tag + ".gx", got["gx"], prior["gx0"].f64 + rgx, dtype)
+    check_grad(tag + ".gq", got["gq"], prior["gq0"].f64 + rgq, dtype)
+    check_grad(tag + ".gy0", got["gy0"], rgy0, dtype)
+    check_grad(tag + ".gl0", got["gl0"], rgl0, dtype)
+
+
+# ------------------------------------------------------ N-way lse merge ----
+
+LSE_MERGE = [
+    # dtype, S, rows, D     lanes per row x chunks per lane
+    (BF16, 4, 1000, 128),   # 16 x 1
+    (F16, 1, 77, 64),       # 8 x 1, a single input
+    (F32, 3, 50, 40),       # 8 x 1 with 3 idle lanes per row
+    (BF16, 2, 300, 4096),   # 64 x 8
+    (BF16, 5, 129, 1000),   # 64 x 2, partial last chunk round
+    (F16, 8, 333, 8),       # 1 x 1
+]
+
+
+def _lm_inputs(dtype, S, rows, D, seed, neg_inf=True):
+    t = draw(seed, [("ys", (S, rows, D), 1.0, dtype), ("lses", (S, rows), 2.0, F32),
+                    ("gy", (rows, D), 1.0, dtype), ("gl", (rows,), 1.0, F32)])
+    lses = t["lses"].f64.copy()
+    if neg_inf and S > 1:
+        lses[1, ::7] = -np.inf          # an input that contributes nothing to some rows
+        lses[:, 3 % rows] = -np.inf     # a row that sees nothing at all
+    return t, lses
+
+
+@pytest.mark.parametrize("case", LSE_MERGE, ids=lambda c: "-".join(map(str, c)))
+@pytest.mark.parametrize("with_gl", [True, False], ids=["gl", "no_gl"])
+def test_lse_merge_parity(case, with_gl):
+    torch = need_gpu()
+    dtype, S, rows, D = case
+    log(f"lse_merge parity {case} gl={with_gl}")
+    t, lses = _lm_inputs(dtype, S, rows, D, seed=91 + S + D)
+    ys, gy = dev(t["ys"]), dev(t["gy"])
+    ls = torch.from_numpy(lses.astype(np.float32)).cuda()
+    gl = dev(t["gl"]) if with_gl else None
+    y, lse = guarded((rows, D), dtype), guarded_f32((rows,))
+    gys, gls = guarded((S, rows, D), dtype), guarded_f32((S, rows))
+    lib.lse_merge_fwd(dtype, ys, ls, y, lse, S, rows, D)
+    lib.lse_merge_bwd(dtype, ys, ls, gy, gl, gys, gls, S, rows, D)
+    torch.cuda.synchronize()
+    got = {n: host(v) for n, v in (("y", y), ("lse", lse), ("gys", gys), ("gls", gls))}
+    check_guards()
+    ry, rl = oracle.lse_merge_fwd(t["ys"].f64, lses)
+    rgy, rgl = oracle.lse_merge_bwd(t["ys"].f64, lses, t["gy"].f64, t["gl"].f64 if with_gl else None)
+    tag = f"lse_merge{case}"
+    check_output(tag + ".y", got["y"], ry, dtype)
+    check_lse(tag + ".lse", got["lse"], rl, dtype)
+    check_grad(tag + ".gys", got["gys"], rgy, dtype)
+    check_grad(tag + ".glses", got["gls"], rgl, dtype)
+    if S > 1:
+        dead = np.isneginf(lses)
+        assert np.all(got["gys"][dead] == 0) and np.all(got["gls"][dead] == 0)
+
+
+def test_split_keys_attention_merge():
+    """Split-KV attention: fa_fwd on three ragged key ranges, merged by
+    lse_merge_fwd, against the oracle's attention over all keys."""
+    torch = need_gpu()
+    from attention_fa2_tiles_amd.inputs import AttnWorkload, attn_inputs
+    B, H, M, D = 1, 4, 200, 128
+    splits = [100, 77, 123]
+    N = sum(splits)
+    wl = AttnWorkload("split", BF16, B, H, M, N, D, False, seed=97)
+    t = attn_inputs(wl, ("q", "k", "v"))
+    q, k, v = (dev(t[n]) for n in ("q", "k", "v"))
+    S, rows = len(splits), B * H * M
+    ys = torch.empty((S, B, H, M, D), dtype=torch.bfloat16, device="cuda")
+    ls = torch.empty((S, B, H, M), dtype=torch.float32, device="cuda")
+    j = 0
+    for s, n in enumerate(splits):
+        ks, vs = k[:, :, j:j + n].contiguous(), v[:, :, j:j + n].contiguous()
+        lib.fa_fwd(BF16, q, ks, vs, ys[s], ls[s], B, H, M, n, D, 0, 0.0)
+        j += n
+    y, lse = guarded((rows, D), BF16), guarded_f32((rows,))
+    lib.lse_merge_fwd(BF16, ys, ls, y, lse, S, rows, D)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attn_fwd(t["q"].f64, t["k"].f64, t["v"].f64, False, wl.scale())
+    check_output("split.o", host(y), ro.reshape(rows, D), BF16)
+    check_lse("split.lse", host(lse), rl.reshape(rows), BF16)
+    check_guards()
