@@ -47,13 +47,18 @@ int check_scalars(std::initializer_list<const void*> ps) {
   return FA_OK;
 }
 
-int check_attn_shape(int B, int H, int M, int N, int D) {
+// Head dims: 32, 64, 128 for every entry point; 256 for fp32 everywhere and
+// for fp16/bf16 in the plain forward only (full = false: the fused JVP, the
+// piecewise forward and every backward step, whose 16-bit kernels keep
+// more per-row state than a 256-wide head leaves room for).
+int check_attn_shape(int B, int H, int M, int N, int D, int dtype = FA_F32, bool full = true) {
   if (B <= 0 || H <= 0 || M <= 0 || N <= 0 || D <= 0) return FA_ERR_SHAPE;
   // grid sizes and element offsets must stay representable
   const int64_t bh = (int64_t)B * H;
   if (bh > (1 << 24) || M > (1 << 24) || N > (1 << 24)) return FA_ERR_SHAPE;
   if (bh * (int64_t)(M > N ? M : N) * D > ((int64_t)1 << 46)) return FA_ERR_SHAPE;
-  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  if (D != 32 && D != 64 && D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
+  if (D == 256 && dtype != FA_F32 && !full) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
@@ -121,7 +126,7 @@ int fa_fwd(int dtype, const void* q, const void* k, const void* v, void* o, floa
   FA_TRY(check_dtype(dtype));
   FA_TRY(check_tensors({q, k, v, o}));
   FA_TRY(check_scalars({lse}));
-  FA_TRY(check_attn_shape(B, H, M, N, D));
+  FA_TRY(check_attn_shape(B, H, M, N, D, dtype, true));
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
   float scale;
   FA_TRY(resolve_scale(sm_scale, D, &scale));
@@ -161,7 +166,7 @@ static int bwd_common(int dtype, int variant, const void* q, const void* k, cons
   if (variant == fa::PW) FA_TRY(check_tensors({q2, k2, dq2, dk2}));
   FA_TRY(check_scalars({lse}));
   FA_TRY(check_opt_scalars({dlse}));
-  FA_TRY(check_attn_shape(B, H, M, N, D));
+  FA_TRY(check_attn_shape(B, H, M, N, D, dtype, false));
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
   float scale;
   FA_TRY(resolve_scale(sm_scale, D, &scale));
@@ -206,7 +211,7 @@ int fa_bwd_delta(int dtype, const void* o, const void* dout, const float* dlse, 
   FA_TRY(check_tensors({o, dout}));
   FA_TRY(check_scalars({delta}));
   FA_TRY(check_opt_scalars({dlse}));
-  FA_TRY(check_attn_shape(B, H, M, M, D));
+  FA_TRY(check_attn_shape(B, H, M, M, D, dtype, true));
   return hip_status(
       fa::launch_attn_delta(dtype, o, dout, dlse, delta, (int64_t)B * H * M, D, (hipStream_t)stream));
 }
@@ -220,7 +225,7 @@ static int bwd_pass(bool dkdv, int dtype, const void* q, const void* k, const vo
   else
     FA_TRY(check_tensors({q, k, v, dout, dq}));
   FA_TRY(check_scalars({lse, delta}));
-  FA_TRY(check_attn_shape(B, H, M, N, D));
+  FA_TRY(check_attn_shape(B, H, M, N, D, dtype, false));
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
   float scale;
   FA_TRY(resolve_scale(sm_scale, D, &scale));
@@ -266,7 +271,7 @@ int fa_fwd_jvp(int dtype, const void* q, const void* k, const void* v, const voi
   FA_TRY(check_tensors({q, k, v, tq, tk, tv, o, to}));
   FA_TRY(check_scalars({lse}));
   FA_TRY(check_opt_scalars({tlse}));
-  FA_TRY(check_attn_shape(B, H, M, N, D));
+  FA_TRY(check_attn_shape(B, H, M, N, D, dtype, false));
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
   float scale;
   FA_TRY(resolve_scale(sm_scale, D, &scale));
@@ -298,7 +303,7 @@ int pw_fwd(int dtype, const void* q1, const void* k1, const void* q2, const void
   FA_TRY(check_dtype(dtype));
   FA_TRY(check_tensors({q1, k1, q2, k2, v, o}));
   FA_TRY(check_scalars({lse}));
-  FA_TRY(check_attn_shape(B, H, M, N, D));
+  FA_TRY(check_attn_shape(B, H, M, N, D, dtype, false));
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
   float scale;
   FA_TRY(resolve_scale(sm_scale, D, &scale));

@@ -75,6 +75,11 @@ hipError_t launch_delta_t(const void* o, const void* dout, const float* dlse, fl
   else if (D == 128)
     hipLaunchKernelGGL((delta_kernel<T, 128>), grid, block, 0, s, (const T*)o, (const T*)dout, dlse, delta,
                        rows);
+  else if (D == 32)
+    hipLaunchKernelGGL((delta_kernel<T, 32>), grid, block, 0, s, (const T*)o, (const T*)dout, dlse, delta, rows);
+  else if (D == 256)
+    hipLaunchKernelGGL((delta_kernel<T, 256>), grid, block, 0, s, (const T*)o, (const T*)dout, dlse, delta,
+                       rows);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -83,10 +88,11 @@ hipError_t launch_delta_t(const void* o, const void* dout, const float* dlse, fl
 // ============================================================ dK/dV pass ==
 template <int D, int VAR>
 struct DkdvShape {
-  static constexpr int WAVES = (VAR == PW) ? 4 : 8;
+  // D = 32 tiles are too small to split their loads over 8 waves
+  static constexpr int WAVES = (VAR == PW || D == 32) ? 4 : 8;
   static constexpr int NT = 64 * WAVES;
-  static constexpr int KB = 32 * WAVES;           // keys per workgroup
-  static constexpr int QB = (D == 64) ? 64 : 32;  // query rows per streamed block
+  static constexpr int KB = 32 * WAVES;                        // keys per workgroup
+  static constexpr int QB = (D == 64 || D == 32) ? 64 : 32;    // query rows per streamed block
   static constexpr int NS = 3;                    // ring stages
 };
 
@@ -512,7 +518,7 @@ void attn_dkdv_kernel(const BwdParams p) {
 // =============================================================== dQ pass ==
 template <int D, int VAR>
 struct DqShape {
-  static constexpr int WAVES = (VAR == PW) ? 4 : 8;
+  static constexpr int WAVES = (VAR == PW || D == 32) ? 4 : 8;
   static constexpr int NT = 64 * WAVES;
   static constexpr int BM = 32 * WAVES;  // queries per workgroup
   static constexpr int BN = 64;          // keys per streamed block
@@ -944,6 +950,11 @@ hipError_t dispatch(const BwdArgs& a, hipStream_t s) {
     if (DKDV) return pw ? dkdv_t<T, 128, PW>(a, s) : dkdv_t<T, 128, PLAIN>(a, s);
     return pw ? dq_t<T, 128, PW>(a, s) : dq_t<T, 128, PLAIN>(a, s);
   }
+  if (a.D == 32) {
+    if (DKDV) return pw ? dkdv_t<T, 32, PW>(a, s) : dkdv_t<T, 32, PLAIN>(a, s);
+    return pw ? dq_t<T, 32, PW>(a, s) : dq_t<T, 32, PLAIN>(a, s);
+  }
+
   return hipErrorInvalidValue;
 }
 

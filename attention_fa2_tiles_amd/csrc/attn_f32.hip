@@ -5,8 +5,9 @@
 // the Triton tutorial's online-softmax forward and recompute backward, the
 // JVP recurrences of its ENABLE_JVP path, FlagAttention's piecewise score
 // selection -- but one wavefront owns one query row (forward, dQ) or one key
-// row (dK/dV): each lane holds D/64 of the row's head dimension and every dot
-// product is a butterfly reduction across the wavefront.  This path serves
+// row (dK/dV): lane l holds head-dimension elements l, l + 64, ... (E of
+// them; for D = 32 the upper half-wave holds none) and every dot product is
+// a butterfly reduction across the wavefront.  This path serves
 // small fp32 problems, where the 1e-4 accuracy bar rather than throughput is
 // what matters.
 #include "common.h"
@@ -23,21 +24,40 @@ __device__ __forceinline__ float wave_sum(float x) {
 
 __device__ __forceinline__ bool near_pair(int dist, int w) { return dist <= w && dist >= -w; }
 
-template <int E>
+// Head-dimension elements per lane, and whether lane holds element
+// lane + 64 e of a row of D (rows of 32 leave the upper half-wave idle).
+template <int D>
+constexpr int elems() {
+  return (D + 63) / 64;
+}
+template <int D>
+__device__ __forceinline__ bool has_col(int lane, int e) {
+  return D % 64 == 0 || lane + 64 * e < D;
+}
+template <int D>
+__device__ __forceinline__ float ld_col(const float* p, int lane, int e) {
+  return has_col<D>(lane, e) ? p[lane + 64 * e] : 0.f;
+}
+template <int D>
+__device__ __forceinline__ void st_col(float* p, int lane, int e, float v) {
+  if (has_col<D>(lane, e)) p[lane + 64 * e] = v;
+}
+
+template <int D, int E>
 __device__ __forceinline__ float dot_row(const float (&a)[E], const float* b, int lane) {
   float s = 0.f;
 #pragma unroll
-  for (int e = 0; e < E; ++e) s += a[e] * b[lane + 64 * e];
+  for (int e = 0; e < E; ++e) s += a[e] * ld_col<D>(b, lane, e);
   return wave_sum(s);
 }
 
-// One wave per query row.  E = D / 64 head-dim elements per lane.
-template <int E, int VAR>
+// One wave per query row.
+template <int D, int VAR>
 __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a, float scale, int64_t rows) {
+  constexpr int E = elems<D>();
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
-  constexpr int D = 64 * E;
   const int bh = (int)(row / a.M), i = (int)(row % a.M);
   const int pshift = a.N - a.M;
   const int64_t qoff = row * D, kbase = (int64_t)bh * a.N * D;
@@ -45,9 +65,9 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a, float scale, in
   float q[E], q2[E], tq[E], acc[E], accg[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    q[e] = Q[lane + 64 * e];
-    q2[e] = VAR == PW ? ((const float*)a.q2)[qoff + lane + 64 * e] : 0.f;
-    tq[e] = VAR == JVP ? ((const float*)a.tq)[qoff + lane + 64 * e] : 0.f;
+    q[e] = ld_col<D>(Q, lane, e);
+    q2[e] = VAR == PW ? ld_col<D>((const float*)a.q2 + qoff, lane, e) : 0.f;
+    tq[e] = VAR == JVP ? ld_col<D>((const float*)a.tq + qoff, lane, e) : 0.f;
     acc[e] = 0.f;
     accg[e] = 0.f;
   }
@@ -57,58 +77,58 @@ __global__ __launch_bounds__(256) void fwd_f32_kernel(FwdArgs a, float scale, in
     const int64_t ko = kbase + (int64_t)j * D;
     float s;
     if (VAR == PW && !near_pair(i + pshift - j, a.w))
-      s = dot_row<E>(q2, (const float*)a.k2 + ko, lane) * scale;
+      s = dot_row<D>(q2, (const float*)a.k2 + ko, lane) * scale;
     else
-      s = dot_row<E>(q, (const float*)a.k + ko, lane) * scale;
+      s = dot_row<D>(q, (const float*)a.k + ko, lane) * scale;
     const float m_new = fmaxf(m, s);
     const float alpha = expf(m - m_new);  // m = -inf on the first key -> 0
     const float pv = expf(s - m_new);
     l = alpha * l + pv;
     const float* V = (const float*)a.v + ko;
     if (VAR == JVP) {
-      const float sd = dot_row<E>(tq, (const float*)a.k + ko, lane) + dot_row<E>(q, (const float*)a.tk + ko, lane);
+      const float sd = dot_row<D>(tq, (const float*)a.k + ko, lane) + dot_row<D>(q, (const float*)a.tk + ko, lane);
       const float ps = pv * sd * scale;
       mu = alpha * mu + ps;
       const float* TV = (const float*)a.tv + ko;
 #pragma unroll
-      for (int e = 0; e < E; ++e) accg[e] = alpha * accg[e] + ps * V[lane + 64 * e] + pv * TV[lane + 64 * e];
+      for (int e = 0; e < E; ++e) accg[e] = alpha * accg[e] + ps * ld_col<D>(V, lane, e) + pv * ld_col<D>(TV, lane, e);
     }
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = alpha * acc[e] + pv * V[lane + 64 * e];
+    for (int e = 0; e < E; ++e) acc[e] = alpha * acc[e] + pv * ld_col<D>(V, lane, e);
     m = m_new;
   }
   const bool has = l > 0.f;
   const float inv = has ? 1.f / l : 0.f;
   float* O = (float*)a.o + qoff;
 #pragma unroll
-  for (int e = 0; e < E; ++e) O[lane + 64 * e] = acc[e] * inv;
+  for (int e = 0; e < E; ++e) st_col<D>(O, lane, e, acc[e] * inv);
   if (lane == 0) a.lse[row] = has ? m + logf(l) : kNegInf;
   if (VAR == JVP) {
     float* TO = (float*)a.to + qoff;
     const float c = mu * inv;
 #pragma unroll
-    for (int e = 0; e < E; ++e) TO[lane + 64 * e] = (accg[e] - c * acc[e]) * inv;
+    for (int e = 0; e < E; ++e) st_col<D>(TO, lane, e, (accg[e] - c * acc[e]) * inv);
     // LSE tangent: sum_j P_ij Sdot_ij (0 for a row with no visible key)
     if (lane == 0 && a.tlse) a.tlse[row] = c;
   }
 }
 
 // One wave per query row: dQ (piecewise: dQ1 and dQ2).
-template <int E, int VAR>
+template <int D, int VAR>
 __global__ __launch_bounds__(256) void dq_f32_kernel(BwdArgs a, int64_t rows) {
+  constexpr int E = elems<D>();
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
-  constexpr int D = 64 * E;
   const int bh = (int)(row / a.M), i = (int)(row % a.M);
   const int pshift = a.N - a.M;
   const int64_t qoff = row * D, kbase = (int64_t)bh * a.N * D;
   float q[E], q2[E], dO[E], dq[E], dq2[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    q[e] = ((const float*)a.q)[qoff + lane + 64 * e];
-    q2[e] = VAR == PW ? ((const float*)a.q2)[qoff + lane + 64 * e] : 0.f;
-    dO[e] = ((const float*)a.dout)[qoff + lane + 64 * e];
+    q[e] = ld_col<D>((const float*)a.q + qoff, lane, e);
+    q2[e] = VAR == PW ? ld_col<D>((const float*)a.q2 + qoff, lane, e) : 0.f;
+    dO[e] = ld_col<D>((const float*)a.dout + qoff, lane, e);
     dq[e] = 0.f;
     dq2[e] = 0.f;
   }
@@ -118,41 +138,41 @@ __global__ __launch_bounds__(256) void dq_f32_kernel(BwdArgs a, int64_t rows) {
     const int64_t ko = kbase + (int64_t)j * D;
     const bool far = VAR == PW && !near_pair(i + pshift - j, a.w);
     const float* Kr = far ? (const float*)a.k2 + ko : (const float*)a.k + ko;
-    const float s = dot_row<E>(far ? q2 : q, Kr, lane) * a.sm_scale;
+    const float s = dot_row<D>(far ? q2 : q, Kr, lane) * a.sm_scale;
     const float pv = expf(s - lse);
-    const float dp = dot_row<E>(dO, (const float*)a.v + ko, lane);
+    const float dp = dot_row<D>(dO, (const float*)a.v + ko, lane);
     const float ds = pv * (dp - dl);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       if (far)
-        dq2[e] += ds * Kr[lane + 64 * e];
+        dq2[e] += ds * ld_col<D>(Kr, lane, e);
       else
-        dq[e] += ds * Kr[lane + 64 * e];
+        dq[e] += ds * ld_col<D>(Kr, lane, e);
     }
   }
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    ((float*)a.dq)[qoff + lane + 64 * e] = dq[e] * a.sm_scale;
-    if (VAR == PW) ((float*)a.dq2)[qoff + lane + 64 * e] = dq2[e] * a.sm_scale;
+    st_col<D>((float*)a.dq + qoff, lane, e, dq[e] * a.sm_scale);
+    if (VAR == PW) st_col<D>((float*)a.dq2 + qoff, lane, e, dq2[e] * a.sm_scale);
   }
 }
 
 // One wave per key row: dK, dV (piecewise: dK1, dK2, dV).
-template <int E, int VAR>
+template <int D, int VAR>
 __global__ __launch_bounds__(256) void dkdv_f32_kernel(BwdArgs a, int64_t rows) {
+  constexpr int E = elems<D>();
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
-  constexpr int D = 64 * E;
   const int bh = (int)(row / a.N), j = (int)(row % a.N);
   const int pshift = a.N - a.M;
   const int64_t koff = row * D, qbase = (int64_t)bh * a.M * D, lbase = (int64_t)bh * a.M;
   float k[E], k2[E], v[E], dk[E], dk2[E], dv[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    k[e] = ((const float*)a.k)[koff + lane + 64 * e];
-    k2[e] = VAR == PW ? ((const float*)a.k2)[koff + lane + 64 * e] : 0.f;
-    v[e] = ((const float*)a.v)[koff + lane + 64 * e];
+    k[e] = ld_col<D>((const float*)a.k + koff, lane, e);
+    k2[e] = VAR == PW ? ld_col<D>((const float*)a.k2 + koff, lane, e) : 0.f;
+    v[e] = ld_col<D>((const float*)a.v + koff, lane, e);
     dk[e] = dk2[e] = dv[e] = 0.f;
   }
   const int ibeg = a.causal ? max(0, j - pshift) : 0;
@@ -161,80 +181,86 @@ __global__ __launch_bounds__(256) void dkdv_f32_kernel(BwdArgs a, int64_t rows) 
     const float lse = a.lse[lbase + i];
     const bool far = VAR == PW && !near_pair(i + pshift - j, a.w);
     const float* Qr = far ? (const float*)a.q2 + qo : (const float*)a.q + qo;
-    const float s = dot_row<E>(far ? k2 : k, Qr, lane) * a.sm_scale;
+    const float s = dot_row<D>(far ? k2 : k, Qr, lane) * a.sm_scale;
     const float pv = (lse == kNegInf) ? 0.f : expf(s - lse);
     const float* dOr = (const float*)a.dout + qo;
-    const float dp = dot_row<E>(v, dOr, lane);
+    const float dp = dot_row<D>(v, dOr, lane);
     const float ds = pv * (dp - a.delta[lbase + i]);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      dv[e] += pv * dOr[lane + 64 * e];
+      dv[e] += pv * ld_col<D>(dOr, lane, e);
       if (far)
-        dk2[e] += ds * Qr[lane + 64 * e];
+        dk2[e] += ds * ld_col<D>(Qr, lane, e);
       else
-        dk[e] += ds * Qr[lane + 64 * e];
+        dk[e] += ds * ld_col<D>(Qr, lane, e);
     }
   }
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    ((float*)a.dv)[koff + lane + 64 * e] = dv[e];
-    ((float*)a.dk)[koff + lane + 64 * e] = dk[e] * a.sm_scale;
-    if (VAR == PW) ((float*)a.dk2)[koff + lane + 64 * e] = dk2[e] * a.sm_scale;
+    st_col<D>((float*)a.dv + koff, lane, e, dv[e]);
+    st_col<D>((float*)a.dk + koff, lane, e, dk[e] * a.sm_scale);
+    if (VAR == PW) st_col<D>((float*)a.dk2 + koff, lane, e, dk2[e] * a.sm_scale);
   }
 }
 
-template <int E>
+template <int D>
 hipError_t fwd_e(const FwdArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.B * a.H * a.M;
   dim3 grid((unsigned)((rows + 3) / 4)), block(256);
   switch (a.variant) {
-    case PLAIN: hipLaunchKernelGGL((fwd_f32_kernel<E, PLAIN>), grid, block, 0, s, a, a.sm_scale, rows); break;
-    case JVP: hipLaunchKernelGGL((fwd_f32_kernel<E, JVP>), grid, block, 0, s, a, a.sm_scale, rows); break;
-    case PW: hipLaunchKernelGGL((fwd_f32_kernel<E, PW>), grid, block, 0, s, a, a.sm_scale, rows); break;
+    case PLAIN: hipLaunchKernelGGL((fwd_f32_kernel<D, PLAIN>), grid, block, 0, s, a, a.sm_scale, rows); break;
+    case JVP: hipLaunchKernelGGL((fwd_f32_kernel<D, JVP>), grid, block, 0, s, a, a.sm_scale, rows); break;
+    case PW: hipLaunchKernelGGL((fwd_f32_kernel<D, PW>), grid, block, 0, s, a, a.sm_scale, rows); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <int E>
+template <int D>
 hipError_t dq_e(const BwdArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.B * a.H * a.M;
   dim3 grid((unsigned)((rows + 3) / 4)), block(256);
   if (a.variant == PW)
-    hipLaunchKernelGGL((dq_f32_kernel<E, PW>), grid, block, 0, s, a, rows);
+    hipLaunchKernelGGL((dq_f32_kernel<D, PW>), grid, block, 0, s, a, rows);
   else
-    hipLaunchKernelGGL((dq_f32_kernel<E, PLAIN>), grid, block, 0, s, a, rows);
+    hipLaunchKernelGGL((dq_f32_kernel<D, PLAIN>), grid, block, 0, s, a, rows);
   return hipGetLastError();
 }
 
-template <int E>
+template <int D>
 hipError_t dkdv_e(const BwdArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.B * a.H * a.N;
   dim3 grid((unsigned)((rows + 3) / 4)), block(256);
   if (a.variant == PW)
-    hipLaunchKernelGGL((dkdv_f32_kernel<E, PW>), grid, block, 0, s, a, rows);
+    hipLaunchKernelGGL((dkdv_f32_kernel<D, PW>), grid, block, 0, s, a, rows);
   else
-    hipLaunchKernelGGL((dkdv_f32_kernel<E, PLAIN>), grid, block, 0, s, a, rows);
+    hipLaunchKernelGGL((dkdv_f32_kernel<D, PLAIN>), grid, block, 0, s, a, rows);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t s) {
-  if (a.D == 64) return fwd_e<1>(a, s);
-  if (a.D == 128) return fwd_e<2>(a, s);
+  if (a.D == 32) return fwd_e<32>(a, s);
+  if (a.D == 64) return fwd_e<64>(a, s);
+  if (a.D == 128) return fwd_e<128>(a, s);
+  if (a.D == 256) return fwd_e<256>(a, s);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_dq_f32(const BwdArgs& a, hipStream_t s) {
-  if (a.D == 64) return dq_e<1>(a, s);
-  if (a.D == 128) return dq_e<2>(a, s);
+  if (a.D == 32) return dq_e<32>(a, s);
+  if (a.D == 64) return dq_e<64>(a, s);
+  if (a.D == 128) return dq_e<128>(a, s);
+  if (a.D == 256) return dq_e<256>(a, s);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_dkdv_f32(const BwdArgs& a, hipStream_t s) {
-  if (a.D == 64) return dkdv_e<1>(a, s);
-  if (a.D == 128) return dkdv_e<2>(a, s);
+  if (a.D == 32) return dkdv_e<32>(a, s);
+  if (a.D == 64) return dkdv_e<64>(a, s);
+  if (a.D == 128) return dkdv_e<128>(a, s);
+  if (a.D == 256) return dkdv_e<256>(a, s);
   return hipErrorInvalidValue;
 }
 

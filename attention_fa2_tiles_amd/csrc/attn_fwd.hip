@@ -38,7 +38,7 @@ constexpr int kLdsBytes = 160 * 1024;
 // Each wave owns 32 query rows.
 template <int VAR, int D>
 struct FwdShape {
-  static constexpr int WAVES = (VAR == JVP && D == 128) ? 4 : 8;
+  static constexpr int WAVES = (D == 32 || D == 256 || (VAR == JVP && D == 128)) ? 4 : 8;
   static constexpr int NT = 64 * WAVES;
   static constexpr int BM = 32 * WAVES;
 };
@@ -297,7 +297,7 @@ void attn_fwd_kernel(const FwdParams p) {
           }
         }
       }
-    } else if constexpr (!kJvp) {
+    } else if constexpr (!kJvp && ST * KK <= 16) {
       // All ST * KK row reads of the K tile are put in flight first; product
       // i then waits only for read i.  Reads and products alternate between
       // the ST score tiles (independent accumulation chains).
@@ -316,6 +316,14 @@ void attn_fwd_kernel(const FwdParams p) {
         s[I % ST] = mfma32x32x16(kr.template get<V8>(I), qf[I / ST], s[I % ST]);
         __builtin_amdgcn_sched_barrier(0);
       });
+    } else if constexpr (!kJvp) {
+      // wide heads: one row read per product
+#pragma unroll
+      for (int st = 0; st < ST; ++st) {
+        s[st] = zero16();
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) s[st] = mfma32x32x16(krow8(cur.k[0], st, kk), qf[kk], s[st]);
+      }
     } else {
 #pragma unroll
       for (int st = 0; st < ST; ++st) {
@@ -854,7 +862,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
   p.w = a.w;
   dim3 grid(p.nmb * p.BH), block(FwdShape<VAR, D>::NT);
   const bool ragged = a.M % 64 != 0 || a.N % 64 != 0;
-  if constexpr (VAR == PLAIN) {
+  if constexpr (VAR == PLAIN && (D == 64 || D == 128)) {
     static_assert(FwdShape<PLAIN, D>::NT == 64 * kPipeWaves, "same launch shape");
     if (a.causal && ragged)
       hipLaunchKernelGGL((attn_fwd_pipe_kernel<T, D, true, true>), grid, block, 0, s, p);
@@ -891,6 +899,10 @@ template <typename T>
 hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
   if (a.D == 64) return launch_var<T, 64>(a, s);
   if (a.D == 128) return launch_var<T, 128>(a, s);
+  if (a.D == 32) return launch_var<T, 32>(a, s);
+  // D = 256: plain attention only (two K/V stages of the JVP and piecewise
+  // variants do not fit in the CU's LDS)
+  if (a.D == 256) return a.variant == PLAIN ? launch_t<T, 256, PLAIN>(a, s) : hipErrorInvalidValue;
   return hipErrorInvalidValue;
 }
 

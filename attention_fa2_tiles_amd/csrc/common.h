@@ -258,9 +258,10 @@ struct TransTile {
 
 template <int D>
 __device__ __forceinline__ int swz(int m) {
-  static_assert(D == 64 || D == 128, "head dim");
-  if constexpr (D == 128) return ((m & 3) << 2) | ((m >> 2) & 3);
-  else return (((m >> 1) & 1) << 2) | ((m >> 2) & 3);
+  static_assert(D == 32 || D == 64 || D == 128 || D == 256, "head dim");
+  if constexpr (D >= 128) return ((m & 3) << 2) | ((m >> 2) & 3);
+  else if constexpr (D == 64) return (((m >> 1) & 1) << 2) | ((m >> 2) & 3);
+  else return (m >> 2) & 3;
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));

@@ -38,8 +38,11 @@
  *   attention backward's workspace 4 bytes; the merge backward's workspace
  *   16 bytes.
  * - Supported attention shapes: B, H, M, N >= 1 (any lengths; the kernels
- *   mask the last partial tile); D in {64, 128} (FA_ERR_UNSUPPORTED
- *   otherwise).
+ *   mask the last partial tile); D in {32, 64, 128, 256}, the head dims the
+ *   tutorial's Function accepts apart from 16.  D = 256 in fp16/bf16 is
+ *   supported by fa_fwd and fa_bwd_delta only (the fused JVP, piecewise
+ *   attention and the backward need fp32 there); every other D, or D = 256
+ *   on those entry points in fp16/bf16, gives FA_ERR_UNSUPPORTED.
  *
  * Citations name the page and the function or passage whose computation the
  * entry point performs:

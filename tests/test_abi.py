@@ -77,7 +77,8 @@ def fwd_args(**kw):
     (dict(B=0), -2),
     (dict(M=-64), -2),
     (dict(D=96), -6),
-    (dict(D=32), -6),
+    (dict(D=48), -6),
+    (dict(D=16), -6),
     (dict(causal=2), -6),
     (dict(sm_scale=-1.0), -6),
     (dict(sm_scale=float("nan")), -6),
@@ -102,6 +103,19 @@ def test_bwd_rejects_small_workspace():
     args = [2, P[0], P[1], P[2], P[3], P[5], P[4], P[4] + 2, P[6], P[7], P[8], P[9], 1 << 20,
             1, 2, 128, 128, 64, 1, 0.0, None]
     assert status(lib.fa_bwd, *args) == -4
+
+
+def test_head_dim_256_support():
+    # 16-bit D = 256: plain forward only; the JVP and the backward reject it
+    assert status(lib.fa_fwd_jvp, 1, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], None,
+                  1, 1, 64, 64, 256, 0, 0.0) == -6
+    assert status(lib.fa_bwd_dq, 2, P[0], P[1], P[2], P[3], P[4], P[5], P[6],
+                  1, 1, 64, 64, 256, 0, 0.0) == -6
+    assert status(lib.pw_fwd, 2, P[0], P[1], P[2], P[3], P[4], P[5], P[6],
+                  1, 1, 64, 64, 256, 1, 0.0, 10) == -6
+    args = [2, P[0], P[1], P[2], P[3], P[5], P[4], None, P[6], P[7], P[8], P[9], 1 << 20,
+            1, 2, 128, 128, 256, 1, 0.0, None]
+    assert status(lib.fa_bwd, *args) == -6
 
 
 def test_step_entry_points_reject():

@@ -112,7 +112,27 @@ SMALL = [
     (BF16, 1, 2, 300, 1000, 128, True),   # causal key tail past a full tile
     (BF16, 1, 1, 64, 65, 128, False),     # one key past a tile
     (F32, 1, 2, 100, 130, 64, True),
+    # head dims 32 and (fp32) 256
+    (BF16, 1, 2, 200, 150, 32, True),
+    (F16, 2, 2, 128, 128, 32, False),
+    (F16, 1, 2, 77, 300, 32, True),
+    (F32, 1, 2, 100, 77, 32, True),
+    (F32, 1, 1, 64, 96, 256, True),
+    (F32, 1, 1, 70, 50, 256, False),
 ]
+
+
+@pytest.mark.parametrize("case", [(BF16, 2, 2, 200, 300, 256, True), (F16, 1, 2, 256, 256, 256, False),
+                                  (BF16, 1, 2, 128, 128, 256, True), (F16, 1, 1, 33, 65, 256, False)],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_head_dim_256_forward(case):
+    """fp16/bf16 D = 256 is served by the plain forward only."""
+    dtype, B, H, M, N, D, causal = case
+    wl = AttnWorkload("d256", dtype, B, H, M, N, D, causal, seed=13 + M + N)
+    log(f"fa d256 forward parity {case}")
+    t = attn_inputs(wl)
+    got = run_fwd_bwd(wl, t, with_bwd=False, guard=True)
+    compare(wl, t, got, with_bwd=False)
 
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "-".join(map(str, c)))

@@ -54,6 +54,9 @@ JVP_SMALL = [
     (F32, 1, 2, 128, 192, 128, True),
     (F16, 1, 2, 100, 150, 64, True),      # ragged lengths
     (BF16, 1, 2, 150, 100, 128, False),
+    (F16, 1, 2, 150, 100, 32, True),      # head dims 32 and (fp32) 256
+    (BF16, 2, 2, 128, 128, 32, False),
+    (F32, 1, 1, 64, 80, 256, True),
 ]
 
 
@@ -142,6 +145,9 @@ PW_SMALL = [
     (F32, 1, 2, 128, 192, 128, False, 50),
     (F16, 1, 2, 200, 170, 64, True, 50),       # ragged lengths
     (BF16, 1, 2, 130, 250, 128, False, 60),
+    (F16, 1, 2, 200, 170, 32, True, 50),       # head dims 32 and (fp32) 256
+    (BF16, 1, 2, 256, 256, 32, False, 100),
+    (F32, 1, 1, 64, 96, 256, True, 20),
 ]
 
 
