@@ -18,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa2tiles.so")
-SOURCES = ["attn_fwd.hip", "attn_bwd.hip", "attn_f32.hip", "merge.hip", "lse_merge.hip", "api.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip", "attn_f32.hip", "merge.hip", "lse_merge.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

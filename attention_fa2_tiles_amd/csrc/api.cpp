@@ -148,6 +148,34 @@ int fa_fwd(int dtype, const void* q, const void* k, const void* v, void* o, floa
   return run_fwd(a, (hipStream_t)stream);
 }
 
+int fa_fwd_fp8(int out_dtype, const void* q, const void* k, const void* vt, void* o, float* lse, int B, int H,
+               int M, int N, int D, int causal, float sm_scale, void* stream) {
+  if (out_dtype != FA_F16 && out_dtype != FA_BF16) return FA_ERR_DTYPE;
+  FA_TRY(check_tensors({q, k, vt, o}));
+  FA_TRY(check_scalars({lse}));
+  FA_TRY(check_attn_shape(B, H, M, N, D, out_dtype, true));
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  if (N % 16 != 0) return FA_ERR_UNSUPPORTED;
+  if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+  float scale;
+  FA_TRY(resolve_scale(sm_scale, D, &scale));
+  fa::Fp8Args a = {};
+  a.out_dtype = out_dtype;
+  a.q = q;
+  a.k = k;
+  a.vt = vt;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  a.M = M;
+  a.N = N;
+  a.D = D;
+  a.causal = causal;
+  a.sm_scale = scale;
+  return hip_status(fa::launch_attn_fwd_fp8(a, (hipStream_t)stream));
+}
+
 size_t fa_bwd_workspace_size(int B, int H, int M, int N, int D, int dtype) {
   (void)N;
   (void)D;

@@ -87,7 +87,20 @@ struct LseMergeArgs {
   int D;
 };
 
+struct Fp8Args {
+  int out_dtype;           // fa_dtype of o (fp16 or bf16)
+  const void* q;           // [B, H, M, D] e5m2
+  const void* k;           // [B, H, N, D] e5m2
+  const void* vt;          // [B, H, D, N] e5m2
+  void* o;                 // [B, H, M, D]
+  float* lse;              // [B, H, M]
+  int B, H, M, N, D;
+  int causal;
+  float sm_scale;          // resolved (> 0)
+};
+
 hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t s);
+hipError_t launch_attn_fwd_fp8(const Fp8Args& a, hipStream_t s);
 // delta = rowsum(o * dout) - dlse (dlse may be NULL: zeros)
 hipError_t launch_attn_delta(int dtype, const void* o, const void* dout, const float* dlse, float* delta,
                              int64_t rows, int D, hipStream_t s);

@@ -16,7 +16,8 @@ from dataclasses import dataclass, field
 import numpy as np
 
 F32, F16, BF16 = 0, 1, 2  # same numbering as the C ABI's dtype codes
-DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16"}
+F8E5M2 = 3                # storage only: OCP float8 e5m2 bytes (fa_fwd_fp8's q, k, vt)
+DTYPE_NAMES = {F32: "f32", F16: "f16", BF16: "bf16", F8E5M2: "f8e5m2"}
 
 
 def bf16_bits_from_f32(a):
@@ -30,6 +31,20 @@ def bf16_bits_from_f32(a):
 
 def f32_from_bf16_bits(bits):
     return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def e5m2_bits_from_f32(a):
+    """Round float32 -> float8 e5m2 (via float16, then round-to-nearest-even
+    on the low 8 bits of the float16 pattern: e5m2 is float16 with a 2-bit
+    mantissa); returns uint8 bit patterns.  Inputs here are far below the
+    e5m2 maximum (57344)."""
+    h = np.ascontiguousarray(a, dtype=np.float32).astype(np.float16).view(np.uint16).astype(np.uint32)
+    lsb = (h >> 8) & 1
+    return ((h + 0x7F + lsb) >> 8).astype(np.uint8)
+
+
+def f16_from_e5m2_bits(bits):
+    return (np.asarray(bits, dtype=np.uint8).astype(np.uint16) << 8).view(np.float16)
 
 
 def to_storage(a32, dtype):
@@ -46,6 +61,9 @@ def to_storage(a32, dtype):
     if dtype == BF16:
         s = bf16_bits_from_f32(a32)
         return s, f32_from_bf16_bits(s).astype(np.float64)
+    if dtype == F8E5M2:
+        s = e5m2_bits_from_f32(a32)
+        return s, f16_from_e5m2_bits(s).astype(np.float64)
     raise ValueError(f"unknown dtype code {dtype}")
 
 
@@ -53,6 +71,8 @@ def from_storage(s, dtype):
     """Storage array -> float64 (inverse of the rounding step's view)."""
     if dtype == BF16:
         return f32_from_bf16_bits(np.asarray(s, dtype=np.uint16)).astype(np.float64)
+    if dtype == F8E5M2:
+        return f16_from_e5m2_bits(s).astype(np.float64)
     return np.asarray(s).astype(np.float64)
 
 

@@ -40,6 +40,7 @@ _SIGNATURES = {
     "fa_strerror": ([_I], ctypes.c_char_p),
     "fa_version": ([], _I),
     "fa_fwd": ([_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P], _I),
+    "fa_fwd_fp8": ([_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P], _I),
     "fa_bwd_workspace_size": ([_I, _I, _I, _I, _I, _I], _Z),
     "fa_bwd": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _I, _F, _P], _I),
     "fa_bwd_delta": ([_I, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
@@ -121,6 +122,11 @@ def fa_version():
 def fa_fwd(dtype, q, k, v, o, lse, B, H, M, N, D, causal, sm_scale, stream=None):
     _check("fa_fwd", load().fa_fwd(dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                                    B, H, M, N, D, int(causal), sm_scale, _stream(stream)))
+
+
+def fa_fwd_fp8(out_dtype, q, k, vt, o, lse, B, H, M, N, D, causal, sm_scale, stream=None):
+    _check("fa_fwd_fp8", load().fa_fwd_fp8(out_dtype, _ptr(q), _ptr(k), _ptr(vt), _ptr(o), _ptr(lse),
+                                           B, H, M, N, D, int(causal), sm_scale, _stream(stream)))
 
 
 def fa_bwd_workspace_size(B, H, M, N, D, dtype):

@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 HEADLINE = "causal_bf16_b4h16_s2048_d128"
 METRIC = "attention fwd/bwd TFLOP/s + % bf16 MFMA peak; residual-merge HBM GB/s"
 
@@ -257,6 +258,30 @@ def bench_jvp(torch, timer, name, iters):
     tf = 3 * wl.fwd_flops() / (ms * 1e-3) / 1e12
     return {"ms": round(ms, 4), "TFLOP/s": round(tf, 2), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
             "counted_flops": "3 x forward"}
+
+
+def bench_fp8(torch, timer, iters):
+    """fa_fwd_fp8 on the causal headline shape (B4 H16 2048 D128), e5m2
+    q, k, v^t, bf16 output."""
+    import numpy as np
+    from attention_fa2_tiles_amd import lib
+    from attention_fa2_tiles_amd.inputs import BF16, F8E5M2, WORKLOADS, AttnWorkload, attn_inputs
+    from gpu_util import empty, empty_f32
+    base = WORKLOADS[HEADLINE]
+    wl = AttnWorkload("fp8_causal_b4h16_s2048_d128", F8E5M2, base.B, base.H, base.M, base.N, base.D, True,
+                      base.seed)
+    progress(f"component {wl.name}")
+    t = attn_inputs(wl, ("q", "k", "v"))
+    q = torch.from_numpy(t["q"].storage).cuda()
+    k = torch.from_numpy(t["k"].storage).cuda()
+    vt = torch.from_numpy(np.ascontiguousarray(np.swapaxes(t["v"].storage, 2, 3))).cuda()
+    del t
+    B, H, M, N, D = wl.B, wl.H, wl.M, wl.N, wl.D
+    o, lse = empty((B, H, M, D), BF16), empty_f32((B, H, M))
+    ms = timer.avg_ms(lambda: lib.fa_fwd_fp8(BF16, q, k, vt, o, lse, B, H, M, N, D, 1, 0.0), iters)
+    tf = wl.fwd_flops() / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 4), "TFLOP/s": round(tf, 2), "frac_fp8_peak": round(tf / PEAK_FP8_TFLOPS, 4),
+            "inputs": "e5m2 q, k, v (v transposed)", "output": "bf16"}
 
 
 def bench_pw(torch, timer, iters):
@@ -486,6 +511,7 @@ def main():
         components["jvp_f16_b4h16_s1024_d64_causal"] = bench_jvp(torch, timer, "jvp_f16_b4h16_s1024_d64_causal", iters)
         components["jvp_f16_b4h16_s1024_d64"] = bench_jvp(torch, timer, "jvp_f16_b4h16_s1024_d64", iters)
         components["piecewise_f16_b2h16_s4096_d64_w1024"] = bench_pw(torch, timer, iters)
+        components["fp8_causal_b4h16_s2048_d128"] = bench_fp8(torch, timer, iters)
         components["merge_bf16_rows32768_d4096"] = bench_merge(torch, timer, iters)
         components["lse_merge_bf16_s4_rows131072_d128"] = bench_lse_merge(torch, timer, iters)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)

@@ -91,6 +91,21 @@ int fa_fwd(int dtype, const void* q, const void* k, const void* v, void* o, floa
            int B, int H, int M, int N, int D, int causal, float sm_scale, void* stream);
 
 /*
+ * FP8 attention forward [tutorial: _attn_fwd with FP8_OUTPUT inputs, the
+ * float8 e5m2 path of its test and benchmark].  q [B,H,M,D], k [B,H,N,D]
+ * and vt [B,H,D,N] (V transposed, keys contiguous, as the tutorial feeds an
+ * fp8 V) hold OCP float8 e5m2 bytes; o [B,H,M,D] is written in out_dtype
+ * (FA_F16 or FA_BF16; the tutorial writes fp8 and upcasts to compare),
+ * lse [B,H,M] fp32 as fa_fwd.  Both products use fp8 matrix instructions
+ * with fp32 accumulation; P is rounded to float8 e4m3 for P V (the tutorial
+ * rounds it to e5m2).  D in {64, 128}; N a multiple of 16 (the V^t rows are
+ * read in 16-key chunks); FA_ERR_UNSUPPORTED otherwise, FA_ERR_DTYPE for
+ * another out_dtype.
+ */
+int fa_fwd_fp8(int out_dtype, const void* q, const void* k, const void* vt, void* o, float* lse,
+               int B, int H, int M, int N, int D, int causal, float sm_scale, void* stream);
+
+/*
  * Attention backward [tutorial: _attn_bwd_preprocess, _attn_bwd_dkdv,
  * _attn_bwd_dq, with the non-causal block range from the comment thread;
  * piecewise: _bwd_preprocess, _bwd_kv_kernel, _bwd_q_kernel].

@@ -118,6 +118,16 @@ def test_head_dim_256_support():
     assert status(lib.fa_bwd, *args) == -6
 
 
+def test_fp8_forward_rejects():
+    f = lib.fa_fwd_fp8
+    ok = [2, P[0], P[1], P[2], P[3], P[4], 1, 2, 64, 128, 128, 1, 0.0]
+    assert status(f, *ok[:9], 100, *ok[10:]) == -6      # N not a multiple of 16
+    assert status(f, *ok[:10], 32, *ok[11:]) == -6      # head dim 32 has no fp8 kernel
+    assert status(f, 0, *ok[1:]) == -3                  # fp32 output is not offered
+    assert status(f, *ok[:3], None, *ok[4:]) == -1
+    assert status(f, 2, P[0] + 8, *ok[2:]) == -4
+
+
 def test_step_entry_points_reject():
     assert status(lib.fa_bwd_delta, 1, P[0], P[1], None, None, 1, 1, 64, 64) == -1
     assert status(lib.fa_bwd_delta, 1, P[0], P[1], None, P[2], 1, 1, 64, 48) == -6
