@@ -11,18 +11,22 @@
 // Non-causal passes visit every block (the correction from the tutorial's
 // comment thread); causal passes start or stop at the diagonal.  In the
 // piecewise variant dS is split by the distance rule into the (q1, k1) and
-// (q2, k2) parts.
+// (q2, k2) parts: a block wholly on one side of the rule runs the plain pass
+// on that side's operands, a block that straddles it runs it twice, once
+// per side with the other side's pairs masked (dV collects P from both).
 //
 // Layout on CDNA4 (both passes stream tiles through a three-stage LDS ring
 // filled by direct global -> LDS loads, prefetching two blocks ahead):
-//  * dK/dV pass: 32 keys per wave, 8 waves (4 for piecewise) per workgroup.
+//  * dK/dV pass: 32 keys per wave, 8 waves (4 for piecewise at D = 128)
+//    per workgroup.
 //    K stays in registers (B operand of S = Q K^t), each wave's 32 rows of V
 //    stay in LDS (B operand of dP = dO V^t).  Query blocks of Q, dO and their
 //    LSE / Delta rows stream through the ring.  Each lane owns one key, so P
 //    and dS leave the score products already laid out as the B operands of
 //    dV^t += dO^t P and dK^t += Q^t dS, whose A operands (dO^t, Q^t) are
 //    transposing LDS reads of the same row-major tiles.
-//  * dQ pass: 32 queries per wave, 8 waves (4 for piecewise) per workgroup,
+//  * dQ pass: 32 queries per wave, 8 waves (4 for piecewise at D = 128)
+//    per workgroup,
 //    Q and dO resident in registers; 64-key blocks of K and V stream through
 //    the ring.  S^t = K Q^t and dP^t = V dO^t put one query per lane (LSE and
 //    Delta are per-lane scalars) and dQ^t += K^t dS^t reads K^t with
@@ -88,8 +92,9 @@ hipError_t launch_delta_t(const void* o, const void* dout, const float* dlse, fl
 // ============================================================ dK/dV pass ==
 template <int D, int VAR>
 struct DkdvShape {
-  // D = 32 tiles are too small to split their loads over 8 waves
-  static constexpr int WAVES = (VAR == PW || D == 32) ? 4 : 8;
+  // D = 32 tiles are too small to split their loads over 8 waves; the
+  // piecewise operand pairs fit 8 waves' registers only up to D = 64
+  static constexpr int WAVES = ((VAR == PW && D > 64) || D == 32) ? 4 : 8;
   static constexpr int NT = 64 * WAVES;
   static constexpr int KB = 32 * WAVES;                        // keys per workgroup
   static constexpr int QB = (D == 64 || D == 32) ? 64 : 32;    // query rows per streamed block
@@ -300,27 +305,29 @@ void attn_dkdv_kernel(const BwdParams p) {
   const int voff = (int)(reinterpret_cast<const char*>(smem.v[wave]) - sbase);
   const float neg_inv_scale = -1.f / p.sm_scale;
 
-  // One query block for this wave from stage S; MASK selects the
-  // causal-diagonal path.  Rows with LSE = -inf (no visible key) only occur
-  // in causal blocks whose every pair is masked, where P is 0 (plain: the
-  // score starts at -inf; piecewise: P is set to 0 after the exponent).
-  auto block = [&](auto stage_c, int i0, auto mask_tag) {
+  // One query block for this wave from stage S.  SEL picks the score
+  // operands and the dK accumulator: 0 = (Q tile, K, dK), 1 = (Q2 tile, K2,
+  // dK2) (piecewise only); dV takes P from either.  MODE masks pairs: none,
+  // the causal diagonal, or one side of the piecewise rule on a block that
+  // straddles it (each side also under the causal mask).  A masked pair's
+  // score starts at -inf, so its P and dS are 0; rows with LSE = -inf (no
+  // visible key) only occur in causal blocks whose every pair is masked.
+  auto sub = [&](auto stage_c, int i0, auto sel_c, auto mode_c) {
     constexpr int S = decltype(stage_c)::value;
-    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr int SEL = decltype(sel_c)::value;
+    constexpr int MODE = decltype(mode_c)::value;
     constexpr int kSt = (int)(__builtin_offsetof(Sm, st) + S * sizeof(St));
     constexpr int kDo = kSt + (int)__builtin_offsetof(St, dout);
-    constexpr int kQ0 = kSt + (int)__builtin_offsetof(St, q);
-    constexpr int kQ1 = kQ0 + Tile::ELEMS * 2;
+    constexpr int kQs = kSt + (int)__builtin_offsetof(St, q) + SEL * Tile::ELEMS * 2;
     const St& cur = smem.st[S];
-    bool an = true, af = false;
-    if constexpr (kPw) pw_classify(i0, i0 + QB - 1, kw0, kw0 + 31, pshift, p.w, an, af);
-    f32x16 s[ST], dp[ST], dsf[kPw ? ST : 1];
+    auto& ks = pick<SEL>(kf, k2f);
+    auto& dks = pick<SEL>(dkt, dk2t);
+    f32x16 s[ST], dp[ST];
 #pragma unroll
     for (int st = 0; st < ST; ++st) {
       // The score accumulator starts at -LSE / sm_scale and the dP one at
       // +Delta (this lane's 16 rows): scale2 * S is then the exponent of P
       // and the second product gives -(dP - Delta).
-      f32x16 sinit, dinit;
       {
         const f32x4* l4 = reinterpret_cast<const f32x4*>(cur.stats + 32 * st + 8 * h);
         const f32x4* d4 = reinterpret_cast<const f32x4*>(cur.stats + QB + 32 * st + 8 * h);
@@ -330,147 +337,98 @@ void attn_dkdv_kernel(const BwdParams p) {
           const f32x4 dv = d4[(g & 1) + 4 * (g >> 1)];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            sinit[4 * g + e] = lv[e] * neg_inv_scale;
-            dinit[4 * g + e] = dv[e];
+            s[st][4 * g + e] = lv[e] * neg_inv_scale;
+            dp[st][4 * g + e] = dv[e];
           }
         }
       }
+      if constexpr (MODE != kMaskNone) {
+        // row i0 + 32 st + perm_row(r, h) sits at distance perm_row(r, 0) - c0
+        // from key kj
+        const int c0 = kj - pshift - i0 - 32 * st - 8 * h;
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (!pair_kept<MODE, CAUSAL>(perm_row(r, 0) - c0, p.w)) s[st][r] = kNegInf;
+      }
+      // S = Q K^t and Delta - dP = Delta + dO (-V)^t, interleaved
       const int so = st * 32 * D * 2;
-      if constexpr (kPw) {
-        // scores S = Q K^t (rows: queries in swap23 order; column: this key)
-        f32x16 s1 = sinit, s2 = sinit;
-        if (!af) {
 #pragma unroll
-          for (int kk = 0; kk < KK; ++kk) s1 = mfma32x32x16(rd8(kQ0 + so, kk), kf[kk], s1);
-        }
-        if (!an) {
-#pragma unroll
-          for (int kk = 0; kk < KK; ++kk) s2 = mfma32x32x16(rd8(kQ1 + so, kk), k2f[kk], s2);
-        }
-        if (an) {
-          s[st] = s1;
-        } else if (af) {
-          s[st] = s2;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = i0 + 32 * st + perm_row(r, h);
-            s[st][r] = pw_near(row + pshift - kj, p.w) ? s1[r] : s2[r];
-          }
-        }
-        dp[st] = dinit;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) dp[st] = mfma32x32x16(rd8(kDo + so, kk), rd8(voff, kk), dp[st]);
-      } else {
-        // S = Q K^t and Delta - dP = Delta + dO (-V)^t, interleaved; on a
-        // causal diagonal block a pair whose key kj lies beyond its row
-        // i0 + 32 st + perm_row(r, h) starts at -inf, so that P = 0 there
-        s[st] = sinit;
-        dp[st] = dinit;
-        if constexpr (MASK) {
-          const int thr = kj - pshift - i0 - 32 * st - 8 * h;
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (thr > perm_row(r, 0)) s[st][r] = kNegInf;
-        }
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          s[st] = mfma32x32x16(rd8(kQ0 + so, kk), kf[kk], s[st]);
-          dp[st] = mfma32x32x16(rd8(kDo + so, kk), rd8(voff, kk), dp[st]);
-        }
-      }
-      if constexpr (!kPw) continue;  // plain: P / dS are formed during the accumulation below
-      // causal mask: key kj is beyond row i0 + 32 st + perm_row(r, h)
-      const int thr = kj - pshift - i0 - 32 * st - 8 * h;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = exp2_fast(s[st][r] * p.scale2);
-        if constexpr (MASK) {
-          if (thr > perm_row(r, 0)) pv = 0.f;
-        }
-        const float nds = pv * dp[st][r];  // -dS
-        s[st][r] = pv;
-        if constexpr (kPw) {
-          if (an) {
-            dp[st][r] = nds;
-          } else if (af) {
-            dp[st][r] = 0.f;
-            dsf[st][r] = nds;
-          } else {
-            const int row = i0 + 32 * st + perm_row(r, h);
-            const bool nr = pw_near(row + pshift - kj, p.w);
-            dp[st][r] = nr ? nds : 0.f;
-            dsf[st][r] = nr ? 0.f : nds;
-          }
-        } else {
-          dp[st][r] = nds;
-        }
+      for (int kk = 0; kk < KK; ++kk) {
+        s[st] = mfma32x32x16(rd8(kQs + so, kk), ks[kk], s[st]);
+        dp[st] = mfma32x32x16(rd8(kDo + so, kk), rd8(voff, kk), dp[st]);
       }
     }
-    V8 pb[PT], dsb[PT], dsfb[kPw ? PT : 1];
-    if constexpr (kPw) {
-#pragma unroll
-      for (int t = 0; t < PT; ++t) {
-        pb[t] = pack8<T>(s[t >> 1], 8 * (t & 1));
-        dsb[t] = pack8<T>(dp[t >> 1], 8 * (t & 1));
-        dsfb[t] = pack8<T>(dsf[t >> 1], 8 * (t & 1));
+    V8 pb[PT], dsb[PT];
+    // P and -dS of operand slot t (8 rows of the score tile): exponent,
+    // product with Delta - dP, packing.  Element e of slot t is formed right after
+    // the e-th product of the accumulation of slot t - 1: a wave's vector
+    // work overlaps matrix work best when it sits between its own products
+    // (with two waves per SIMD); slot 0 has nothing before it to hide under.
+    constexpr int kPer = 8 / (2 * DT) > 0 ? 8 / (2 * DT) : 1;  // elements per product
+    static_assert(8 % (2 * DT) == 0 || 2 * DT % 8 == 0, "slot split");
+    auto element = [&](auto tc, auto ec) {
+      constexpr int t = decltype(tc)::value, e = decltype(ec)::value;
+      constexpr int st = t >> 1, r = 8 * (t & 1) + e;
+      const float pv = exp2_fast(s[st][r] * p.scale2);
+      dp[st][r] = pv * dp[st][r];  // -dS
+      s[st][r] = pv;
+      if constexpr (e == 7) {
+        pb[t] = pack8<T>(s[st], 8 * (t & 1));
+        dsb[t] = pack8<T>(dp[st], 8 * (t & 1));
       }
-      // dV^t += dO^t P ;  -dK^t += Q^t (-dS_near) ;  -dK2^t += Q2^t (-dS_far)
-      if (!af)
-        accum_tr2<T, D, PT, kDo, kQ0>(dvt, dkt, tra, pb, dsb);
-      else
-        accum_tr<T, D, PT, kDo>(dvt, tra, pb);
-      if (!an) accum_tr<T, D, PT, kQ1>(dk2t, tra, dsfb);
+    };
+    static_for<8>([&](auto ec) { element(ic<0>{}, ec); });
+    // dV^t += dO^t P ;  -dK^t += Q^t (-dS), slot by slot, d-tile by d-tile;
+    // the two transposing operands of step k + 1 are read during step k.
+    TrOps<T, 1> xo[2], yo[2];
+    auto rd = [&](auto kc) {
+      constexpr int k = decltype(kc)::value, t = k / DT, dt = k % DT;
+      tr_issue<T, D, 1, kDo + t * 16 * D * 2>(xo[k & 1], tra, dt);
+      tr_issue<T, D, 1, kQs + t * 16 * D * 2>(yo[k & 1], tra, dt);
+    };
+    rd(ic<0>{});
+    static_for<PT * DT>([&](auto kc) {
+      constexpr int k = decltype(kc)::value, t = k / DT, dt = k % DT;
+      if constexpr (k + 1 < PT * DT) {
+        rd(ic<k + 1>{});
+        asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(xo[k & 1].op[0]), "+v"(yo[k & 1].op[0]));
+      } else {
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(xo[k & 1].op[0]), "+v"(yo[k & 1].op[0]));
+      }
+      // elements of slot t + 1 placed after this step's two products
+      constexpr int e0 = 2 * dt * kPer;
+      dvt[dt] = mfma32x32x16(xo[k & 1].op[0], pb[t], dvt[dt]);
+      if constexpr (t + 1 < PT) {
+        static_for<kPer>([&](auto uc) { element(ic<t + 1>{}, ic<e0 + decltype(uc)::value>{}); });
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      dks[dt] = mfma32x32x16(yo[k & 1].op[0], dsb[t], dks[dt]);
+      if constexpr (t + 1 < PT) {
+        static_for<kPer>([&](auto uc) { element(ic<t + 1>{}, ic<e0 + kPer + decltype(uc)::value>{}); });
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // One query block for this wave from stage S; MASK: a causal-diagonal
+  // block.  Piecewise: a block wholly on one side of the rule is one pass
+  // with that side's operands; a block that straddles it is two passes, each
+  // masked to its side.
+  auto block = [&](auto stage_c, int i0, auto mask_tag) {
+    constexpr int M0 = decltype(mask_tag)::value ? kMaskCausal : kMaskNone;
+    if constexpr (!kPw) {
+      sub(stage_c, i0, ic<0>{}, ic<M0>{});
     } else {
-      // P and -dS of operand slot t (8 rows of the score tile): exponent,
-      // product with Delta - dP, packing.  Element e of slot t is formed right after
-      // the e-th product of the accumulation of slot t - 1: a wave's vector
-      // work overlaps matrix work best when it sits between its own products
-      // (with two waves per SIMD); slot 0 has nothing before it to hide under.
-      constexpr int kPer = 8 / (2 * DT) > 0 ? 8 / (2 * DT) : 1;  // elements per product
-      static_assert(8 % (2 * DT) == 0 || 2 * DT % 8 == 0, "slot split");
-      auto element = [&](auto tc, auto ec) {
-        constexpr int t = decltype(tc)::value, e = decltype(ec)::value;
-        constexpr int st = t >> 1, r = 8 * (t & 1) + e;
-        const float pv = exp2_fast(s[st][r] * p.scale2);
-        dp[st][r] = pv * dp[st][r];  // -dS
-        s[st][r] = pv;
-        if constexpr (e == 7) {
-          pb[t] = pack8<T>(s[st], 8 * (t & 1));
-          dsb[t] = pack8<T>(dp[st], 8 * (t & 1));
-        }
-      };
-      static_for<8>([&](auto ec) { element(ic<0>{}, ec); });
-      // dV^t += dO^t P ;  -dK^t += Q^t (-dS), slot by slot, d-tile by d-tile;
-      // the two transposing operands of step k + 1 are read during step k.
-      TrOps<T, 1> xo[2], yo[2];
-      auto rd = [&](auto kc) {
-        constexpr int k = decltype(kc)::value, t = k / DT, dt = k % DT;
-        tr_issue<T, D, 1, kDo + t * 16 * D * 2>(xo[k & 1], tra, dt);
-        tr_issue<T, D, 1, kQ0 + t * 16 * D * 2>(yo[k & 1], tra, dt);
-      };
-      rd(ic<0>{});
-      static_for<PT * DT>([&](auto kc) {
-        constexpr int k = decltype(kc)::value, t = k / DT, dt = k % DT;
-        if constexpr (k + 1 < PT * DT) {
-          rd(ic<k + 1>{});
-          asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(xo[k & 1].op[0]), "+v"(yo[k & 1].op[0]));
-        } else {
-          asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(xo[k & 1].op[0]), "+v"(yo[k & 1].op[0]));
-        }
-        // elements of slot t + 1 placed after this step's two products
-        constexpr int e0 = 2 * dt * kPer;
-        dvt[dt] = mfma32x32x16(xo[k & 1].op[0], pb[t], dvt[dt]);
-        if constexpr (t + 1 < PT) {
-          static_for<kPer>([&](auto uc) { element(ic<t + 1>{}, ic<e0 + decltype(uc)::value>{}); });
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        dkt[dt] = mfma32x32x16(yo[k & 1].op[0], dsb[t], dkt[dt]);
-        if constexpr (t + 1 < PT) {
-          static_for<kPer>([&](auto uc) { element(ic<t + 1>{}, ic<e0 + kPer + decltype(uc)::value>{}); });
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      });
+      bool an, af;
+      pw_classify(i0, i0 + QB - 1, kw0, kw0 + 31, pshift, p.w, an, af);
+      if (an) {
+        sub(stage_c, i0, ic<0>{}, ic<M0>{});
+      } else if (af) {
+        sub(stage_c, i0, ic<1>{}, ic<M0>{});
+      } else {
+        sub(stage_c, i0, ic<0>{}, ic<kMaskNear>{});
+        sub(stage_c, i0, ic<1>{}, ic<kMaskFar>{});
+      }
     }
   };
 
@@ -518,7 +476,7 @@ void attn_dkdv_kernel(const BwdParams p) {
 // =============================================================== dQ pass ==
 template <int D, int VAR>
 struct DqShape {
-  static constexpr int WAVES = (VAR == PW || D == 32) ? 4 : 8;
+  static constexpr int WAVES = ((VAR == PW && D > 64) || D == 32) ? 4 : 8;
   static constexpr int NT = 64 * WAVES;
   static constexpr int BM = 32 * WAVES;  // queries per workgroup
   static constexpr int BN = 64;          // keys per streamed block
@@ -675,171 +633,116 @@ void attn_dq_kernel(const BwdParams p) {
     return *reinterpret_cast<const V8*>(sbase + off + rofs[kk]);
   };
 
-  // One key block for this wave from stage S; MASK selects the
-  // causal-diagonal path.
-  auto block = [&](auto stage_c, int n0, auto mask_tag) {
+  // One key block for this wave from stage S.  SEL picks the score operands
+  // and the accumulator: 0 = (K tile, Q, dQ), 1 = (K2 tile, Q2, dQ2)
+  // (piecewise only).  MODE masks pairs: none, the causal diagonal, or one
+  // side of the piecewise rule on a block that straddles it (each side also
+  // under the causal mask); a masked pair's score starts at -inf, so P = 0.
+  // The vector work of each score tile is spread between matrix products
+  // that do not depend on it (a wave's vector work overlaps matrix work best
+  // when it sits between its own products, with two waves per SIMD): tile
+  // 0's P / dS between tile 1's score products, tile 1's between the dQ
+  // products of tile 0.
+  auto sub = [&](auto stage_c, int n0, auto sel_c, auto mode_c) {
     constexpr int S = decltype(stage_c)::value;
-    constexpr bool MASK = decltype(mask_tag)::value;
-    constexpr int kK0 = (int)(__builtin_offsetof(Sm, k) + S * Tile::ELEMS * 2);
-    constexpr int kK1 = kK0 + NS * Tile::ELEMS * 2;
+    constexpr int SEL = decltype(sel_c)::value;
+    constexpr int MODE = decltype(mode_c)::value;
+    constexpr int kKs = (int)(__builtin_offsetof(Sm, k) + (SEL * NS + S) * Tile::ELEMS * 2);
     constexpr int kV = (int)(__builtin_offsetof(Sm, v) + S * Tile::ELEMS * 2);
-    bool an = true, af = false;
-    if constexpr (kPw) pw_classify(row0, row0 + 31, n0, n0 + BN - 1, pshift, p.w, an, af);
-    V8 dsb[PT], dsfb[kPw ? PT : 1];
-    if constexpr (!kPw) {
-      // Plain: the vector work of each score tile is spread between matrix
-      // products that do not depend on it (a wave's vector work overlaps
-      // matrix work best when it sits between its own products, with two
-      // waves per SIMD): tile 0's P / dS between tile 1's score products,
-      // tile 1's between the dQ products of tile 0.  On a causal diagonal
-      // block a pair whose key n0 + 32 st + perm_row(r, h) lies beyond this
-      // query starts at -inf, so that P = 0 there.
-      static_assert(ST == 2 && PT == 4, "two score tiles of 32 keys");
-      f32x16 s[ST], dp[ST];
-#pragma unroll
-      for (int st = 0; st < ST; ++st) {
-        s[st] = zero16();
-        dp[st] = zero16();
-        if constexpr (MASK) {
-          const int thr = qi + pshift - n0 - 32 * st - 8 * h;
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (perm_row(r, 0) > thr) s[st][r] = kNegInf;
-        }
-      }
-      // element r of tile st: P, dS = P (dP - Delta), packed per 8 rows.  The
-      // exponent is at most 0 for every key that exists (LSE bounds each of
-      // its row's scores); with ragged lengths it is clamped there, so that a
-      // zero-filled key past the last one (S = 0) cannot overflow P when LSE
-      // is very negative (its dS then meets a zero K row).
-      auto element = [&](auto stc, auto rc) {
-        constexpr int st = decltype(stc)::value, r = decltype(rc)::value;
-        const float x = fmaf(s[st][r], p.scale2, -lse2);
-        const float pv = exp2_fast(RAGGED ? fminf(x, 0.f) : x);
-        dp[st][r] = pv * (dp[st][r] - dl);
-        if constexpr (r % 8 == 7) dsb[2 * st + r / 8] = pack8<T>(dp[st], r - 7);
-      };
-      // S^t = K Q^t (rows: keys in swap23 order; column: this query) and
-      // dP^t = V dO^t of tile st; after product pair kk, between(kk)
-      auto products = [&](auto stc, auto&& between) {
-        constexpr int st = decltype(stc)::value;
-        constexpr int so = st * 32 * D * 2;
-        static_for<KK>([&](auto kc) {
-          constexpr int kk = decltype(kc)::value;
-          s[st] = mfma32x32x16(rd8(kK0 + so, kk), qf[kk], s[st]);
-          dp[st] = mfma32x32x16(rd8(kV + so, kk), dof[kk], dp[st]);
-          between(kc);
-          __builtin_amdgcn_sched_barrier(0);
-        });
-      };
-      products(ic<0>{}, [](auto) {});
-      constexpr int kPerKK = 16 / KK;  // tile-0 elements per product pair
-      products(ic<1>{}, [&](auto kc) {
-        constexpr int kk = decltype(kc)::value;
-        static_for<kPerKK>([&](auto uc) { element(ic<0>{}, ic<kk * kPerKK + decltype(uc)::value>{}); });
-      });
-      // dQ^t += K^t dS^t slot by slot, d-tile by d-tile; the transposing
-      // operand of step k + 1 is read during step k; tile 1's elements sit
-      // between the products of slots 0 and 1.
-      TrOps<T, 1> ko[2];
-      auto rd = [&](auto kc) {
-        constexpr int k = decltype(kc)::value, t = k / DT, dt = k % DT;
-        tr_issue<T, D, 1, kK0 + t * 16 * D * 2>(ko[k & 1], tra, dt);
-      };
-      constexpr int kPerStep = 16 / (2 * DT);  // tile-1 elements per product of slots 0, 1
-      rd(ic<0>{});
-      static_for<PT * DT>([&](auto kc) {
-        constexpr int k = decltype(kc)::value, t = k / DT, dt = k % DT;
-        if constexpr (k + 1 < PT * DT) {
-          rd(ic<k + 1>{});
-          asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(ko[k & 1].op[0]));
-        } else {
-          asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(ko[k & 1].op[0]));
-        }
-        dqt[dt] = mfma32x32x16(ko[k & 1].op[0], dsb[t], dqt[dt]);
-        if constexpr (t < 2) {
-          static_for<kPerStep>([&](auto uc) { element(ic<1>{}, ic<k * kPerStep + decltype(uc)::value>{}); });
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      });
-      return;
-    }
+    static_assert(ST == 2 && PT == 4, "two score tiles of 32 keys");
+    auto& qs = pick<SEL>(qf, q2f);
+    auto& acc = pick<SEL>(dqt, dq2t);
+    V8 dsb[PT];
+    f32x16 s[ST], dp[ST];
 #pragma unroll
     for (int st = 0; st < ST; ++st) {
-      const int so = st * 32 * D * 2;
-      // S^t = K Q^t (rows: keys in swap23 order; column: this query) and
-      // dP^t = V dO^t
-      f32x16 s, dp = zero16();
-      if constexpr (kPw) {
-        f32x16 s1 = zero16(), s2 = zero16();
-        if (!af) {
+      s[st] = zero16();
+      dp[st] = zero16();
+      if constexpr (MODE != kMaskNone) {
+        // key n0 + 32 st + perm_row(r, h) sits at distance c1 - perm_row(r, 0)
+        // from this query
+        const int c1 = qi + pshift - n0 - 32 * st - 8 * h;
 #pragma unroll
-          for (int kk = 0; kk < KK; ++kk) s1 = mfma32x32x16(rd8(kK0 + so, kk), qf[kk], s1);
-        }
-        if (!an) {
-#pragma unroll
-          for (int kk = 0; kk < KK; ++kk) s2 = mfma32x32x16(rd8(kK1 + so, kk), q2f[kk], s2);
-        }
-        if (an) {
-          s = s1;
-        } else if (af) {
-          s = s2;
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = n0 + 32 * st + perm_row(r, h);
-            s[r] = pw_near(qi + pshift - key, p.w) ? s1[r] : s2[r];
-          }
-        }
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) dp = mfma32x32x16(rd8(kV + so, kk), dof[kk], dp);
-      } else {
-        s = zero16();
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          s = mfma32x32x16(rd8(kK0 + so, kk), qf[kk], s);
-          dp = mfma32x32x16(rd8(kV + so, kk), dof[kk], dp);
-        }
-      }
-      f32x16 dsf;
-      // causal mask: key n0 + 32 st + perm_row(r, h) is beyond this query
-      const int thr = qi + pshift - n0 - 32 * st - 8 * h;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        // (clamped as in the plain path: a zero-filled key past the last one)
-        const float x = fmaf(s[r], p.scale2, -lse2);
-        float pv = exp2_fast(RAGGED ? fminf(x, 0.f) : x);
-        if constexpr (MASK) {
-          if (perm_row(r, 0) > thr) pv = 0.f;
-        }
-        const float ds = pv * (dp[r] - dl);
-        if constexpr (kPw) {
-          if (an) {
-            dp[r] = ds;
-          } else if (af) {
-            dp[r] = 0.f;
-            dsf[r] = ds;
-          } else {
-            const int key = n0 + 32 * st + perm_row(r, h);
-            const bool nr = pw_near(qi + pshift - key, p.w);
-            dp[r] = nr ? ds : 0.f;
-            dsf[r] = nr ? 0.f : ds;
-          }
-        } else {
-          dp[r] = ds;
-        }
-      }
-      dsb[2 * st] = pack8<T>(dp, 0);
-      dsb[2 * st + 1] = pack8<T>(dp, 8);
-      if constexpr (kPw) {
-        dsfb[2 * st] = pack8<T>(dsf, 0);
-        dsfb[2 * st + 1] = pack8<T>(dsf, 8);
+        for (int r = 0; r < 16; ++r)
+          if (!pair_kept<MODE, CAUSAL>(c1 - perm_row(r, 0), p.w)) s[st][r] = kNegInf;
       }
     }
-    // dQ^t += K^t dS^t  (dQ2^t += K2^t dS_far^t)
-    if (!kPw || !af) accum_tr<T, D, PT, kK0>(dqt, tra, dsb);
-    if constexpr (kPw) {
-      if (!an) accum_tr<T, D, PT, kK1>(dq2t, tra, dsfb);
+    // element r of tile st: P, dS = P (dP - Delta), packed per 8 rows.  The
+    // exponent is at most 0 for every key that exists (LSE bounds each of
+    // its row's scores); with ragged lengths it is clamped there, so that a
+    // zero-filled key past the last one (S = 0) cannot overflow P when LSE
+    // is very negative (its dS then meets a zero K row).
+    auto element = [&](auto stc, auto rc) {
+      constexpr int st = decltype(stc)::value, r = decltype(rc)::value;
+      const float x = fmaf(s[st][r], p.scale2, -lse2);
+      const float pv = exp2_fast(RAGGED ? fminf(x, 0.f) : x);
+      dp[st][r] = pv * (dp[st][r] - dl);
+      if constexpr (r % 8 == 7) dsb[2 * st + r / 8] = pack8<T>(dp[st], r - 7);
+    };
+    // S^t = K Q^t (rows: keys in swap23 order; column: this query) and
+    // dP^t = V dO^t of tile st; after product pair kk, between(kk)
+    auto products = [&](auto stc, auto&& between) {
+      constexpr int st = decltype(stc)::value;
+      constexpr int so = st * 32 * D * 2;
+      static_for<KK>([&](auto kc) {
+        constexpr int kk = decltype(kc)::value;
+        s[st] = mfma32x32x16(rd8(kKs + so, kk), qs[kk], s[st]);
+        dp[st] = mfma32x32x16(rd8(kV + so, kk), dof[kk], dp[st]);
+        between(kc);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    };
+    products(ic<0>{}, [](auto) {});
+    constexpr int kPerKK = 16 / KK;  // tile-0 elements per product pair
+    products(ic<1>{}, [&](auto kc) {
+      constexpr int kk = decltype(kc)::value;
+      static_for<kPerKK>([&](auto uc) { element(ic<0>{}, ic<kk * kPerKK + decltype(uc)::value>{}); });
+    });
+    // dQ^t += K^t dS^t slot by slot, d-tile by d-tile; the transposing
+    // operand of step k + 1 is read during step k; tile 1's elements sit
+    // between the products of slots 0 and 1.
+    TrOps<T, 1> ko[2];
+    auto rd = [&](auto kc) {
+      constexpr int k = decltype(kc)::value, t = k / DT, dt = k % DT;
+      tr_issue<T, D, 1, kKs + t * 16 * D * 2>(ko[k & 1], tra, dt);
+    };
+    constexpr int kPerStep = 16 / (2 * DT);  // tile-1 elements per product of slots 0, 1
+    rd(ic<0>{});
+    static_for<PT * DT>([&](auto kc) {
+      constexpr int k = decltype(kc)::value, t = k / DT, dt = k % DT;
+      if constexpr (k + 1 < PT * DT) {
+        rd(ic<k + 1>{});
+        asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(ko[k & 1].op[0]));
+      } else {
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(ko[k & 1].op[0]));
+      }
+      acc[dt] = mfma32x32x16(ko[k & 1].op[0], dsb[t], acc[dt]);
+      if constexpr (t < 2) {
+        static_for<kPerStep>([&](auto uc) { element(ic<1>{}, ic<k * kPerStep + decltype(uc)::value>{}); });
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // One key block for this wave from stage S; MASK: a causal-diagonal
+  // block.  Piecewise: a block wholly on one side of the rule is one pass
+  // with that side's operands; a block that straddles it is two passes, each
+  // masked to its side.
+  auto block = [&](auto stage_c, int n0, auto mask_tag) {
+    constexpr int M0 = decltype(mask_tag)::value ? kMaskCausal : kMaskNone;
+    if constexpr (!kPw) {
+      sub(stage_c, n0, ic<0>{}, ic<M0>{});
+    } else {
+      bool an, af;
+      pw_classify(row0, row0 + 31, n0, n0 + BN - 1, pshift, p.w, an, af);
+      if (an) {
+        sub(stage_c, n0, ic<0>{}, ic<M0>{});
+      } else if (af) {
+        sub(stage_c, n0, ic<1>{}, ic<M0>{});
+      } else {
+        sub(stage_c, n0, ic<0>{}, ic<kMaskNear>{});
+        sub(stage_c, n0, ic<1>{}, ic<kMaskFar>{});
+      }
     }
   };
 

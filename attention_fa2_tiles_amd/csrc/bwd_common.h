@@ -51,6 +51,32 @@ __device__ __forceinline__ void pw_classify(int r_lo, int r_hi, int c_lo, int c_
   all_far = (w < 0) || (dmin > w) || (dmax < -w);
 }
 
+// Pair masks of a score tile: none, the causal one (dist >= 0), or one side
+// of the piecewise rule (near: |dist| <= w; far: the rest), each side also
+// under the causal mask when CAUSAL.  dist = query + (N - M) - key.
+constexpr int kMaskNone = 0, kMaskCausal = 1, kMaskNear = 2, kMaskFar = 3;
+
+template <int MODE, bool CAUSAL>
+__device__ __forceinline__ bool pair_kept(int dist, int w) {
+  if constexpr (MODE == kMaskNone) {
+    return true;
+  } else if constexpr (MODE == kMaskCausal) {
+    return dist >= 0;
+  } else {
+    const bool side = (MODE == kMaskNear) == pw_near(dist, w);
+    return CAUSAL ? side && dist >= 0 : side;
+  }
+}
+
+// Compile-time choice between two operand sets (registers or accumulators).
+template <int SEL, typename A, typename B>
+__device__ __forceinline__ auto& pick(A& a, B& b) {
+  if constexpr (SEL == 0)
+    return a;
+  else
+    return b;
+}
+
 // 16-byte row reads of a DTile: row m, chunk c, as a byte offset.
 template <int D>
 __device__ __forceinline__ uint32_t row_chunk_ofs(int m, int c) {
