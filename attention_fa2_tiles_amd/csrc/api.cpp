@@ -84,19 +84,32 @@ int run_fwd(FwdArgs& a, hipStream_t s) {
   return hip_status(a.dtype == FA_F32 ? fa::launch_attn_fwd_f32(a, s) : fa::launch_attn_fwd(a, s));
 }
 
-int run_bwd_steps(BwdArgs& a, const void* o, const float* dlse, float* delta, hipStream_t s, bool do_delta,
-                  bool do_dkdv, bool do_dq) {
-  if (do_delta) {
+// The whole backward.  16-bit dtypes: the dQ pass forms Delta itself and
+// writes it for the dK/dV pass that follows (two launches); fp32: the Delta
+// kernel, then the two passes.
+int run_bwd(BwdArgs& a, const void* o, const float* dlse, float* delta, hipStream_t s) {
+  if (a.dtype == FA_F32) {
     FA_TRY(hip_status(fa::launch_attn_delta(a.dtype, o, a.dout, dlse, delta, (int64_t)a.B * a.H * a.M, a.D, s)));
+    a.delta = delta;
+    FA_TRY(hip_status(fa::launch_attn_dkdv_f32(a, s)));
+    return hip_status(fa::launch_attn_dq_f32(a, s));
   }
+  a.o = o;
+  a.dlse = dlse;
+  a.delta_out = delta;
+  FA_TRY(hip_status(fa::launch_attn_dq(a, s)));
+  a.o = nullptr;
+  a.dlse = nullptr;
+  a.delta_out = nullptr;
   a.delta = delta;
-  if (do_dkdv) {
-    FA_TRY(hip_status(a.dtype == FA_F32 ? fa::launch_attn_dkdv_f32(a, s) : fa::launch_attn_dkdv(a, s)));
-  }
-  if (do_dq) {
-    FA_TRY(hip_status(a.dtype == FA_F32 ? fa::launch_attn_dq_f32(a, s) : fa::launch_attn_dq(a, s)));
-  }
-  return FA_OK;
+  return hip_status(fa::launch_attn_dkdv(a, s));
+}
+
+// One pass of the backward (dK/dV or dQ) reading a given Delta.
+int run_bwd_pass(BwdArgs& a, const float* delta, hipStream_t s, bool dkdv) {
+  a.delta = delta;
+  if (dkdv) return hip_status(a.dtype == FA_F32 ? fa::launch_attn_dkdv_f32(a, s) : fa::launch_attn_dkdv(a, s));
+  return hip_status(a.dtype == FA_F32 ? fa::launch_attn_dq_f32(a, s) : fa::launch_attn_dq(a, s));
 }
 
 size_t delta_bytes(int B, int H, int M) { return (size_t)B * H * M * sizeof(float); }
@@ -223,7 +236,7 @@ static int bwd_common(int dtype, int variant, const void* q, const void* k, cons
   a.causal = causal;
   a.sm_scale = scale;
   a.w = w;
-  return run_bwd_steps(a, o, dlse, (float*)workspace, (hipStream_t)stream, true, true, true);
+  return run_bwd(a, o, dlse, (float*)workspace, (hipStream_t)stream);
 }
 
 int fa_bwd(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -275,7 +288,7 @@ static int bwd_pass(bool dkdv, int dtype, const void* q, const void* k, const vo
   a.D = D;
   a.causal = causal;
   a.sm_scale = scale;
-  return run_bwd_steps(a, nullptr, nullptr, (float*)delta, (hipStream_t)stream, false, dkdv, !dkdv);
+  return run_bwd_pass(a, delta, (hipStream_t)stream, dkdv);
 }
 
 int fa_bwd_dkdv(int dtype, const void* q, const void* k, const void* v, const void* dout, const float* lse,
@@ -290,6 +303,45 @@ int fa_bwd_dq(int dtype, const void* q, const void* k, const void* v, const void
               void* stream) {
   return bwd_pass(false, dtype, q, k, v, dout, lse, delta, dq, nullptr, nullptr, B, H, M, N, D, causal, sm_scale,
                   stream);
+}
+
+int fa_bwd_dq_delta(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, const float* dlse, float* delta, void* dq, int B, int H, int M, int N, int D,
+                    int causal, float sm_scale, void* stream) {
+  FA_TRY(check_dtype(dtype));
+  FA_TRY(check_tensors({q, k, v, o, dout, dq}));
+  FA_TRY(check_scalars({lse, delta}));
+  FA_TRY(check_opt_scalars({dlse}));
+  FA_TRY(check_attn_shape(B, H, M, N, D, dtype, false));
+  if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+  float scale;
+  FA_TRY(resolve_scale(sm_scale, D, &scale));
+  BwdArgs a = {};
+  a.dtype = dtype;
+  a.variant = fa::PLAIN;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.B = B;
+  a.H = H;
+  a.M = M;
+  a.N = N;
+  a.D = D;
+  a.causal = causal;
+  a.sm_scale = scale;
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == FA_F32) {
+    FA_TRY(hip_status(fa::launch_attn_delta(dtype, o, dout, dlse, delta, (int64_t)B * H * M, D, s)));
+    a.delta = delta;
+    return hip_status(fa::launch_attn_dq_f32(a, s));
+  }
+  a.o = o;
+  a.dlse = dlse;
+  a.delta_out = delta;
+  return hip_status(fa::launch_attn_dq(a, s));
 }
 
 int fa_fwd_jvp(int dtype, const void* q, const void* k, const void* v, const void* tq, const void* tk,

@@ -61,10 +61,11 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ o, con
     const Row8<T> a = *reinterpret_cast<const Row8<T>*>(o + row * D + 8 * c);
     const Row8<T> b = *reinterpret_cast<const Row8<T>*>(dout + row * D + 8 * c);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sum += (float)a.e[e] * (float)b.e[e];
+    for (int e = 0; e < 8; ++e) sum = fmaf((float)a.e[e], (float)b.e[e], sum);
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off, 64);
+  // (the dQ pass that forms Delta itself sums in this same order)
   // A gradient reaching LSE adds P * dLSE to dS, i.e. it lowers Delta.
   if (row < rows && c == 0) delta[row] = dlse ? sum - dlse[row] : sum;
 }
@@ -558,7 +559,30 @@ void attn_dq_kernel(const BwdParams p) {
       if constexpr (kPw) q2f[kk] = *reinterpret_cast<const V8*>((const T*)p.q2 + off + 16 * kk);
     }
     lse2 = lse_to_log2(p.lse[(int64_t)bh * p.M + qr]);
-    dl = p.delta[(int64_t)bh * p.M + qr];
+    if (p.delta_out) {
+      // Delta_i = sum_d O_id dO_id - dLSE_i, in the delta kernel's order:
+      // fma chains over 16-byte chunks, then the chunk sums pairwise with
+      // stride half the chunk count (chunk 2 kk + h sits in slot kk of half h)
+      const T* orow = (const T*)p.o + off;
+      float cs[KK];
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const V8 ov = *reinterpret_cast<const V8*>(orow + 16 * kk);
+        cs[kk] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) cs[kk] = fmaf((float)ov[e], (float)dof[kk][e], cs[kk]);
+      }
+#pragma unroll
+      for (int half = KK / 2; half >= 1; half /= 2) {
+#pragma unroll
+        for (int kk = 0; kk < half; ++kk) cs[kk] += cs[kk + half];
+      }
+      dl = halves_sum(cs[0]);
+      if (p.dlse) dl -= p.dlse[(int64_t)bh * p.M + qr];
+      if (h == 0 && (!RAGGED || qi < p.M)) p.delta_out[(int64_t)bh * p.M + qi] = dl;
+    } else {
+      dl = p.delta[(int64_t)bh * p.M + qr];
+    }
   }
 
   f32x16 dqt[DT], dq2t[kPw ? DT : 1];
@@ -791,6 +815,9 @@ BwdParams make_params(const BwdArgs& a) {
   p.dout = a.dout;
   p.lse = a.lse;
   p.delta = a.delta;
+  p.o = a.o;
+  p.dlse = a.dlse;
+  p.delta_out = a.delta_out;
   p.dq = a.dq;
   p.dk = a.dk;
   p.dv = a.dv;

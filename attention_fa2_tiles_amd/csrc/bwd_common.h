@@ -22,6 +22,11 @@ struct BwdParams {
   const void* dout;
   const float* lse;
   const float* delta;
+  // dQ pass only: when delta_out is set, the pass forms each row's Delta from
+  // o, dout and dlse itself and writes it there (delta is then unused)
+  const void* o;
+  const float* dlse;
+  float* delta_out;
   void* dq;
   void* dk;
   void* dv;

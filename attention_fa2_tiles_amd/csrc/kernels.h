@@ -41,6 +41,9 @@ struct BwdArgs {
   const void* dout;
   const float* lse;
   const float* delta;
+  const void* o;           // dQ pass with Delta: o, dlse (may be NULL) and
+  const float* dlse;       // the Delta output; NULL delta_out = read delta
+  float* delta_out;
   void* dq;                // (PW: dq1)
   void* dk;                // (PW: dk1)
   void* dv;

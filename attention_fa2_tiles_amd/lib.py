@@ -46,6 +46,7 @@ _SIGNATURES = {
     "fa_bwd_delta": ([_I, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "fa_bwd_dkdv": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P], _I),
     "fa_bwd_dq": ([_I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P], _I),
+    "fa_bwd_dq_delta": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P], _I),
     "fa_fwd_jvp": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P], _I),
     "pw_fwd": ([_I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P], _I),
     "pw_bwd_workspace_size": ([_I, _I, _I, _I, _I, _I], _Z),
@@ -155,6 +156,12 @@ def fa_bwd_dq(dtype, q, k, v, dout, lse, delta, dq, B, H, M, N, D, causal, sm_sc
     _check("fa_bwd_dq", load().fa_bwd_dq(dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse),
                                          _ptr(delta), _ptr(dq), B, H, M, N, D, int(causal), sm_scale,
                                          _stream(stream)))
+
+
+def fa_bwd_dq_delta(dtype, q, k, v, o, dout, lse, dlse, delta, dq, B, H, M, N, D, causal, sm_scale, stream=None):
+    _check("fa_bwd_dq_delta", load().fa_bwd_dq_delta(dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout),
+                                                     _ptr(lse), _ptr(dlse), _ptr(delta), _ptr(dq), B, H, M, N, D,
+                                                     int(causal), sm_scale, _stream(stream)))
 
 
 def fa_fwd_jvp(dtype, q, k, v, tq, tk, tv, o, lse, to, tlse, B, H, M, N, D, causal, sm_scale, stream=None):

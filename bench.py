@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the tiled-attention hot path on one MI355X.
 
-One step = fa_fwd + fa_bwd (Delta, dK/dV and dQ launches) on the causal bf16
+One step = fa_fwd + fa_bwd (a dQ launch that also forms Delta, then dK/dV) on the causal bf16
 workload B=4, H=16, M=N=2048, D=128 with inputs already resident in HBM.
 ``value`` is that step's throughput in TFLOP/s under the Triton tutorial's
 flop convention (forward 4*B*H*M*N*D, halved for causal; backward 2.5x the
@@ -96,7 +96,9 @@ def attn_calls(wl, d, b):
         "delta": lambda: lib.fa_bwd_delta(wl.dtype, b["o"], do, None, b["delta"], B, H, M, D),
         "dkdv": lambda: lib.fa_bwd_dkdv(wl.dtype, q, k, v, do, b["lse"], b["delta"], b["dk"], b["dv"],
                                         B, H, M, N, D, c, s),
-        "dq": lambda: lib.fa_bwd_dq(wl.dtype, q, k, v, do, b["lse"], b["delta"], b["dq"], B, H, M, N, D, c, s),
+        # the launch fa_bwd makes for 16-bit dtypes: the dQ pass forming Delta
+        "dq": lambda: lib.fa_bwd_dq_delta(wl.dtype, q, k, v, b["o"], do, b["lse"], None, b["delta"], b["dq"],
+                                          B, H, M, N, D, c, s),
     }
 
 
@@ -106,8 +108,9 @@ def kernel_work(wl):
     GEMM-equivalents of 2*M*N*D flops per head (halved when causal): the
     forward does two (S, PV); the backward's five (S recomputed, dP, dV, dK,
     dQ -- the 2.5x of the flop convention) are split as four for the dK/dV
-    kernel and one (dQ) for the dQ kernel, which also recomputes S and dP.
-    Delta is bandwidth-bound: it reads O and dO and writes one fp32 per row."""
+    kernel and one (dQ) for the dQ kernel, which also recomputes S and dP
+    and forms Delta (reading O).  The standalone Delta kernel (fp32 path) is
+    bandwidth-bound: it reads O and dO and writes one fp32 per row."""
     g = 2.0 * wl.B * wl.H * wl.M * wl.N * wl.D * (0.5 if wl.causal else 1.0)
     es = 4 if wl.dtype == 0 else 2
     return {
@@ -188,7 +191,7 @@ def bench_headline(torch, args, timer):
 
     progress("per-kernel timing")
     iters = max(args.steps, 10)
-    per = {k: timer.avg_ms(calls[k], iters) for k in ("fwd", "delta", "dkdv", "dq")}
+    per = {k: timer.avg_ms(calls[k], iters) for k in ("fwd", "dq", "dkdv")}
     work = kernel_work(wl)
     kernels = {}
     for k, ms in per.items():
@@ -413,7 +416,7 @@ def profile_mode(torch):
     b = attn_buffers(torch, wl, d)
     calls = attn_calls(wl, d, b)
     calls["fwd"]()
-    for k in ("fwd", "delta", "dkdv", "dq"):
+    for k in ("fwd", "dq", "dkdv"):
         for _ in range(3):
             calls[k]()
         torch.cuda.synchronize()

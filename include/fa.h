@@ -114,10 +114,13 @@ int fa_fwd_fp8(int out_dtype, const void* q, const void* k, const void* vt, void
  * fp32 is the gradient reaching the LSE output (e.g. resmerge_bwd's gl0);
  * NULL means zeros and gives the pages' backward.  The pages' backward has
  * no such input: by the chain rule dLSE_i/dS_ij = P_ij, so it enters as
- * dS = P (dP - (Delta - dlse)).  Three launches on `stream`:
+ * dS = P (dP - (Delta - dlse)).  The steps:
  *   Delta_i = sum_d o_id dout_id - dlse_i           (fa_bwd_delta)
  *   dK, dV  with K/V resident, looping over queries  (fa_bwd_dkdv)
  *   dQ      with Q resident, looping over keys       (fa_bwd_dq)
+ * For fp16/bf16 fa_bwd makes two launches on `stream`: fa_bwd_dq_delta (the
+ * dQ pass forming Delta as it loads each query row, and writing it to the
+ * workspace), then fa_bwd_dkdv; for fp32, the three steps above in order.
  * workspace: device buffer of at least fa_bwd_workspace_size() bytes (it
  * holds Delta); it is scratch, its content on return is unspecified.
  */
@@ -140,6 +143,14 @@ int fa_bwd_dkdv(int dtype, const void* q, const void* k, const void* v, const vo
 int fa_bwd_dq(int dtype, const void* q, const void* k, const void* v, const void* dout,
               const float* lse, const float* delta, void* dq,
               int B, int H, int M, int N, int D, int causal, float sm_scale, void* stream);
+/* The preprocess and the dQ pass in one launch [tutorial: _attn_bwd_preprocess
+ * and _attn_bwd_dq]: each query row's Delta is formed from o, dout and dlse
+ * (NULL = zeros) as that row's operands are loaded, written to delta [B,H,M]
+ * fp32 (bit-identical to fa_bwd_delta's) and used for dq.  fp32 runs
+ * fa_bwd_delta then fa_bwd_dq.  Same argument rules as fa_bwd_dq. */
+int fa_bwd_dq_delta(int dtype, const void* q, const void* k, const void* v, const void* o,
+                    const void* dout, const float* lse, const float* dlse, float* delta, void* dq,
+                    int B, int H, int M, int N, int D, int causal, float sm_scale, void* stream);
 
 /*
  * Fused forward-mode JVP [tutorial: the ENABLE_JVP path of _attn_fwd_inner

@@ -136,6 +136,14 @@ def test_step_entry_points_reject():
                   1, 1, 64, 64, 64, 0, 0.0) == -1
     assert status(lib.fa_bwd_dq, 2, P[0], P[1], P[2], P[3], P[4], P[5], P[6],
                   1, 1, 64, 64, 64, 3, 0.0) == -6
+    f = lib.fa_bwd_dq_delta
+    ok = [2, P[0], P[1], P[2], P[3], P[4], P[5], None, P[6], P[7], 1, 1, 64, 64, 64, 0, 0.0]
+    assert status(f, *ok[:4], None, *ok[5:]) == -1                 # o missing
+    assert status(f, *ok[:8], None, *ok[9:]) == -1                 # delta missing
+    assert status(f, *ok[:7], P[8] + 2, *ok[8:]) == -4             # dlse misaligned
+    assert status(f, *ok[:14], 256, *ok[15:]) == -6                # 16-bit D = 256
+    assert status(f, *ok[:15], 2, *ok[16:]) == -6                  # causal not 0/1
+    assert status(f, 5, *ok[1:]) == -3
 
 
 def test_jvp_and_pw_reject():

@@ -177,6 +177,33 @@ def test_steps_equal_fused_bwd():
         assert np.array_equal(a[n], b[n]), n
 
 
+@pytest.mark.parametrize("case", [(BF16, 1, 2, 256, 256, 128, True, False), (F16, 2, 2, 300, 200, 64, False, True),
+                                  (BF16, 1, 3, 130, 250, 32, True, True), (F16, 1, 2, 512, 512, 128, False, False),
+                                  (F32, 1, 2, 128, 192, 64, True, True)],
+                         ids=lambda c: "-".join(map(str, c)))
+def test_dq_delta_equals_steps(case):
+    """fa_bwd_dq_delta forms the same Delta as fa_bwd_delta (bit for bit,
+    with and without an LSE gradient) and the same dq as fa_bwd_dq reading it."""
+    torch = need_gpu()
+    dtype, B, H, M, N, D, causal, with_dlse = case
+    wl = AttnWorkload("dq_delta", dtype, B, H, M, N, D, causal, seed=9 + M)
+    log(f"dq+delta vs steps {case}")
+    t = attn_inputs(wl)
+    q, k, v, do = (dev(t[n]) for n in ("q", "k", "v", "do"))
+    dlse = dev(draw(wl.seed + 1, [("dlse", (B, H, M), 1.0, F32)])["dlse"]) if with_dlse else None
+    o, lse = filled((B, H, M, D), dtype), empty_f32((B, H, M))
+    lib.fa_fwd(dtype, q, k, v, o, lse, B, H, M, N, D, causal, wl.sm_scale)
+    d1, d2 = guarded_f32((B, H, M)), guarded_f32((B, H, M))
+    q1, q2 = guarded((B, H, M, D), dtype), guarded((B, H, M, D), dtype)
+    lib.fa_bwd_delta(dtype, o, do, dlse, d1, B, H, M, D)
+    lib.fa_bwd_dq(dtype, q, k, v, do, lse, d1, q1, B, H, M, N, D, causal, wl.sm_scale)
+    lib.fa_bwd_dq_delta(dtype, q, k, v, o, do, lse, dlse, d2, q2, B, H, M, N, D, causal, wl.sm_scale)
+    torch.cuda.synchronize()
+    check_guards()
+    assert np.array_equal(host(d1), host(d2)), "delta"
+    assert np.array_equal(host(q1), host(q2)), "dq"
+
+
 def test_deterministic():
     wl = AttnWorkload("det", F16, 1, 4, 256, 256, 64, False, seed=6)
     t = attn_inputs(wl)
