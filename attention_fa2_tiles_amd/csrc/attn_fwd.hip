@@ -28,6 +28,9 @@
 namespace fa {
 namespace {
 
+template <int V>
+using ic = std::integral_constant<int, V>;
+
 constexpr int kBN = 64;           // keys per K/V block
 constexpr float kRescaleSlack = 8.0f;  // log2 units: P may reach 2^8 before a rescale
 constexpr int kLdsBytes = 160 * 1024;
@@ -519,25 +522,33 @@ void attn_fwd_kernel(const FwdParams p) {
 // has four stages: block j (V read), j + 1 (K read), j + 2 (landed) and j + 3
 // (loading).  The loop is unrolled by the four stages so every LDS address is
 // a per-lane register plus an immediate.
+//
+// Piecewise variant (D = 64): each stage also holds a K2 tile; a block is
+// loaded with the K tiles its workgroup needs, and a wave forms the scores
+// of a block wholly on one side of the distance rule from that side's
+// operands, or, on a block that straddles it, takes the (q1, k1) scores and
+// replaces the far pairs by (q2, k2) scores formed after them.
 // ---------------------------------------------------------------------------
 constexpr int kPipeNS = 4;
 constexpr int kPipeWaves = 8;
 
-template <typename T, int D>
+template <typename T, int D, int VAR>
 struct alignas(256) PipeSmem {
   using Tile = DTile<T, kBN, D, kPipeWaves>;
-  T k[kPipeNS][Tile::ELEMS];
+  static constexpr int NK = (VAR == PW) ? 2 : 1;
+  T k[NK][kPipeNS][Tile::ELEMS];  // K (piecewise: K1, then K2)
   T v[kPipeNS][Tile::ELEMS];
 };
 
-template <typename T, int D, bool CAUSAL, bool RAGGED>
+template <typename T, int D, int VAR, bool CAUSAL, bool RAGGED>
 __global__ __launch_bounds__(64 * kPipeWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attn_fwd_pipe_kernel(const FwdParams p) {
   constexpr int kWaves = kPipeWaves;
   constexpr int kBM = 32 * kWaves;
   constexpr int NS = kPipeNS;
+  constexpr bool kPw = VAR == PW;
   using V8 = typename Vec8<T>::type;
-  using Sm = PipeSmem<T, D>;
+  using Sm = PipeSmem<T, D, VAR>;
   using Tile = typename Sm::Tile;
   using Dma = DmaTile<T, kBN, D, kWaves>;
   constexpr int KK = D / 16;
@@ -552,7 +563,9 @@ void attn_fwd_pipe_kernel(const FwdParams p) {
   constexpr int kTileBytes = Tile::ELEMS * 2;
   static_assert(sizeof(Sm) <= kLdsBytes, "LDS budget");
   static_assert(NSC % NR == 0 && NSC % NPV == 0 && MPP % 2 == 0, "interleave shape");
-  static_assert((NS - 1) * kTileBytes + (ST - 1) * 32 * D * 2 <= 65535, "K read immediates");
+  constexpr int kK2Bytes = NS * kTileBytes;  // K2 tiles follow the K tiles
+  static_assert((kPw ? kK2Bytes : 0) + (NS - 1) * kTileBytes + (ST - 1) * 32 * D * 2 <= 65535,
+                "K read immediates");
   static_assert((NS - 1) * kTileBytes + (PT - 1) * 16 * D * 2 <= 65535, "V read immediates");
 
   __shared__ Sm smem;
@@ -594,12 +607,17 @@ void attn_fwd_pipe_kernel(const FwdParams p) {
   };
 
   // (lanes past the last query row read that row; their results are not stored)
-  V8 qf[KK];
+  V8 qf[KK], q2f[kPw ? KK : 1];
   if (wave_valid) {
-    const T* qrow = (const T*)p.q + qbase + (int64_t)(RAGGED ? min(qi, p.M - 1) : qi) * D + 8 * h;
+    const int64_t qoff = qbase + (int64_t)(RAGGED ? min(qi, p.M - 1) : qi) * D + 8 * h;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const V8*>(qrow + 16 * kk);
+    for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const V8*>((const T*)p.q + qoff + 16 * kk);
+    if constexpr (kPw) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) q2f[kk] = *reinterpret_cast<const V8*>((const T*)p.q2 + qoff + 16 * kk);
+    }
   }
+  const T* gk2 = kPw ? (const T*)p.k2 + kbase : gk;
 
   f32x16 acc[DT];
 #pragma unroll
@@ -628,32 +646,63 @@ void attn_fwd_pipe_kernel(const FwdParams p) {
     }
   }
 
-  // (CHK: the tile may lack rows: only in the prologue, since in the loop
-  // every tile lies inside the keys)
-  auto issue = [&](int jb, auto chk) {
+  // Piecewise: is every pair of rows [r_lo, r_hi] x keys [t0, t0 + 63] near
+  // (|dist| <= w), or every pair far?
+  auto pw_class = [&](int r_lo, int r_hi, int t0, bool& all_near, bool& all_far) {
+    const int dmax = r_hi + pshift - t0;
+    const int dmin = r_lo + pshift - (t0 + kBN - 1);
+    all_near = (dmax <= p.w) && (dmin >= -p.w);
+    all_far = (p.w < 0) || (dmin > p.w) || (dmax < -p.w);
+  };
+
+  // Issue the direct loads of block jb; returns this wave's number of load
+  // instructions.  (CHK: the tile may lack rows: only in the prologue, since
+  // in the loop every tile lies inside the keys)
+  auto issue = [&](int jb, auto chk) -> int {
     const int st = jb % NS;
     const int kb = key_block(jb);
     const int t0 = tile_start(kb);
     const int64_t off = (int64_t)t0 * D;
+    bool need_k = true, need_k2 = false;
+    if constexpr (kPw) {
+      bool an, af;
+      pw_class(m0, wg_last_row, t0, an, af);
+      need_k = !af;
+      need_k2 = !an;
+    }
     if constexpr (RAGGED && decltype(chk)::value) {
       const int nr = p.N - t0;  // rows of this tile that exist
-      dma.load_rows(gk + off, smem.k[st], wave, lane, nr);
+      if (need_k) dma.load_rows(gk + off, smem.k[0][st], wave, lane, nr);
+      if (kPw && need_k2) dma.load_rows(gk2 + off, smem.k[kPw ? 1 : 0][st], wave, lane, nr);
       dma.load_rows(gv + off, smem.v[st], wave, lane, nr);
     } else {
-      dma.load(gk + off, smem.k[st], wave);
+      if (need_k) dma.load(gk + off, smem.k[0][st], wave);
+      if (kPw && need_k2) dma.load(gk2 + off, smem.k[kPw ? 1 : 0][st], wave);
       dma.load(gv + off, smem.v[st], wave);
     }
+    return Dma::PER_WAVE * (1 + (int)need_k + (int)(kPw && need_k2));
   };
-  constexpr int kLoads = 2 * Dma::PER_WAVE;
+  // Wait until every load but the newest n (one block's) has landed; loads
+  // complete in issue order.  A piecewise block may skip one K tile.
+  auto wait_all_but = [&](int n) {
+    if constexpr (kPw)
+      wait_vmcnt_any<3 * Dma::PER_WAVE, 2 * Dma::PER_WAVE>(n);
+    else
+      wait_vmcnt<2 * Dma::PER_WAVE>();
+  };
   auto active = [&](int jb) { return wave_valid && (!CAUSAL || jb * kBN <= row0 + 31 + pshift); };
   auto needs_mask = [&](int jb) { return CAUSAL && (jb * kBN + kBN - 1 > row0 + pshift); };
 
-  // K row read i of stage S (i = kk * ST + st), as inline asm.
-  auto kread = [&](auto stage_c, auto i_c, u32x4& r) {
+  // K row read i of stage S (i = kk * ST + st) from tile set KS (0: K,
+  // 1: K2), as inline asm.
+  auto kread = [&](auto stage_c, auto i_c, u32x4& r, auto set_c) {
     constexpr int S = decltype(stage_c)::value;
     constexpr int I = decltype(i_c)::value;
+    constexpr int KS = decltype(set_c)::value;
     const uint32_t a = kaddr[I / ST];
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(S * kTileBytes + (I % ST) * 32 * D * 2));
+    asm volatile("ds_read_b128 %0, %1 offset:%2"
+                 : "=v"(r)
+                 : "v"(a), "i"(KS * kK2Bytes + S * kTileBytes + (I % ST) * 32 * D * 2));
   };
   // Wait for K read i.  Reads are kept kWin deep: 0 .. kWin-1 are issued
   // first and read i + kWin right after product i (reads complete in issue
@@ -665,21 +714,62 @@ void attn_fwd_pipe_kernel(const FwdParams p) {
     asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(r) : "n"(CNT));
   };
 
-  // Score products of the block in stage S into sn; after product i, run
-  // between(i) (exponent work of the previous block, or nothing).
-  auto scores = [&](auto stage_c, f32x16 (&sn)[ST], auto&& between) {
+  // Score products of tile set KS (query operands qs) of the block in
+  // stage S into sn; after product i, run between(i) (exponent work of the
+  // previous block, or nothing).
+  auto scores_set = [&](auto stage_c, auto set_c, const V8 (&qs)[KK], f32x16 (&sn)[ST], auto&& between) {
     u32x4 kr[NR];
-    static_for<kWin>([&](auto ic) { kread(stage_c, ic, kr[decltype(ic)::value]); });
+    static_for<kWin>([&](auto ic) { kread(stage_c, ic, kr[decltype(ic)::value], set_c); });
 #pragma unroll
     for (int st = 0; st < ST; ++st) sn[st] = zero16();
     static_for<NR>([&](auto ic) {
       constexpr int I = decltype(ic)::value;
       kwait(ic, kr[I]);
-      sn[I % ST] = mfma32x32x16(__builtin_bit_cast(V8, kr[I]), qf[I / ST], sn[I % ST]);
-      if constexpr (I + kWin < NR) kread(stage_c, std::integral_constant<int, I + kWin>{}, kr[I + kWin]);
+      sn[I % ST] = mfma32x32x16(__builtin_bit_cast(V8, kr[I]), qs[I / ST], sn[I % ST]);
+      if constexpr (I + kWin < NR) kread(stage_c, std::integral_constant<int, I + kWin>{}, kr[I + kWin], set_c);
       between(ic);
       __builtin_amdgcn_sched_barrier(0);
     });
+  };
+  // Scores of block jb (in stage S) into sn.  Piecewise: from the side of
+  // the rule the wave's pairs lie on; a straddling block takes the (q1, k1)
+  // scores, then forms the (q2, k2) ones one 32-key tile at a time and
+  // replaces the far pairs (key t0 + 32 st + perm_row(r, h) is at distance
+  // c1 - perm_row(r, 0) from this lane's query).
+  auto scores = [&](auto stage_c, int jb, f32x16 (&sn)[ST], auto&& between) {
+    if constexpr (!kPw) {
+      scores_set(stage_c, ic<0>{}, qf, sn, between);
+    } else {
+      const int t0 = tile_start(key_block(jb));
+      bool an, af;
+      pw_class(row0, row0 + 31, t0, an, af);
+      if (af) {
+        scores_set(stage_c, ic<1>{}, q2f, sn, between);
+      } else {
+        scores_set(stage_c, ic<0>{}, qf, sn, between);
+        if (!an) {
+          static_for<ST>([&](auto stc) {
+            constexpr int st = decltype(stc)::value;
+            u32x4 kr[KK];
+            static_for<KK>([&](auto kc) {
+              kread(stage_c, ic<decltype(kc)::value * ST + st>{}, kr[decltype(kc)::value], ic<1>{});
+            });
+            f32x16 s2 = zero16();
+            static_for<KK>([&](auto kc) {
+              constexpr int kk = decltype(kc)::value;
+              asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(kr[kk]) : "n"(KK - 1 - kk));
+              s2 = mfma32x32x16(__builtin_bit_cast(V8, kr[kk]), q2f[kk], s2);
+            });
+            const int c1 = qi + pshift - t0 - 32 * st - 8 * h;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int dist = c1 - perm_row(r, 0);
+              if (!(dist <= p.w && dist >= -p.w)) sn[st][r] = s2[r];
+            }
+          });
+        }
+      }
+    }
   };
 
   // Mask of the raw scores of key block kb (tile from key t0): keys beyond
@@ -755,11 +845,12 @@ void attn_fwd_pipe_kernel(const FwdParams p) {
   // Prologue: the query operands have landed; blocks 0, 1, 2 are issued and
   // blocks 0 and 1 have landed; the scores of block 0 and its max are taken.
   wait_vmcnt0();
+  int n_new = 0;  // load instructions of the newest block issued
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
-    if (j < nblk) issue(j, std::true_type{});
+    if (j < nblk) n_new = issue(j, std::true_type{});
   if (nblk > NS - 2)
-    wait_vmcnt<kLoads>();
+    wait_all_but(n_new);
   else
     wait_vmcnt0();
   lds_barrier();
@@ -771,7 +862,7 @@ void attn_fwd_pipe_kernel(const FwdParams p) {
     sb[st] = zero16();
   }
   if (nblk > 0 && active(0)) {
-    scores(std::integral_constant<int, 0>{}, sa, [](auto) {});
+    scores(std::integral_constant<int, 0>{}, 0, sa, [](auto) {});
     if (tail_first || needs_mask(0)) apply_mask(sa, key_block(0));
     float mx = kNegInf;
 #pragma unroll
@@ -786,14 +877,14 @@ void attn_fwd_pipe_kernel(const FwdParams p) {
   auto step = [&](auto stage_c, int jb, f32x16 (&sc)[ST], f32x16 (&sn)[ST]) {
     constexpr int S = decltype(stage_c)::value;
     constexpr int SN = (S + 1) % NS;
-    if (jb + NS - 1 < nblk) issue(jb + NS - 1, std::false_type{});
+    if (jb + NS - 1 < nblk) n_new = issue(jb + NS - 1, std::false_type{});
     const bool a_c = active(jb);
     const bool a_n = jb + 1 < nblk && active(jb + 1);
     const float neg_m = (m_i == kNegInf) ? 0.f : -m_i;
     if (a_c) {
       // scores of block jb + 1 || exponents of block jb
       if (a_n)
-        scores(std::integral_constant<int, SN>{}, sn, [&](auto ic) { exp_step(sc, neg_m, ic); });
+        scores(std::integral_constant<int, SN>{}, jb + 1, sn, [&](auto ic) { exp_step(sc, neg_m, ic); });
       else
         static_for<NR>([&](auto ic) { exp_step(sc, neg_m, ic); });
       V8 pb[PT];
@@ -813,7 +904,7 @@ void attn_fwd_pipe_kernel(const FwdParams p) {
       if (a_n) rescale(halves_max(fmaxf(mx[0], mx[1])) * p.scale2);
     }
     if (jb + NS - 1 < nblk)
-      wait_vmcnt<kLoads>();
+      wait_all_but(n_new);
     else
       wait_vmcnt0();
     lds_barrier();
@@ -862,16 +953,16 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
   p.w = a.w;
   dim3 grid(p.nmb * p.BH), block(FwdShape<VAR, D>::NT);
   const bool ragged = a.M % 64 != 0 || a.N % 64 != 0;
-  if constexpr (VAR == PLAIN && (D == 64 || D == 128)) {
-    static_assert(FwdShape<PLAIN, D>::NT == 64 * kPipeWaves, "same launch shape");
+  if constexpr ((VAR == PLAIN && (D == 64 || D == 128)) || (VAR == PW && D == 64)) {
+    static_assert(FwdShape<VAR, D>::NT == 64 * kPipeWaves, "same launch shape");
     if (a.causal && ragged)
-      hipLaunchKernelGGL((attn_fwd_pipe_kernel<T, D, true, true>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((attn_fwd_pipe_kernel<T, D, VAR, true, true>), grid, block, 0, s, p);
     else if (a.causal)
-      hipLaunchKernelGGL((attn_fwd_pipe_kernel<T, D, true, false>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((attn_fwd_pipe_kernel<T, D, VAR, true, false>), grid, block, 0, s, p);
     else if (ragged)
-      hipLaunchKernelGGL((attn_fwd_pipe_kernel<T, D, false, true>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((attn_fwd_pipe_kernel<T, D, VAR, false, true>), grid, block, 0, s, p);
     else
-      hipLaunchKernelGGL((attn_fwd_pipe_kernel<T, D, false, false>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((attn_fwd_pipe_kernel<T, D, VAR, false, false>), grid, block, 0, s, p);
   } else {
     if (a.causal && ragged)
       hipLaunchKernelGGL((attn_fwd_kernel<T, D, VAR, true, true>), grid, block, 0, s, p);

@@ -144,6 +144,8 @@ PW_SMALL = [
     (F16, 1, 2, 640, 704, 64, True, 150),      # several workgroups, M != N
     (BF16, 2, 2, 512, 448, 64, False, 90),     # M > N, both signs of dist
     (F16, 1, 2, 333, 517, 64, True, 77),       # ragged, several workgroups
+    (F16, 1, 2, 190, 333, 64, False, 70),      # ragged, partial key block first
+    (BF16, 1, 2, 300, 200, 64, True, 40),      # M > N: rows with no visible key
     (F32, 1, 2, 128, 128, 64, True, 20),
     (F32, 1, 2, 128, 192, 128, False, 50),
     (F16, 1, 2, 200, 170, 64, True, 50),       # ragged lengths
