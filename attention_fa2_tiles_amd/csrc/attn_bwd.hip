@@ -118,6 +118,9 @@ struct alignas(256) DkdvSmem {
   using VTile = DTile<T, 32, D, 1, false>;  // natural key order
   DkdvStage<T, D, VAR> st[Sh::NS];
   T v[Sh::WAVES][VTile::ELEMS];
+  // piecewise: each wave's 32 rows of K2 (the far side's B operand), read
+  // from LDS like V to leave their registers to the accumulators
+  T k2[(VAR == PW) ? Sh::WAVES * VTile::ELEMS : 1];
 };
 
 template <int D, int VAR>
@@ -170,22 +173,24 @@ void attn_dkdv_kernel(const BwdParams p) {
   const int64_t kbase = (int64_t)bh * p.N * D;
   const int64_t lbase = (int64_t)bh * p.M;
 
-  // Resident operands: this wave's 32 rows of V in LDS, K (K1, K2) columns
-  // in registers (lane li feeds key kj).  Keys past the last one read the
-  // last key; their columns are not stored.
-  V8 kf[KK], k2f[kPw ? KK : 1];
+  // Resident operands: this wave's 32 rows of V (piecewise: and of K2) in
+  // LDS, K (K1) columns in registers (lane li feeds key kj).  Keys past the
+  // last one read the last key; their columns are not stored.
+  V8 kf[KK];
   if (wave_valid) {
     const T* vsrc = (const T*)p.v + kbase + (int64_t)kw0 * D;
-    if (!RAGGED || p.N - kw0 >= 32)
+    const T* k2src = kPw ? (const T*)p.k2 + kbase + (int64_t)kw0 * D : vsrc;
+    T* k2dst = smem.k2 + (kPw ? wave * VTile::ELEMS : 0);
+    if (!RAGGED || p.N - kw0 >= 32) {
       VTile::load(smem.v[wave], vsrc, 0, lane);
-    else
+      if constexpr (kPw) VTile::load(k2dst, k2src, 0, lane);
+    } else {
       VTile::load_lim(smem.v[wave], vsrc, 0, lane, p.N - kw0);
+      if constexpr (kPw) VTile::load_lim(k2dst, k2src, 0, lane, p.N - kw0);
+    }
     const int64_t off = kbase + (int64_t)(RAGGED ? min(kj, p.N - 1) : kj) * D + 8 * h;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      kf[kk] = *reinterpret_cast<const V8*>((const T*)p.k + off + 16 * kk);
-      if constexpr (kPw) k2f[kk] = *reinterpret_cast<const V8*>((const T*)p.k2 + off + 16 * kk);
-    }
+    for (int kk = 0; kk < KK; ++kk) kf[kk] = *reinterpret_cast<const V8*>((const T*)p.k + off + 16 * kk);
   }
 
   f32x16 dvt[DT], dkt[DT], dk2t[kPw ? DT : 1];
@@ -304,6 +309,7 @@ void attn_dkdv_kernel(const BwdParams p) {
     return *reinterpret_cast<const V8*>(sbase + off + rofs[kk]);
   };
   const int voff = (int)(reinterpret_cast<const char*>(smem.v[wave]) - sbase);
+  const int k2off = (int)(reinterpret_cast<const char*>(smem.k2 + (kPw ? wave * VTile::ELEMS : 0)) - sbase);
   const float neg_inv_scale = -1.f / p.sm_scale;
 
   // One query block for this wave from stage S.  SEL picks the score
@@ -321,8 +327,14 @@ void attn_dkdv_kernel(const BwdParams p) {
     constexpr int kDo = kSt + (int)__builtin_offsetof(St, dout);
     constexpr int kQs = kSt + (int)__builtin_offsetof(St, q) + SEL * Tile::ELEMS * 2;
     const St& cur = smem.st[S];
-    auto& ks = pick<SEL>(kf, k2f);
     auto& dks = pick<SEL>(dkt, dk2t);
+    // B operand of the score product: K from registers, K2 from LDS
+    auto kop = [&](int kk) -> V8 {
+      if constexpr (SEL == 0)
+        return kf[kk];
+      else
+        return rd8(k2off, kk);
+    };
     f32x16 s[ST], dp[ST];
 #pragma unroll
     for (int st = 0; st < ST; ++st) {
@@ -355,7 +367,7 @@ void attn_dkdv_kernel(const BwdParams p) {
       const int so = st * 32 * D * 2;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        s[st] = mfma32x32x16(rd8(kQs + so, kk), ks[kk], s[st]);
+        s[st] = mfma32x32x16(rd8(kQs + so, kk), kop(kk), s[st]);
         dp[st] = mfma32x32x16(rd8(kDo + so, kk), rd8(voff, kk), dp[st]);
       }
     }
