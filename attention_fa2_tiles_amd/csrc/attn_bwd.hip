@@ -560,6 +560,7 @@ void attn_dq_kernel(const BwdParams p) {
   // Query-side operands stay in registers for the whole pass.
   // (lanes past the last query row read that row; their results are not stored)
   V8 qf[KK], q2f[kPw ? KK : 1], dof[KK];
+  V8 of[KK];  // this row's O chunks, when the pass forms Delta
   float lse2 = __builtin_huge_valf(), dl = 0.f;
   const int qr = RAGGED ? min(qi, p.M - 1) : qi;
   if (wave_valid) {
@@ -572,26 +573,8 @@ void attn_dq_kernel(const BwdParams p) {
     }
     lse2 = lse_to_log2(p.lse[(int64_t)bh * p.M + qr]);
     if (p.delta_out) {
-      // Delta_i = sum_d O_id dO_id - dLSE_i, in the delta kernel's order:
-      // fma chains over 16-byte chunks, then the chunk sums pairwise with
-      // stride half the chunk count (chunk 2 kk + h sits in slot kk of half h)
-      const T* orow = (const T*)p.o + off;
-      float cs[KK];
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const V8 ov = *reinterpret_cast<const V8*>(orow + 16 * kk);
-        cs[kk] = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) cs[kk] = fmaf((float)ov[e], (float)dof[kk][e], cs[kk]);
-      }
-#pragma unroll
-      for (int half = KK / 2; half >= 1; half /= 2) {
-#pragma unroll
-        for (int kk = 0; kk < half; ++kk) cs[kk] += cs[kk + half];
-      }
-      dl = halves_sum(cs[0]);
-      if (p.dlse) dl -= p.dlse[(int64_t)bh * p.M + qr];
-      if (h == 0 && (!RAGGED || qi < p.M)) p.delta_out[(int64_t)bh * p.M + qi] = dl;
+      for (int kk = 0; kk < KK; ++kk) of[kk] = *reinterpret_cast<const V8*>((const T*)p.o + off + 16 * kk);
     } else {
       dl = p.delta[(int64_t)bh * p.M + qr];
     }
@@ -646,9 +629,9 @@ void attn_dq_kernel(const BwdParams p) {
       wait_vmcnt<2 * Dma::PER_WAVE>();
   };
 
-  // Prologue: the query operands have landed; blocks 0 .. NS-2 are in
-  // flight and block 0 has landed.
-  wait_vmcnt0();
+  // Prologue: blocks 0 .. NS-2 are issued right behind the query operands
+  // (all but the newest block's loads, the query operands included, have
+  // landed after the wait).
   int n_new = 0;
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
@@ -658,6 +641,27 @@ void attn_dq_kernel(const BwdParams p) {
   else
     wait_vmcnt0();
   lds_barrier();
+
+  if (wave_valid && p.delta_out) {
+    // Delta_i = sum_d O_id dO_id - dLSE_i, in the delta kernel's order: fma
+    // chains over 16-byte chunks, then the chunk sums pairwise with stride
+    // half the chunk count (chunk 2 kk + h sits in slot kk of half h)
+    float cs[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      cs[kk] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cs[kk] = fmaf((float)of[kk][e], (float)dof[kk][e], cs[kk]);
+    }
+#pragma unroll
+    for (int half = KK / 2; half >= 1; half /= 2) {
+#pragma unroll
+      for (int kk = 0; kk < half; ++kk) cs[kk] += cs[kk + half];
+    }
+    dl = halves_sum(cs[0]);
+    if (p.dlse) dl -= p.dlse[(int64_t)bh * p.M + qr];
+    if (h == 0 && (!RAGGED || qi < p.M)) p.delta_out[(int64_t)bh * p.M + qi] = dl;
+  }
 
   uint32_t rofs[KK];
 #pragma unroll

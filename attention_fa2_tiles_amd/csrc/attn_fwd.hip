@@ -245,9 +245,8 @@ void attn_fwd_kernel(const FwdParams p) {
       wait_vmcnt<kTileLoads * (St::NK + St::NV)>();
   };
 
-  // Prologue: the query operands have landed; blocks 0 .. NS-2 are in
-  // flight and block 0 has landed.
-  wait_vmcnt0();
+  // Prologue: blocks 0 .. NS-2 are issued right behind the query operands;
+  // block 0 (and the query operands) have landed after the wait.
   int n_new = 0;
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
@@ -842,9 +841,9 @@ void attn_fwd_pipe_kernel(const FwdParams p) {
     });
   };
 
-  // Prologue: the query operands have landed; blocks 0, 1, 2 are issued and
-  // blocks 0 and 1 have landed; the scores of block 0 and its max are taken.
-  wait_vmcnt0();
+  // Prologue: blocks 0, 1, 2 are issued right behind the query operands;
+  // blocks 0 and 1 (and the query operands) have landed; the scores of
+  // block 0 and its max are taken.
   int n_new = 0;  // load instructions of the newest block issued
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
