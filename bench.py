@@ -43,7 +43,13 @@ def progress(msg):
 
 class Timer:
     """Average duration of repeated launches, from HIP events recorded on the
-    stream the library launches on (torch's current stream)."""
+    stream the library launches on (torch's current stream).  Before timing,
+    the launch is repeated for WARM_S seconds: after the host-side input
+    set-up of a workload the GPU's clocks have dropped, and they take about
+    0.2 s of work to ramp up again (a loop of a hundred 100 us launches timed
+    right away reads 10-20% slow)."""
+
+    WARM_S = 0.3
 
     def __init__(self, torch):
         self.torch = torch
@@ -53,6 +59,11 @@ class Timer:
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < self.WARM_S:
+            for _ in range(10):
+                fn()
+            torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
         start.record()
