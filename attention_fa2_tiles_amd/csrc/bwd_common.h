@@ -1,6 +1,6 @@
 // Pieces of the attention backward kernels: launch parameters, the
-// piecewise distance rule, and the LDS addressing and accumulation helpers
-// for transposing operand reads.
+// piecewise distance rule and pair masks, and the LDS addressing of the
+// transposing operand reads.
 // Everything here has internal linkage in each translation unit.
 #pragma once
 
@@ -139,63 +139,6 @@ __device__ __forceinline__ void tr_issue(TrOps<T, NOPS>& x, const TrAddr<D>& a, 
     static_assert(tr_fits<D, NOPS, OFF - 32768>(), "tile beyond the 96 KiB reach of the hi addresses");
     const uint32_t hi[2] = {a.lo[dt][0] + 32768u, a.lo[dt][1] + 32768u};
     x.template issue_imm<D, OFF - 32768>(hi);
-  }
-}
-
-// acc[dt] += X^t B over the d-tiles of the tile X at byte offset OFF of the
-// LDS allocation (transposing reads; the reads of d-tile dt + 1 are in
-// flight during the products of d-tile dt).
-template <typename T, int D, int NOPS, int OFF>
-__device__ __forceinline__ void accum_tr(f32x16 (&acc)[D / 32], const TrAddr<D>& a,
-                                         const typename Vec8<T>::type (&b)[NOPS]) {
-  constexpr int DT = D / 32;
-  TrOps<T, NOPS> xa, xb;
-  tr_issue<T, D, NOPS, OFF>(xa, a, 0);
-  xa.wait();
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    TrOps<T, NOPS>& cx = (dt & 1) ? xb : xa;
-    TrOps<T, NOPS>& nx = (dt & 1) ? xa : xb;
-    if (dt + 1 < DT) tr_issue<T, D, NOPS, OFF>(nx, a, dt + 1);
-#pragma unroll
-    for (int t = 0; t < NOPS; ++t) acc[dt] = mfma32x32x16(cx.op[t], b[t], acc[dt]);
-    __builtin_amdgcn_sched_barrier(0);
-    if (dt + 1 < DT) nx.wait();
-  }
-}
-
-// Two such accumulations over the same d-tiles, interleaved (four products
-// per batch of reads): accA += XA^t bA, accB += XB^t bB.
-template <typename T, int D, int NOPS, int OFFA, int OFFB>
-__device__ __forceinline__ void accum_tr2(f32x16 (&accA)[D / 32], f32x16 (&accB)[D / 32], const TrAddr<D>& a,
-                                          const typename Vec8<T>::type (&bA)[NOPS],
-                                          const typename Vec8<T>::type (&bB)[NOPS]) {
-  constexpr int DT = D / 32;
-  TrOps<T, NOPS> xa, xb, ya, yb;
-  tr_issue<T, D, NOPS, OFFA>(xa, a, 0);
-  tr_issue<T, D, NOPS, OFFB>(ya, a, 0);
-  xa.wait();
-  ya.wait();
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    TrOps<T, NOPS>& cx = (dt & 1) ? xb : xa;
-    TrOps<T, NOPS>& nx = (dt & 1) ? xa : xb;
-    TrOps<T, NOPS>& cy = (dt & 1) ? yb : ya;
-    TrOps<T, NOPS>& ny = (dt & 1) ? ya : yb;
-    if (dt + 1 < DT) {
-      tr_issue<T, D, NOPS, OFFA>(nx, a, dt + 1);
-      tr_issue<T, D, NOPS, OFFB>(ny, a, dt + 1);
-    }
-#pragma unroll
-    for (int t = 0; t < NOPS; ++t) {
-      accA[dt] = mfma32x32x16(cx.op[t], bA[t], accA[dt]);
-      accB[dt] = mfma32x32x16(cy.op[t], bB[t], accB[dt]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (dt + 1 < DT) {
-      nx.wait();
-      ny.wait();
-    }
   }
 }
 
