@@ -130,7 +130,7 @@ int fa_bwd(int dtype, const void* q, const void* k, const void* v, const void* o
            void* workspace, size_t workspace_bytes,
            int B, int H, int M, int N, int D, int causal, float sm_scale, void* stream);
 
-/* The three steps of fa_bwd, exposed separately so each can be timed. */
+/* The steps of fa_bwd, exposed separately so each can be timed. */
 /* delta [B,H,M] fp32 <- rowsum(o * dout) - dlse (dlse may be NULL)
  * [tutorial: _attn_bwd_preprocess] */
 int fa_bwd_delta(int dtype, const void* o, const void* dout, const float* dlse, float* delta,
