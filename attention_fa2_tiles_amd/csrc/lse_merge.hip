@@ -35,6 +35,10 @@ struct alignas(16) Ch8 {
   T e[8];
 };
 
+// 8 elements; stores as 16-byte vectors with the non-temporal hint (the
+// outputs are written once; measured 5% faster forward, 14% faster
+// backward).  Loads keep the default policy: the backward reads each input
+// chunk twice, and with the hint on the loads both passes were 15% slower.
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float (&f)[8]) {
   const Ch8<T> c = *reinterpret_cast<const Ch8<T>*>(p);
@@ -44,10 +48,14 @@ __device__ __forceinline__ void load8(const T* p, float (&f)[8]) {
 
 template <typename T>
 __device__ __forceinline__ void store8(T* p, const float (&f)[8]) {
+  constexpr int NV = (int)sizeof(Ch8<T>) / 16;
   Ch8<T> c;
 #pragma unroll
   for (int i = 0; i < 8; ++i) c.e[i] = (T)f[i];
-  *reinterpret_cast<Ch8<T>*>(p) = c;
+  u32x4 raw[NV];
+  __builtin_memcpy(raw, &c, sizeof(c));
+#pragma unroll
+  for (int v = 0; v < NV; ++v) __builtin_nontemporal_store(raw[v], reinterpret_cast<u32x4*>(p) + v);
 }
 
 // Row maximum and normaliser of the S logits of one row (logits at

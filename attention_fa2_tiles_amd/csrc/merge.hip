@@ -20,8 +20,8 @@
 // wavefront, then the team's partial sums in LDS in wavefront order) and the
 // output pass, so every input byte is read from HBM once; the row loads and
 // stores carry the non-temporal hint (measured: 8% faster forward, 6%
-// faster backward at 32768 x 4096 bf16; the same hint on the N-way merge's
-// 256-byte rows made it 15% slower, so it is used here only).  The
+// faster backward at 32768 x 4096 bf16; the N-way merge, whose backward
+// reads its inputs twice, takes it on its stores only).  The
 // pseudo-query q is loaded once per thread.  gq is reduced deterministically: each thread
 // accumulates its columns over the rows of its workgroup, the workgroup
 // writes one partial row, and a second kernel adds the partial rows in index
