@@ -18,10 +18,12 @@
 // the current row is reduced and written.  The row stays in registers
 // between the reductions (x.x, x.q, gy.(y0-x): butterflies across the
 // wavefront, then the team's partial sums in LDS in wavefront order) and the
-// output pass, so every input byte is read from HBM once; the row loads and
-// stores carry the non-temporal hint (measured: 8% faster forward, 6%
-// faster backward at 32768 x 4096 bf16; the N-way merge, whose backward
-// reads its inputs twice, takes it on its stores only).  The
+// output pass, so every input byte is read from HBM once.  Cache policy, as
+// measured at 32768 x 4096 bf16: the forward's row loads carry the
+// non-temporal hint and its stores do not (153 -> 125 us; with the hint on
+// the stores as well, 140 us), the backward's loads and stores both carry
+// it (266 -> 251 us; either alone, 264 us).  The N-way merge, whose
+// backward reads its inputs twice, takes it on its stores only.  The
 // pseudo-query q is loaded once per thread.  gq is reduced deterministically: each thread
 // accumulates its columns over the rows of its workgroup, the workgroup
 // writes one partial row, and a second kernel adds the partial rows in index
@@ -200,7 +202,7 @@ __global__ __launch_bounds__(kTeamWG) void merge_fwd_kernel(MergeArgs a) {
       chunk_f32<T>(yc[j], yf);
 #pragma unroll
       for (int i = 0; i < E; ++i) of[i] = mx.alpha * yf[i] + mx.beta * xf[i];
-      __builtin_nontemporal_store(f32_chunk<T>(of), &oc[tm.t + j * 64 * WPR]);
+      oc[tm.t + j * 64 * WPR] = f32_chunk<T>(of);
     }
     if (tm.t == 0) a.lse[row] = mx.m + logf(mx.Z);
   }
