@@ -21,8 +21,9 @@
 // output pass, so every input byte is read from HBM once.  Cache policy, as
 // measured at 32768 x 4096 bf16: the forward's row loads carry the
 // non-temporal hint and its stores do not (153 -> 125 us; with the hint on
-// the stores as well, 140 us), the backward's loads and stores both carry
-// it (266 -> 251 us; either alone, 264 us).  The N-way merge, whose
+// the stores as well, 140 us), the backward's loads and its gy0 stores
+// carry it and its gx stores do not (266 -> 232 us; loads only 264 us,
+// loads and both stores 251 us, gx instead of gy0 233 us).  The N-way merge, whose
 // backward reads its inputs twice, takes it on its stores only.  The
 // pseudo-query q is loaded once per thread.  gq is reduced deterministically: each thread
 // accumulates its columns over the rows of its workgroup, the workgroup
@@ -291,7 +292,7 @@ __global__ __launch_bounds__(kTeamWG) void merge_bwd_kernel(MergeArgs a) {
 #pragma unroll
         for (int i = 0; i < E; ++i) gx[i] += old[i];
       }
-      __builtin_nontemporal_store(f32_chunk<T>(gx), &gxc[tm.t + j * 64 * WPR]);
+      gxc[tm.t + j * 64 * WPR] = f32_chunk<T>(gx);
       __builtin_nontemporal_store(f32_chunk<T>(gy0), &gyc[tm.t + j * 64 * WPR]);
     }
     if (tm.t == 0) a.gl0[row] = mx.alpha * gl + ab * s;
