@@ -81,7 +81,7 @@ def _fwd_jvp(q, k, v, tq, tk, tv, causal, sm_scale):
     o, to = torch.empty_like(q), torch.empty_like(q)
     lse = torch.empty((B, H, M), dtype=torch.float32, device=q.device)
     tlse = torch.empty_like(lse)
-    lib.fa_fwd_jvp(_code(q), q, k, v, tq, tk, tv, o, lse, to, tlse, B, H, M, N, D, int(causal),
+    lib.fa_fwd_jvp_tlse(_code(q), q, k, v, tq, tk, tv, o, lse, to, tlse, B, H, M, N, D, int(causal),
                    _scale(sm_scale))
     return o, lse, to, tlse
 
@@ -124,8 +124,8 @@ class _Attention(torch.autograd.Function):
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         nb = lib.fa_bwd_workspace_size(B, H, M, N, D, _code(q))
         ws = torch.empty(nb, dtype=torch.uint8, device=q.device)
-        lib.fa_bwd(_code(q), q, k, v, o, do, lse, dlse, dq, dk, dv, ws, nb, B, H, M, N, D,
-                   int(ctx.causal), _scale(ctx.sm_scale))
+        lib.fa_bwd_dlse(_code(q), q, k, v, o, do, lse, dlse, dq, dk, dv, ws, nb, B, H, M, N, D,
+                        int(ctx.causal), _scale(ctx.sm_scale))
         return dq, dk, dv, None, None, None, None, None
 
     @staticmethod
@@ -181,8 +181,8 @@ class _Piecewise(torch.autograd.Function):
         g = [torch.empty_like(t) for t in (q1, k1, q2, k2, v)]
         nb = lib.pw_bwd_workspace_size(B, H, M, N, D, _code(q1))
         ws = torch.empty(nb, dtype=torch.uint8, device=q1.device)
-        lib.pw_bwd(_code(q1), q1, k1, q2, k2, v, o, do, lse, dlse, *g, ws, nb, B, H, M, N, D, int(ctx.causal),
-                   _scale(ctx.sm_scale), int(ctx.w))
+        lib.pw_bwd_dlse(_code(q1), q1, k1, q2, k2, v, o, do, lse, dlse, *g, ws, nb, B, H, M, N, D,
+                        int(ctx.causal), _scale(ctx.sm_scale), int(ctx.w))
         return (*g, None, None, None)
 
 

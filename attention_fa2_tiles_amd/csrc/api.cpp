@@ -16,7 +16,7 @@ using fa::MergeArgs;
 
 namespace {
 
-constexpr int kVersion = 100;
+constexpr int kVersion = 200;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -240,8 +240,16 @@ static int bwd_common(int dtype, int variant, const void* q, const void* k, cons
 }
 
 int fa_bwd(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,
-           const float* lse, const float* dlse, void* dq, void* dk, void* dv, void* workspace,
-           size_t workspace_bytes, int B, int H, int M, int N, int D, int causal, float sm_scale, void* stream) {
+           const float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int H,
+           int M, int N, int D, int causal, float sm_scale, void* stream) {
+  return bwd_common(dtype, fa::PLAIN, q, k, nullptr, nullptr, v, o, dout, lse, nullptr, dq, dk, nullptr, nullptr, dv,
+                    workspace, workspace_bytes, B, H, M, N, D, causal, sm_scale, 0, stream);
+}
+
+int fa_bwd_dlse(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, const float* dlse, void* dq, void* dk, void* dv, void* workspace,
+                size_t workspace_bytes, int B, int H, int M, int N, int D, int causal, float sm_scale,
+                void* stream) {
   return bwd_common(dtype, fa::PLAIN, q, k, nullptr, nullptr, v, o, dout, lse, dlse, dq, dk, nullptr, nullptr, dv,
                     workspace, workspace_bytes, B, H, M, N, D, causal, sm_scale, 0, stream);
 }
@@ -345,8 +353,14 @@ int fa_bwd_dq_delta(int dtype, const void* q, const void* k, const void* v, cons
 }
 
 int fa_fwd_jvp(int dtype, const void* q, const void* k, const void* v, const void* tq, const void* tk,
-               const void* tv, void* o, float* lse, void* to, float* tlse, int B, int H, int M, int N, int D,
-               int causal, float sm_scale, void* stream) {
+               const void* tv, void* o, float* lse, void* to, int B, int H, int M, int N, int D, int causal,
+               float sm_scale, void* stream) {
+  return fa_fwd_jvp_tlse(dtype, q, k, v, tq, tk, tv, o, lse, to, nullptr, B, H, M, N, D, causal, sm_scale, stream);
+}
+
+int fa_fwd_jvp_tlse(int dtype, const void* q, const void* k, const void* v, const void* tq, const void* tk,
+                    const void* tv, void* o, float* lse, void* to, float* tlse, int B, int H, int M, int N, int D,
+                    int causal, float sm_scale, void* stream) {
   FA_TRY(check_dtype(dtype));
   FA_TRY(check_tensors({q, k, v, tq, tk, tv, o, to}));
   FA_TRY(check_scalars({lse}));
@@ -413,9 +427,17 @@ size_t pw_bwd_workspace_size(int B, int H, int M, int N, int D, int dtype) {
 }
 
 int pw_bwd(int dtype, const void* q1, const void* k1, const void* q2, const void* k2, const void* v, const void* o,
-           const void* dout, const float* lse, const float* dlse, void* dq1, void* dk1, void* dq2, void* dk2,
-           void* dv, void* workspace, size_t workspace_bytes, int B, int H, int M, int N, int D, int causal,
-           float sm_scale, int w, void* stream) {
+           const void* dout, const float* lse, void* dq1, void* dk1, void* dq2, void* dk2, void* dv,
+           void* workspace, size_t workspace_bytes, int B, int H, int M, int N, int D, int causal, float sm_scale,
+           int w, void* stream) {
+  return bwd_common(dtype, fa::PW, q1, k1, q2, k2, v, o, dout, lse, nullptr, dq1, dk1, dq2, dk2, dv, workspace,
+                    workspace_bytes, B, H, M, N, D, causal, sm_scale, w, stream);
+}
+
+int pw_bwd_dlse(int dtype, const void* q1, const void* k1, const void* q2, const void* k2, const void* v,
+                const void* o, const void* dout, const float* lse, const float* dlse, void* dq1, void* dk1,
+                void* dq2, void* dk2, void* dv, void* workspace, size_t workspace_bytes, int B, int H, int M, int N,
+                int D, int causal, float sm_scale, int w, void* stream) {
   return bwd_common(dtype, fa::PW, q1, k1, q2, k2, v, o, dout, lse, dlse, dq1, dk1, dq2, dk2, dv, workspace,
                     workspace_bytes, B, H, M, N, D, causal, sm_scale, w, stream);
 }
@@ -455,7 +477,14 @@ size_t resmerge_bwd_workspace_size(int rows, int D) {
 
 int resmerge_bwd(int dtype, const void* x, const void* q, const void* y0, const float* l0, const void* gy,
                  const float* gl, void* gx, float* gq, void* gy0, float* gl0, void* workspace,
-                 size_t workspace_bytes, int rows, int D, float eps, int accumulate, void* stream) {
+                 size_t workspace_bytes, int rows, int D, float eps, void* stream) {
+  return resmerge_bwd_acc(dtype, x, q, y0, l0, gy, gl, gx, gq, gy0, gl0, workspace, workspace_bytes, rows, D, eps, 0,
+                          stream);
+}
+
+int resmerge_bwd_acc(int dtype, const void* x, const void* q, const void* y0, const float* l0, const void* gy,
+                     const float* gl, void* gx, float* gq, void* gy0, float* gl0, void* workspace,
+                     size_t workspace_bytes, int rows, int D, float eps, int accumulate, void* stream) {
   FA_TRY(check_tensors({x, q, y0, gy, gx, gy0}));
   FA_TRY(check_scalars({l0, gq, gl0}));
   if (gl && !aligned(gl, 4)) return FA_ERR_ALIGN;

@@ -42,19 +42,24 @@ _SIGNATURES = {
     "fa_fwd": ([_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P], _I),
     "fa_fwd_fp8": ([_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P], _I),
     "fa_bwd_workspace_size": ([_I, _I, _I, _I, _I, _I], _Z),
-    "fa_bwd": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _I, _F, _P], _I),
+    "fa_bwd": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _I, _F, _P], _I),
+    "fa_bwd_dlse": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _I, _F, _P], _I),
     "fa_bwd_delta": ([_I, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "fa_bwd_dkdv": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P], _I),
     "fa_bwd_dq": ([_I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P], _I),
     "fa_bwd_dq_delta": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P], _I),
-    "fa_fwd_jvp": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P], _I),
+    "fa_fwd_jvp": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P], _I),
+    "fa_fwd_jvp_tlse": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P], _I),
     "pw_fwd": ([_I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I, _P], _I),
     "pw_bwd_workspace_size": ([_I, _I, _I, _I, _I, _I], _Z),
-    "pw_bwd": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
+    "pw_bwd": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
                 _I, _I, _I, _I, _I, _I, _F, _I, _P], _I),
+    "pw_bwd_dlse": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z,
+                     _I, _I, _I, _I, _I, _I, _F, _I, _P], _I),
     "resmerge_fwd": ([_I, _P, _P, _P, _P, _P, _P, _I, _I, _F, _P], _I),
     "resmerge_bwd_workspace_size": ([_I, _I], _Z),
-    "resmerge_bwd": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _F, _I, _P], _I),
+    "resmerge_bwd": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _F, _P], _I),
+    "resmerge_bwd_acc": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _F, _I, _P], _I),
     "lse_merge_fwd": ([_I, _P, _P, _P, _P, _I, _I, _I, _P], _I),
     "lse_merge_bwd": ([_I, _P, _P, _P, _P, _P, _P, _I, _I, _I, _P], _I),
 }
@@ -134,11 +139,19 @@ def fa_bwd_workspace_size(B, H, M, N, D, dtype):
     return load().fa_bwd_workspace_size(B, H, M, N, D, dtype)
 
 
-def fa_bwd(dtype, q, k, v, o, dout, lse, dlse, dq, dk, dv, workspace, workspace_bytes,
+def fa_bwd(dtype, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes,
            B, H, M, N, D, causal, sm_scale, stream=None):
     _check("fa_bwd", load().fa_bwd(dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
-                                   _ptr(dlse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace_bytes,
+                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace_bytes,
                                    B, H, M, N, D, int(causal), sm_scale, _stream(stream)))
+
+
+def fa_bwd_dlse(dtype, q, k, v, o, dout, lse, dlse, dq, dk, dv, workspace, workspace_bytes,
+                B, H, M, N, D, causal, sm_scale, stream=None):
+    _check("fa_bwd_dlse", load().fa_bwd_dlse(dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                             _ptr(dlse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                             workspace_bytes, B, H, M, N, D, int(causal), sm_scale,
+                                             _stream(stream)))
 
 
 def fa_bwd_delta(dtype, o, dout, dlse, delta, B, H, M, D, stream=None):
@@ -164,10 +177,16 @@ def fa_bwd_dq_delta(dtype, q, k, v, o, dout, lse, dlse, delta, dq, B, H, M, N, D
                                                      int(causal), sm_scale, _stream(stream)))
 
 
-def fa_fwd_jvp(dtype, q, k, v, tq, tk, tv, o, lse, to, tlse, B, H, M, N, D, causal, sm_scale, stream=None):
+def fa_fwd_jvp(dtype, q, k, v, tq, tk, tv, o, lse, to, B, H, M, N, D, causal, sm_scale, stream=None):
     _check("fa_fwd_jvp", load().fa_fwd_jvp(dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk), _ptr(tv),
-                                           _ptr(o), _ptr(lse), _ptr(to), _ptr(tlse), B, H, M, N, D, int(causal),
+                                           _ptr(o), _ptr(lse), _ptr(to), B, H, M, N, D, int(causal),
                                            sm_scale, _stream(stream)))
+
+
+def fa_fwd_jvp_tlse(dtype, q, k, v, tq, tk, tv, o, lse, to, tlse, B, H, M, N, D, causal, sm_scale, stream=None):
+    _check("fa_fwd_jvp_tlse", load().fa_fwd_jvp_tlse(dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(tq), _ptr(tk),
+                                                     _ptr(tv), _ptr(o), _ptr(lse), _ptr(to), _ptr(tlse),
+                                                     B, H, M, N, D, int(causal), sm_scale, _stream(stream)))
 
 
 def pw_fwd(dtype, q1, k1, q2, k2, v, o, lse, B, H, M, N, D, causal, sm_scale, w, stream=None):
@@ -179,12 +198,20 @@ def pw_bwd_workspace_size(B, H, M, N, D, dtype):
     return load().pw_bwd_workspace_size(B, H, M, N, D, dtype)
 
 
-def pw_bwd(dtype, q1, k1, q2, k2, v, o, dout, lse, dlse, dq1, dk1, dq2, dk2, dv, workspace, workspace_bytes,
+def pw_bwd(dtype, q1, k1, q2, k2, v, o, dout, lse, dq1, dk1, dq2, dk2, dv, workspace, workspace_bytes,
            B, H, M, N, D, causal, sm_scale, w, stream=None):
     _check("pw_bwd", load().pw_bwd(dtype, _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(v), _ptr(o), _ptr(dout),
-                                   _ptr(lse), _ptr(dlse), _ptr(dq1), _ptr(dk1), _ptr(dq2), _ptr(dk2), _ptr(dv),
+                                   _ptr(lse), _ptr(dq1), _ptr(dk1), _ptr(dq2), _ptr(dk2), _ptr(dv),
                                    _ptr(workspace), workspace_bytes, B, H, M, N, D, int(causal), sm_scale, w,
                                    _stream(stream)))
+
+
+def pw_bwd_dlse(dtype, q1, k1, q2, k2, v, o, dout, lse, dlse, dq1, dk1, dq2, dk2, dv, workspace, workspace_bytes,
+                B, H, M, N, D, causal, sm_scale, w, stream=None):
+    _check("pw_bwd_dlse", load().pw_bwd_dlse(dtype, _ptr(q1), _ptr(k1), _ptr(q2), _ptr(k2), _ptr(v), _ptr(o),
+                                             _ptr(dout), _ptr(lse), _ptr(dlse), _ptr(dq1), _ptr(dk1), _ptr(dq2),
+                                             _ptr(dk2), _ptr(dv), _ptr(workspace), workspace_bytes, B, H, M, N, D,
+                                             int(causal), sm_scale, w, _stream(stream)))
 
 
 def resmerge_fwd(dtype, x, q, y0, l0, y, lse, rows, D, eps, stream=None):
@@ -197,11 +224,18 @@ def resmerge_bwd_workspace_size(rows, D):
 
 
 def resmerge_bwd(dtype, x, q, y0, l0, gy, gl, gx, gq, gy0, gl0, workspace, workspace_bytes, rows, D, eps,
-                 accumulate=0, stream=None):
+                 stream=None):
     _check("resmerge_bwd", load().resmerge_bwd(dtype, _ptr(x), _ptr(q), _ptr(y0), _ptr(l0), _ptr(gy), _ptr(gl),
                                                _ptr(gx), _ptr(gq), _ptr(gy0), _ptr(gl0), _ptr(workspace),
-                                               workspace_bytes, rows, D, eps, int(accumulate),
-                                               _stream(stream)))
+                                               workspace_bytes, rows, D, eps, _stream(stream)))
+
+
+def resmerge_bwd_acc(dtype, x, q, y0, l0, gy, gl, gx, gq, gy0, gl0, workspace, workspace_bytes, rows, D, eps,
+                     accumulate, stream=None):
+    _check("resmerge_bwd_acc", load().resmerge_bwd_acc(dtype, _ptr(x), _ptr(q), _ptr(y0), _ptr(l0), _ptr(gy),
+                                                       _ptr(gl), _ptr(gx), _ptr(gq), _ptr(gy0), _ptr(gl0),
+                                                       _ptr(workspace), workspace_bytes, rows, D, eps,
+                                                       int(accumulate), _stream(stream)))
 
 
 def lse_merge_fwd(dtype, ys, lses, y, lse, S, rows, D, stream=None):

@@ -102,7 +102,7 @@ def attn_calls(wl, d, b):
     q, k, v, do = d["q"], d["k"], d["v"], d["do"]
     return {
         "fwd": lambda: lib.fa_fwd(wl.dtype, q, k, v, b["o"], b["lse"], B, H, M, N, D, c, s),
-        "bwd": lambda: lib.fa_bwd(wl.dtype, q, k, v, b["o"], do, b["lse"], None, b["dq"], b["dk"], b["dv"],
+        "bwd": lambda: lib.fa_bwd(wl.dtype, q, k, v, b["o"], do, b["lse"], b["dq"], b["dk"], b["dv"],
                                   b["ws"], b["ws_bytes"], B, H, M, N, D, c, s),
         "delta": lambda: lib.fa_bwd_delta(wl.dtype, b["o"], do, None, b["delta"], B, H, M, D),
         "dkdv": lambda: lib.fa_bwd_dkdv(wl.dtype, q, k, v, do, b["lse"], b["delta"], b["dk"], b["dv"],
@@ -267,7 +267,7 @@ def bench_jvp(torch, timer, name, iters):
     _, d = attn_setup(torch, wl, names)
     B, H, M, N, D = wl.B, wl.H, wl.M, wl.N, wl.D
     o, to, lse = empty((B, H, M, D), wl.dtype), empty((B, H, M, D), wl.dtype), empty_f32((B, H, M))
-    ms = timer.avg_ms(lambda: lib.fa_fwd_jvp(wl.dtype, *[d[n] for n in names], o, lse, to, None,
+    ms = timer.avg_ms(lambda: lib.fa_fwd_jvp(wl.dtype, *[d[n] for n in names], o, lse, to,
                                              B, H, M, N, D, wl.causal, wl.sm_scale), iters)
     tf = 3 * wl.fwd_flops() / (ms * 1e-3) / 1e12
     return {"ms": round(ms, 4), "TFLOP/s": round(tf, 2), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
@@ -313,7 +313,7 @@ def bench_pw(torch, timer, iters):
     ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
     args = (B, H, M, N, D, wl.causal, wl.sm_scale, PIECEWISE_W)
     fwd = lambda: lib.pw_fwd(wl.dtype, *[d[n] for n in names[:5]], o, lse, *args)
-    bwd = lambda: lib.pw_bwd(wl.dtype, *[d[n] for n in names[:5]], o, d["do"], lse, None, *g, ws, nb, *args)
+    bwd = lambda: lib.pw_bwd(wl.dtype, *[d[n] for n in names[:5]], o, d["do"], lse, *g, ws, nb, *args)
     fwd()
     f_ms = timer.avg_ms(fwd, iters)
     b_ms = timer.avg_ms(bwd, iters)

@@ -44,6 +44,12 @@
  *   attention and the backward need fp32 there); every other D, or D = 256
  *   on those entry points in fp16/bf16, gives FA_ERR_UNSUPPORTED.
  *
+ * The seven entry points of the hot path (fa_fwd, fa_bwd, fa_fwd_jvp,
+ * pw_fwd, pw_bwd, resmerge_fwd, resmerge_bwd) keep the pages' operations
+ * and nothing more; options the pages do not have (a gradient reaching LSE,
+ * the LSE tangent, accumulation into gx/gq) are separate entry points with
+ * their own names (*_dlse, *_tlse, *_acc) and one extra argument each.
+ *
  * Citations name the page and the function or passage whose computation the
  * entry point performs:
  *   [tutorial]  Birch-san's gist _06_fused_attention_blockptr_jvp.py (Triton
@@ -109,13 +115,9 @@ int fa_fwd_fp8(int out_dtype, const void* q, const void* k, const void* vt, void
  * Attention backward [tutorial: _attn_bwd_preprocess, _attn_bwd_dkdv,
  * _attn_bwd_dq, with the non-causal block range from the comment thread;
  * piecewise: _bwd_preprocess, _bwd_kv_kernel, _bwd_q_kernel].
- * Gradients of <dout, O> + <dlse, LSE> with (O, LSE) = fa_fwd(q, k, v); o
- * and lse must be the outputs of fa_fwd on the same inputs.  dlse [B,H,M]
- * fp32 is the gradient reaching the LSE output (e.g. resmerge_bwd's gl0);
- * NULL means zeros and gives the pages' backward.  The pages' backward has
- * no such input: by the chain rule dLSE_i/dS_ij = P_ij, so it enters as
- * dS = P (dP - (Delta - dlse)).  The steps:
- *   Delta_i = sum_d o_id dout_id - dlse_i           (fa_bwd_delta)
+ * Gradients dq, dk, dv of <dout, O> with (O, LSE) = fa_fwd(q, k, v); o
+ * and lse must be the outputs of fa_fwd on the same inputs.  The steps:
+ *   Delta_i = sum_d o_id dout_id                      (fa_bwd_delta)
  *   dK, dV  with K/V resident, looping over queries  (fa_bwd_dkdv)
  *   dQ      with Q resident, looping over keys       (fa_bwd_dq)
  * For fp16/bf16 fa_bwd makes two launches on `stream`: fa_bwd_dq_delta (the
@@ -126,9 +128,23 @@ int fa_fwd_fp8(int out_dtype, const void* q, const void* k, const void* vt, void
  */
 size_t fa_bwd_workspace_size(int B, int H, int M, int N, int D, int dtype);
 int fa_bwd(int dtype, const void* q, const void* k, const void* v, const void* o,
-           const void* dout, const float* lse, const float* dlse, void* dq, void* dk, void* dv,
+           const void* dout, const float* lse, void* dq, void* dk, void* dv,
            void* workspace, size_t workspace_bytes,
            int B, int H, int M, int N, int D, int causal, float sm_scale, void* stream);
+
+/*
+ * fa_bwd with a gradient reaching the LSE output as well (not on the pages:
+ * their backward takes dout only).  Gradients of <dout, O> + <dlse, LSE>;
+ * dlse [B,H,M] fp32 is e.g. resmerge_bwd's gl0 when the attention output
+ * feeds the merge as (y0, l0); NULL means zeros, i.e. exactly fa_bwd.  By
+ * the chain rule dLSE_i/dS_ij = P_ij, so it enters as
+ * dS = P (dP - (Delta - dlse)): Delta_i = sum_d o_id dout_id - dlse_i.
+ * Arguments otherwise as fa_bwd (dlse is inserted after lse).
+ */
+int fa_bwd_dlse(int dtype, const void* q, const void* k, const void* v, const void* o,
+                const void* dout, const float* lse, const float* dlse, void* dq, void* dk, void* dv,
+                void* workspace, size_t workspace_bytes,
+                int B, int H, int M, int N, int D, int causal, float sm_scale, void* stream);
 
 /* The steps of fa_bwd, exposed separately so each can be timed. */
 /* delta [B,H,M] fp32 <- rowsum(o * dout) - dlse (dlse may be NULL)
@@ -159,14 +175,24 @@ int fa_bwd_dq_delta(int dtype, const void* q, const void* k, const void* v, cons
  *   to = d/dt O(q + t*tq, k + t*tk, v + t*tv) at t = 0          [B,H,M,D]
  * computed in the same pass: with Sdot = sm_scale (tq K^T + Q tk^T),
  *   to = (P*Sdot) V - rowsum(P*Sdot) O + P tv.
- * tq is q-like, tk and tv are k-like.  tlse [B,H,M] fp32 (may be NULL)
- * receives the tangent of lse, rowsum(P*Sdot) (dLSE_i/dS_ij = P_ij; the
- * pages return no LSE tangent); 0 for a row with no visible key.
+ * tq is q-like, tk and tv are k-like.
  */
 int fa_fwd_jvp(int dtype, const void* q, const void* k, const void* v,
                const void* tq, const void* tk, const void* tv,
-               void* o, float* lse, void* to, float* tlse,
+               void* o, float* lse, void* to,
                int B, int H, int M, int N, int D, int causal, float sm_scale, void* stream);
+
+/*
+ * fa_fwd_jvp that also returns the tangent of lse (not on the pages: they
+ * return tO only).  tlse [B,H,M] fp32 (may be NULL, which is exactly
+ * fa_fwd_jvp) receives rowsum(P*Sdot), since dLSE_i/dS_ij = P_ij; 0 for a
+ * row with no visible key.  Arguments otherwise as fa_fwd_jvp (tlse is
+ * inserted after to).
+ */
+int fa_fwd_jvp_tlse(int dtype, const void* q, const void* k, const void* v,
+                    const void* tq, const void* tk, const void* tv,
+                    void* o, float* lse, void* to, float* tlse,
+                    int B, int H, int M, int N, int D, int causal, float sm_scale, void* stream);
 
 /*
  * Piecewise attention forward [piecewise: attention() and _fwd_kernel].
@@ -183,16 +209,24 @@ int pw_fwd(int dtype, const void* q1, const void* k1, const void* q2, const void
  * Piecewise attention backward [piecewise: _bwd_preprocess, _bwd_kv_kernel,
  * _bwd_q_kernel].  dS is split by the same distance rule: the near part
  * yields dq1, dk1, the far part dq2, dk2; dv = P^T dout.  o and lse must come
- * from pw_fwd on the same inputs; dlse (may be NULL) as for fa_bwd.
- * workspace as for fa_bwd
+ * from pw_fwd on the same inputs.  workspace as for fa_bwd
  * (pw_bwd_workspace_size() bytes, holds Delta).
  */
 size_t pw_bwd_workspace_size(int B, int H, int M, int N, int D, int dtype);
 int pw_bwd(int dtype, const void* q1, const void* k1, const void* q2, const void* k2,
-           const void* v, const void* o, const void* dout, const float* lse, const float* dlse,
+           const void* v, const void* o, const void* dout, const float* lse,
            void* dq1, void* dk1, void* dq2, void* dk2, void* dv,
            void* workspace, size_t workspace_bytes,
            int B, int H, int M, int N, int D, int causal, float sm_scale, int w, void* stream);
+
+/* pw_bwd with a gradient dlse [B,H,M] fp32 reaching the LSE output (may be
+ * NULL: exactly pw_bwd), entering dS as in fa_bwd_dlse; dlse is inserted
+ * after lse. */
+int pw_bwd_dlse(int dtype, const void* q1, const void* k1, const void* q2, const void* k2,
+                const void* v, const void* o, const void* dout, const float* lse, const float* dlse,
+                void* dq1, void* dk1, void* dq2, void* dk2, void* dv,
+                void* workspace, size_t workspace_bytes,
+                int B, int H, int M, int N, int D, int causal, float sm_scale, int w, void* stream);
 
 /*
  * Block-residual two-way online-softmax merge, forward [merge:
@@ -211,19 +245,28 @@ int resmerge_fwd(int dtype, const void* x, const void* q, const void* y0, const 
  * launcher].  VJP of resmerge_fwd for <gy, y> + <gl, lse>; gl == NULL means
  * zeros.  Outputs: gx, gy0 [rows, D] dtype; gl0 [rows] fp32; gq [D] fp32 =
  * sum over rows, reduced in a fixed order (no float atomics, so repeated
- * calls are bitwise identical).  accumulate = 0: every output is
- * overwritten.  accumulate = 1: the gradient is added to what gx and gq
- * hold (gx rounded once after the fp32 sum), as the page's kernel adds into
- * the caller's grad_intrablock_partial_sum and grad_pseudo_query buffers;
- * gy0 and gl0 are overwritten in both modes, as on the page.  Other values:
- * FA_ERR_UNSUPPORTED.  workspace: at least resmerge_bwd_workspace_size(rows,
- * D) bytes of device scratch (per-block partial sums of gq).
+ * calls are bitwise identical).  Every output is overwritten.  workspace:
+ * at least resmerge_bwd_workspace_size(rows, D) bytes of device scratch
+ * (per-block partial sums of gq).
  */
 size_t resmerge_bwd_workspace_size(int rows, int D);
 int resmerge_bwd(int dtype, const void* x, const void* q, const void* y0, const float* l0,
                  const void* gy, const float* gl, void* gx, float* gq, void* gy0, float* gl0,
-                 void* workspace, size_t workspace_bytes, int rows, int D, float eps,
-                 int accumulate, void* stream);
+                 void* workspace, size_t workspace_bytes, int rows, int D, float eps, void* stream);
+
+/*
+ * resmerge_bwd with the page kernel's accumulate semantics as an option.
+ * accumulate = 0: exactly resmerge_bwd.  accumulate = 1: the gradient is
+ * added to what gx and gq hold (gx rounded once after the fp32 sum), as the
+ * page's kernel adds into the caller's grad_intrablock_partial_sum and
+ * grad_pseudo_query buffers; gy0 and gl0 are overwritten in both modes, as
+ * on the page.  Other values: FA_ERR_UNSUPPORTED.  accumulate is inserted
+ * after eps.
+ */
+int resmerge_bwd_acc(int dtype, const void* x, const void* q, const void* y0, const float* l0,
+                     const void* gy, const float* gl, void* gx, float* gq, void* gy0, float* gl0,
+                     void* workspace, size_t workspace_bytes, int rows, int D, float eps,
+                     int accumulate, void* stream);
 
 /*
  * N-way online-softmax merge of (y, lse) partials, forward [merge: the

@@ -90,30 +90,33 @@ def test_fa_fwd_rejects(kw, code):
 
 
 def test_bwd_rejects_small_workspace():
-    args = [2, P[0], P[1], P[2], P[3], P[5], P[4], None, P[6], P[7], P[8], P[9], 2 * 128 * 4 - 4,
+    args = [2, P[0], P[1], P[2], P[3], P[5], P[4], P[6], P[7], P[8], P[9], 2 * 128 * 4 - 4,
             1, 2, 128, 128, 64, 1, 0.0, None]
     assert status(lib.fa_bwd, *args) == -5
-    args[11] = None
-    args[12] = 1 << 20
+    args[10] = None
+    args[11] = 1 << 20
     assert status(lib.fa_bwd, *args) == -5
-    args = [2, P[0], P[1], P[2], P[3], P[5], P[4], None, None, P[7], P[8], P[9], 1 << 20,
+    args = [2, P[0], P[1], P[2], P[3], P[5], P[4], None, P[7], P[8], P[9], 1 << 20,
             1, 2, 128, 128, 64, 1, 0.0, None]
     assert status(lib.fa_bwd, *args) == -1
-    # an optional LSE gradient must still be 4-byte aligned
+    # the variant with an LSE gradient: that gradient is optional but must be 4-byte aligned
     args = [2, P[0], P[1], P[2], P[3], P[5], P[4], P[4] + 2, P[6], P[7], P[8], P[9], 1 << 20,
             1, 2, 128, 128, 64, 1, 0.0, None]
-    assert status(lib.fa_bwd, *args) == -4
+    assert status(lib.fa_bwd_dlse, *args) == -4
+    args[7] = None
+    args[12] = 4
+    assert status(lib.fa_bwd_dlse, *args) == -5
 
 
 def test_head_dim_256_support():
     # 16-bit D = 256: plain forward only; the JVP and the backward reject it
-    assert status(lib.fa_fwd_jvp, 1, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], None,
+    assert status(lib.fa_fwd_jvp, 1, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8],
                   1, 1, 64, 64, 256, 0, 0.0) == -6
     assert status(lib.fa_bwd_dq, 2, P[0], P[1], P[2], P[3], P[4], P[5], P[6],
                   1, 1, 64, 64, 256, 0, 0.0) == -6
     assert status(lib.pw_fwd, 2, P[0], P[1], P[2], P[3], P[4], P[5], P[6],
                   1, 1, 64, 64, 256, 1, 0.0, 10) == -6
-    args = [2, P[0], P[1], P[2], P[3], P[5], P[4], None, P[6], P[7], P[8], P[9], 1 << 20,
+    args = [2, P[0], P[1], P[2], P[3], P[5], P[4], P[6], P[7], P[8], P[9], 1 << 20,
             1, 2, 128, 128, 256, 1, 0.0, None]
     assert status(lib.fa_bwd, *args) == -6
 
@@ -147,14 +150,18 @@ def test_step_entry_points_reject():
 
 
 def test_jvp_and_pw_reject():
-    assert status(lib.fa_fwd_jvp, 1, P[0], P[1], P[2], None, P[4], P[5], P[6], P[7], P[8], None,
+    assert status(lib.fa_fwd_jvp, 1, P[0], P[1], P[2], None, P[4], P[5], P[6], P[7], P[8],
                   1, 1, 64, 64, 64, 0, 0.0) == -1
-    assert status(lib.fa_fwd_jvp, 1, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], P[9] + 2,
+    assert status(lib.fa_fwd_jvp_tlse, 1, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], P[9] + 2,
                   1, 1, 64, 64, 64, 0, 0.0) == -4
+    assert status(lib.fa_fwd_jvp_tlse, 1, P[0], P[1], P[2], P[3], P[4], P[5], P[6], None, P[8], P[9],
+                  1, 1, 64, 64, 64, 0, 0.0) == -1
     assert status(lib.pw_fwd, 1, P[0], P[1], P[2], P[3], P[4], P[5], P[6],
                   1, 1, 64, 64, 256, 1, 0.0, 10) == -6
-    assert status(lib.pw_bwd, 1, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], None, P[8], P[9], P[10],
+    assert status(lib.pw_bwd, 1, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], P[9], P[10],
                   P[11], P[12], P[13], 0, 1, 1, 64, 64, 64, 1, 0.0, 10) == -5
+    assert status(lib.pw_bwd_dlse, 1, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8] + 1, P[9], P[10],
+                  P[11], P[12], P[13], P[14], 1 << 20, 1, 1, 64, 64, 64, 1, 0.0, 10) == -4
 
 
 def test_merge_rejects():
@@ -174,7 +181,9 @@ def test_merge_rejects():
     args[7] = None  # gx
     assert status(b, *args) == -1
     args[7] = P[7]
-    assert status(b, *args, 2) == -6  # accumulate is 0 or 1
+    assert status(lib.resmerge_bwd_acc, *args, 2) == -6  # accumulate is 0 or 1
+    args[12] = need - 4
+    assert status(lib.resmerge_bwd_acc, *args, 1) == -5
 
 
 def test_load_missing_library_raises():

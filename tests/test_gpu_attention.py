@@ -40,8 +40,12 @@ def run_fwd_bwd(wl, t, with_bwd=True, steps=False, guard=False, dlse=None):
         else:
             ws_bytes = lib.fa_bwd_workspace_size(B, H, M, N, D, wl.dtype)
             ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
-            lib.fa_bwd(wl.dtype, q, k, v, o, do, lse, dlse, dq, dk, dv, ws, ws_bytes, B, H, M, N, D,
-                       wl.causal, wl.sm_scale)
+            if dlse is None:
+                lib.fa_bwd(wl.dtype, q, k, v, o, do, lse, dq, dk, dv, ws, ws_bytes, B, H, M, N, D,
+                           wl.causal, wl.sm_scale)
+            else:
+                lib.fa_bwd_dlse(wl.dtype, q, k, v, o, do, lse, dlse, dq, dk, dv, ws, ws_bytes, B, H, M, N, D,
+                                wl.causal, wl.sm_scale)
         out.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     res = {kk: host(vv) for kk, vv in out.items()}

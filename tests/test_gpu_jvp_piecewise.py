@@ -26,7 +26,7 @@ def run_jvp(wl, t):
     to = guarded((B, H, M, D), wl.dtype)
     lse = guarded_f32((B, H, M))
     tlse = guarded_f32((B, H, M))
-    lib.fa_fwd_jvp(wl.dtype, q, k, v, tq, tk, tv, o, lse, to, tlse, B, H, M, N, D, wl.causal, wl.sm_scale)
+    lib.fa_fwd_jvp_tlse(wl.dtype, q, k, v, tq, tk, tv, o, lse, to, tlse, B, H, M, N, D, wl.causal, wl.sm_scale)
     torch.cuda.synchronize()
     res = {"o": host(o), "lse": host(lse), "to": host(to), "tlse": host(tlse)}
     check_guards()
@@ -107,8 +107,13 @@ def run_pw(wl, t, w, with_bwd=True, dlse=None):
                  (("dq1", q1), ("dk1", k1), ("dq2", q2), ("dk2", k2), ("dv", v))}
         nb = lib.pw_bwd_workspace_size(B, H, M, N, D, wl.dtype)
         ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
-        lib.pw_bwd(wl.dtype, q1, k1, q2, k2, v, o, do, lse, dlse, grads["dq1"], grads["dk1"], grads["dq2"],
-                   grads["dk2"], grads["dv"], ws, nb, B, H, M, N, D, wl.causal, wl.sm_scale, w)
+        gl = [grads[n] for n in ("dq1", "dk1", "dq2", "dk2", "dv")]
+        if dlse is None:
+            lib.pw_bwd(wl.dtype, q1, k1, q2, k2, v, o, do, lse, *gl, ws, nb, B, H, M, N, D, wl.causal,
+                       wl.sm_scale, w)
+        else:
+            lib.pw_bwd_dlse(wl.dtype, q1, k1, q2, k2, v, o, do, lse, dlse, *gl, ws, nb, B, H, M, N, D,
+                            wl.causal, wl.sm_scale, w)
         out.update(grads)
     torch.cuda.synchronize()
     res = {kk: host(vv) for kk, vv in out.items()}

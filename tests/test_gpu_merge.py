@@ -122,7 +122,7 @@ def test_merge_bwd_accumulate(case):
     gq.copy_(dev(prior["gq0"]))
     nb = lib.resmerge_bwd_workspace_size(R, D)
     ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
-    lib.resmerge_bwd(dtype, x, q, y0, l0, gy, gl, gx, gq, gy0, gl0, ws, nb, R, D, eps, 1)
+    lib.resmerge_bwd_acc(dtype, x, q, y0, l0, gy, gl, gx, gq, gy0, gl0, ws, nb, R, D, eps, 1)
     torch.cuda.synchronize()
     got = {n: host(v) for n, v in (("gx", gx), ("gq", gq), ("gy0", gy0), ("gl0", gl0))}
     check_guards()
