@@ -47,18 +47,15 @@ int check_scalars(std::initializer_list<const void*> ps) {
   return FA_OK;
 }
 
-// Head dims: 32, 64, 128 for every entry point; 256 for fp32 everywhere and
-// for fp16/bf16 in the plain forward only (full = false: the fused JVP, the
-// piecewise forward and every backward step, whose 16-bit kernels keep
-// more per-row state than a 256-wide head leaves room for).
-int check_attn_shape(int B, int H, int M, int N, int D, int dtype = FA_F32, bool full = true) {
+// Head dims: 16, 32, 64, 128, 256 (those the tutorial's Function accepts)
+// for every entry point and dtype.
+int check_attn_shape(int B, int H, int M, int N, int D) {
   if (B <= 0 || H <= 0 || M <= 0 || N <= 0 || D <= 0) return FA_ERR_SHAPE;
   // grid sizes and element offsets must stay representable
   const int64_t bh = (int64_t)B * H;
   if (bh > (1 << 24) || M > (1 << 24) || N > (1 << 24)) return FA_ERR_SHAPE;
   if (bh * (int64_t)(M > N ? M : N) * D > ((int64_t)1 << 46)) return FA_ERR_SHAPE;
-  if (D != 32 && D != 64 && D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
-  if (D == 256 && dtype != FA_F32 && !full) return FA_ERR_UNSUPPORTED;
+  if (D != 16 && D != 32 && D != 64 && D != 128 && D != 256) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 
@@ -81,18 +78,19 @@ int hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
   } while (0)
 
 int run_fwd(FwdArgs& a, hipStream_t s) {
-  return hip_status(a.dtype == FA_F32 ? fa::launch_attn_fwd_f32(a, s) : fa::launch_attn_fwd(a, s));
+  return hip_status(fa::fwd_generic(a.dtype, a.variant, a.D) ? fa::launch_attn_fwd_generic(a, s)
+                                                              : fa::launch_attn_fwd(a, s));
 }
 
-// The whole backward.  16-bit dtypes: the dQ pass forms Delta itself and
-// writes it for the dK/dV pass that follows (two launches); fp32: the Delta
-// kernel, then the two passes.
+// The whole backward.  MFMA path (16-bit, D in {32, 64, 128}): the dQ pass
+// forms Delta itself and writes it for the dK/dV pass that follows (two
+// launches); generic path: the Delta kernel, then the two passes.
 int run_bwd(BwdArgs& a, const void* o, const float* dlse, float* delta, hipStream_t s) {
-  if (a.dtype == FA_F32) {
+  if (fa::bwd_generic(a.dtype, a.D)) {
     FA_TRY(hip_status(fa::launch_attn_delta(a.dtype, o, a.dout, dlse, delta, (int64_t)a.B * a.H * a.M, a.D, s)));
     a.delta = delta;
-    FA_TRY(hip_status(fa::launch_attn_dkdv_f32(a, s)));
-    return hip_status(fa::launch_attn_dq_f32(a, s));
+    FA_TRY(hip_status(fa::launch_attn_dkdv_generic(a, s)));
+    return hip_status(fa::launch_attn_dq_generic(a, s));
   }
   a.o = o;
   a.dlse = dlse;
@@ -108,8 +106,9 @@ int run_bwd(BwdArgs& a, const void* o, const float* dlse, float* delta, hipStrea
 // One pass of the backward (dK/dV or dQ) reading a given Delta.
 int run_bwd_pass(BwdArgs& a, const float* delta, hipStream_t s, bool dkdv) {
   a.delta = delta;
-  if (dkdv) return hip_status(a.dtype == FA_F32 ? fa::launch_attn_dkdv_f32(a, s) : fa::launch_attn_dkdv(a, s));
-  return hip_status(a.dtype == FA_F32 ? fa::launch_attn_dq_f32(a, s) : fa::launch_attn_dq(a, s));
+  const bool gen = fa::bwd_generic(a.dtype, a.D);
+  if (dkdv) return hip_status(gen ? fa::launch_attn_dkdv_generic(a, s) : fa::launch_attn_dkdv(a, s));
+  return hip_status(gen ? fa::launch_attn_dq_generic(a, s) : fa::launch_attn_dq(a, s));
 }
 
 size_t delta_bytes(int B, int H, int M) { return (size_t)B * H * M * sizeof(float); }
@@ -139,7 +138,7 @@ int fa_fwd(int dtype, const void* q, const void* k, const void* v, void* o, floa
   FA_TRY(check_dtype(dtype));
   FA_TRY(check_tensors({q, k, v, o}));
   FA_TRY(check_scalars({lse}));
-  FA_TRY(check_attn_shape(B, H, M, N, D, dtype, true));
+  FA_TRY(check_attn_shape(B, H, M, N, D));
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
   float scale;
   FA_TRY(resolve_scale(sm_scale, D, &scale));
@@ -166,7 +165,7 @@ int fa_fwd_fp8(int out_dtype, const void* q, const void* k, const void* vt, void
   if (out_dtype != FA_F16 && out_dtype != FA_BF16) return FA_ERR_DTYPE;
   FA_TRY(check_tensors({q, k, vt, o}));
   FA_TRY(check_scalars({lse}));
-  FA_TRY(check_attn_shape(B, H, M, N, D, out_dtype, true));
+  FA_TRY(check_attn_shape(B, H, M, N, D));
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
   if (N % 16 != 0) return FA_ERR_UNSUPPORTED;
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
@@ -207,7 +206,7 @@ static int bwd_common(int dtype, int variant, const void* q, const void* k, cons
   if (variant == fa::PW) FA_TRY(check_tensors({q2, k2, dq2, dk2}));
   FA_TRY(check_scalars({lse}));
   FA_TRY(check_opt_scalars({dlse}));
-  FA_TRY(check_attn_shape(B, H, M, N, D, dtype, false));
+  FA_TRY(check_attn_shape(B, H, M, N, D));
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
   float scale;
   FA_TRY(resolve_scale(sm_scale, D, &scale));
@@ -260,7 +259,7 @@ int fa_bwd_delta(int dtype, const void* o, const void* dout, const float* dlse, 
   FA_TRY(check_tensors({o, dout}));
   FA_TRY(check_scalars({delta}));
   FA_TRY(check_opt_scalars({dlse}));
-  FA_TRY(check_attn_shape(B, H, M, M, D, dtype, true));
+  FA_TRY(check_attn_shape(B, H, M, M, D));
   return hip_status(
       fa::launch_attn_delta(dtype, o, dout, dlse, delta, (int64_t)B * H * M, D, (hipStream_t)stream));
 }
@@ -274,7 +273,7 @@ static int bwd_pass(bool dkdv, int dtype, const void* q, const void* k, const vo
   else
     FA_TRY(check_tensors({q, k, v, dout, dq}));
   FA_TRY(check_scalars({lse, delta}));
-  FA_TRY(check_attn_shape(B, H, M, N, D, dtype, false));
+  FA_TRY(check_attn_shape(B, H, M, N, D));
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
   float scale;
   FA_TRY(resolve_scale(sm_scale, D, &scale));
@@ -320,7 +319,7 @@ int fa_bwd_dq_delta(int dtype, const void* q, const void* k, const void* v, cons
   FA_TRY(check_tensors({q, k, v, o, dout, dq}));
   FA_TRY(check_scalars({lse, delta}));
   FA_TRY(check_opt_scalars({dlse}));
-  FA_TRY(check_attn_shape(B, H, M, N, D, dtype, false));
+  FA_TRY(check_attn_shape(B, H, M, N, D));
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
   float scale;
   FA_TRY(resolve_scale(sm_scale, D, &scale));
@@ -341,10 +340,10 @@ int fa_bwd_dq_delta(int dtype, const void* q, const void* k, const void* v, cons
   a.causal = causal;
   a.sm_scale = scale;
   hipStream_t s = (hipStream_t)stream;
-  if (dtype == FA_F32) {
+  if (fa::bwd_generic(dtype, D)) {
     FA_TRY(hip_status(fa::launch_attn_delta(dtype, o, dout, dlse, delta, (int64_t)B * H * M, D, s)));
     a.delta = delta;
-    return hip_status(fa::launch_attn_dq_f32(a, s));
+    return hip_status(fa::launch_attn_dq_generic(a, s));
   }
   a.o = o;
   a.dlse = dlse;
@@ -365,7 +364,7 @@ int fa_fwd_jvp_tlse(int dtype, const void* q, const void* k, const void* v, cons
   FA_TRY(check_tensors({q, k, v, tq, tk, tv, o, to}));
   FA_TRY(check_scalars({lse}));
   FA_TRY(check_opt_scalars({tlse}));
-  FA_TRY(check_attn_shape(B, H, M, N, D, dtype, false));
+  FA_TRY(check_attn_shape(B, H, M, N, D));
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
   float scale;
   FA_TRY(resolve_scale(sm_scale, D, &scale));
@@ -397,7 +396,7 @@ int pw_fwd(int dtype, const void* q1, const void* k1, const void* q2, const void
   FA_TRY(check_dtype(dtype));
   FA_TRY(check_tensors({q1, k1, q2, k2, v, o}));
   FA_TRY(check_scalars({lse}));
-  FA_TRY(check_attn_shape(B, H, M, N, D, dtype, false));
+  FA_TRY(check_attn_shape(B, H, M, N, D));
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
   float scale;
   FA_TRY(resolve_scale(sm_scale, D, &scale));

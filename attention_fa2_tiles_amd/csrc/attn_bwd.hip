@@ -82,6 +82,8 @@ hipError_t launch_delta_t(const void* o, const void* dout, const float* dlse, fl
                        rows);
   else if (D == 32)
     hipLaunchKernelGGL((delta_kernel<T, 32>), grid, block, 0, s, (const T*)o, (const T*)dout, dlse, delta, rows);
+  else if (D == 16)
+    hipLaunchKernelGGL((delta_kernel<T, 16>), grid, block, 0, s, (const T*)o, (const T*)dout, dlse, delta, rows);
   else if (D == 256)
     hipLaunchKernelGGL((delta_kernel<T, 256>), grid, block, 0, s, (const T*)o, (const T*)dout, dlse, delta,
                        rows);
@@ -475,15 +477,18 @@ void attn_dkdv_kernel(const BwdParams p) {
     if (qb + 2 < nq) step(ic<2>{}, qb + 2);
   }
 
-  if (!wave_valid || (RAGGED && kj >= p.N)) return;  // keys past the last one
+  // The LDS is free after the last barrier: each wave stages its dV and dK
+  // tiles through its own part of it and stores whole rows (keys past the
+  // last one are not stored).
+  if (!wave_valid) return;
   const float dk_scale = -p.sm_scale;
-  const int64_t orow = kbase + (int64_t)kj * D;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    store_acc_t<T>((T*)p.dv + orow, dvt[dt], 32 * dt, h, 1.f);
-    store_acc_t<T>((T*)p.dk + orow, dkt[dt], 32 * dt, h, dk_scale);
-    if constexpr (kPw) store_acc_t<T>((T*)p.dk2 + orow, dk2t[dt], 32 * dt, h, dk_scale);
-  }
+  static_assert(kWaves * RowStage<D>::kStageBytes <= (int)sizeof(Sm), "output staging fits in the LDS");
+  char* stage = reinterpret_cast<char*>(&smem) + wave * RowStage<D>::kStageBytes;
+  const int nrows = RAGGED ? p.N - kw0 : 32;
+  const int64_t orow = kbase + (int64_t)kw0 * D;
+  store_tile_rows<T, D>((T*)p.dv + orow, nrows, dvt, 1.f, stage, lane);
+  store_tile_rows<T, D>((T*)p.dk + orow, nrows, dkt, dk_scale, stage, lane);
+  if constexpr (kPw) store_tile_rows<T, D>((T*)p.dk2 + orow, nrows, dk2t, dk_scale, stage, lane);
 }
 
 // =============================================================== dQ pass ==
@@ -812,13 +817,16 @@ void attn_dq_kernel(const BwdParams p) {
     if (jb + 2 < nkb) step(ic<2>{}, jb + 2);
   }
 
-  if (!wave_valid || (RAGGED && qi >= p.M)) return;  // lanes past the last query row
-  const int64_t orow = qbase + (int64_t)qi * D;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    store_acc_t<T>((T*)p.dq + orow, dqt[dt], 32 * dt, h, p.sm_scale);
-    if constexpr (kPw) store_acc_t<T>((T*)p.dq2 + orow, dq2t[dt], 32 * dt, h, p.sm_scale);
-  }
+  // The ring is free after the last barrier: each wave stages its dQ tile
+  // through its own part of it and stores whole rows (rows past the last one
+  // are not stored).
+  if (!wave_valid) return;
+  static_assert(kWaves * RowStage<D>::kStageBytes <= (int)sizeof(Sm), "output staging fits in the LDS");
+  char* stage = reinterpret_cast<char*>(&smem) + wave * RowStage<D>::kStageBytes;
+  const int nrows = RAGGED ? p.M - row0 : 32;
+  const int64_t orow = qbase + (int64_t)row0 * D;
+  store_tile_rows<T, D>((T*)p.dq + orow, nrows, dqt, p.sm_scale, stage, lane);
+  if constexpr (kPw) store_tile_rows<T, D>((T*)p.dq2 + orow, nrows, dq2t, p.sm_scale, stage, lane);
 }
 
 BwdParams make_params(const BwdArgs& a) {
@@ -889,22 +897,51 @@ template <typename T, bool DKDV>
 hipError_t dispatch(const BwdArgs& a, hipStream_t s) {
   const bool pw = a.variant == PW;
   if (a.D == 64) {
-    if (DKDV) return pw ? dkdv_t<T, 64, PW>(a, s) : dkdv_t<T, 64, PLAIN>(a, s);
-    return pw ? dq_t<T, 64, PW>(a, s) : dq_t<T, 64, PLAIN>(a, s);
+    if constexpr (DKDV) return pw ? dkdv_t<T, 64, PW>(a, s) : dkdv_t<T, 64, PLAIN>(a, s);
+    else return pw ? dq_t<T, 64, PW>(a, s) : dq_t<T, 64, PLAIN>(a, s);
   }
   if (a.D == 128) {
-    if (DKDV) return pw ? dkdv_t<T, 128, PW>(a, s) : dkdv_t<T, 128, PLAIN>(a, s);
-    return pw ? dq_t<T, 128, PW>(a, s) : dq_t<T, 128, PLAIN>(a, s);
+    if constexpr (DKDV) return pw ? dkdv_t<T, 128, PW>(a, s) : dkdv_t<T, 128, PLAIN>(a, s);
+    else return pw ? dq_t<T, 128, PW>(a, s) : dq_t<T, 128, PLAIN>(a, s);
   }
   if (a.D == 32) {
-    if (DKDV) return pw ? dkdv_t<T, 32, PW>(a, s) : dkdv_t<T, 32, PLAIN>(a, s);
-    return pw ? dq_t<T, 32, PW>(a, s) : dq_t<T, 32, PLAIN>(a, s);
+    if constexpr (DKDV) return pw ? dkdv_t<T, 32, PW>(a, s) : dkdv_t<T, 32, PLAIN>(a, s);
+    else return pw ? dq_t<T, 32, PW>(a, s) : dq_t<T, 32, PLAIN>(a, s);
   }
-
   return hipErrorInvalidValue;
 }
 
 }  // namespace
+
+// The kernels of this file are compiled in parts, so that the build can run
+// them in parallel: FA_BWD_PART selects which launcher (pass x dtype) this
+// translation unit instantiates; 0 holds Delta and the dispatch, and an
+// undefined FA_BWD_PART builds everything in one unit.
+#ifndef FA_BWD_PART
+#define FA_BWD_ALL 1
+#define FA_BWD_PART 0
+#else
+#define FA_BWD_ALL 0
+#endif
+
+#if FA_BWD_ALL || FA_BWD_PART == 1
+hipError_t bwd_dkdv_f16(const BwdArgs& a, hipStream_t s) { return dispatch<_Float16, true>(a, s); }
+#endif
+#if FA_BWD_ALL || FA_BWD_PART == 2
+hipError_t bwd_dkdv_bf16(const BwdArgs& a, hipStream_t s) { return dispatch<__bf16, true>(a, s); }
+#endif
+#if FA_BWD_ALL || FA_BWD_PART == 3
+hipError_t bwd_dq_f16(const BwdArgs& a, hipStream_t s) { return dispatch<_Float16, false>(a, s); }
+#endif
+#if FA_BWD_ALL || FA_BWD_PART == 4
+hipError_t bwd_dq_bf16(const BwdArgs& a, hipStream_t s) { return dispatch<__bf16, false>(a, s); }
+#endif
+
+#if FA_BWD_PART == 0
+hipError_t bwd_dkdv_f16(const BwdArgs& a, hipStream_t s);
+hipError_t bwd_dkdv_bf16(const BwdArgs& a, hipStream_t s);
+hipError_t bwd_dq_f16(const BwdArgs& a, hipStream_t s);
+hipError_t bwd_dq_bf16(const BwdArgs& a, hipStream_t s);
 
 hipError_t launch_attn_delta(int dtype, const void* o, const void* dout, const float* dlse, float* delta,
                              int64_t rows, int D, hipStream_t s) {
@@ -915,15 +952,16 @@ hipError_t launch_attn_delta(int dtype, const void* o, const void* dout, const f
 }
 
 hipError_t launch_attn_dkdv(const BwdArgs& a, hipStream_t s) {
-  if (a.dtype == 1) return dispatch<_Float16, true>(a, s);
-  if (a.dtype == 2) return dispatch<__bf16, true>(a, s);
+  if (a.dtype == 1) return bwd_dkdv_f16(a, s);
+  if (a.dtype == 2) return bwd_dkdv_bf16(a, s);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_dq(const BwdArgs& a, hipStream_t s) {
-  if (a.dtype == 1) return dispatch<_Float16, false>(a, s);
-  if (a.dtype == 2) return dispatch<__bf16, false>(a, s);
+  if (a.dtype == 1) return bwd_dq_f16(a, s);
+  if (a.dtype == 2) return bwd_dq_bf16(a, s);
   return hipErrorInvalidValue;
 }
+#endif
 
 }  // namespace fa

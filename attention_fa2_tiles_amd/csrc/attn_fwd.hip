@@ -33,6 +33,14 @@ using ic = std::integral_constant<int, V>;
 
 constexpr int kBN = 64;           // keys per K/V block
 constexpr float kRescaleSlack = 8.0f;  // log2 units: P may reach 2^8 before a rescale
+
+// The slack a variant may use.  The fp16 JVP packs P * Sdot into fp16 (max
+// 65504): with P up to 2^8 a tangent score above 256 would overflow, so that
+// variant rescales at every new maximum (P <= 1).
+template <typename T, int VAR>
+constexpr float rescale_slack() {
+  return (VAR == JVP && std::is_same<T, _Float16>::value) ? 0.0f : kRescaleSlack;
+}
 constexpr int kLdsBytes = 160 * 1024;
 
 // Launch shape per variant.  Variants whose per-lane state fits in 256
@@ -369,7 +377,7 @@ void attn_fwd_kernel(const FwdParams p) {
       for (int r = 0; r < 16; ++r) mx[(r >> 1) & 3] = fmaxf(mx[(r >> 1) & 3], s[st][r]);
     }
     const float mloc = halves_max(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3]))) * p.scale2;
-    if (__ballot(mloc > m_i + kRescaleSlack) != 0) {
+    if (__ballot(mloc > m_i + rescale_slack<T, VAR>()) != 0) {
       const float m_new = fmaxf(m_i, mloc);
       const float alpha = (m_new == kNegInf) ? 1.f : exp2_fast(m_i - m_new);  // m_i = -inf -> 0
       l_i *= alpha;
@@ -489,29 +497,31 @@ void attn_fwd_kernel(const FwdParams p) {
 
   // ---- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----------------------
   // Waves whose rows lie beyond M (last query block of a head) store nothing.
+  // The ring is free after the last barrier: each wave stages its output
+  // tiles through its own part of it and stores whole rows.
   if (!wave_valid) return;
   const float l = halves_sum(l_i);
   const bool has = l > 0.f;
   const float inv = has ? 1.f / l : 0.f;
-  if (RAGGED && qi >= p.M) return;  // lanes past the last query row
-  T* orow = (T*)p.o + qbase + (int64_t)qi * D;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) store_acc_t<T>(orow, acc[dt], 32 * dt, h, inv);
-  if (h == 0) p.lse[(int64_t)bh * p.M + qi] = has ? (m_i + log2f(l)) * kLn2 : kNegInf;
+  static_assert(kWaves * RowStage<D>::kStageBytes <= (int)sizeof(smem), "output staging fits in the ring");
+  char* stage = reinterpret_cast<char*>(&smem[0]) + wave * RowStage<D>::kStageBytes;
+  const int nrows = RAGGED ? p.M - row0 : 32;
+  store_tile_rows<T, D>((T*)p.o + qbase + (int64_t)row0 * D, nrows, acc, inv, stage, lane);
+  float c = 0.f;
   if constexpr (kJvp) {
     const float mu = halves_sum(mu_i);
-    const float c = mu * inv;  // mu / l
-    T* torow = (T*)p.to + qbase + (int64_t)qi * D;
+    c = mu * inv;  // mu / l
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      f32x16 t;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) t[r] = (accg[dt][r] - c * acc[dt][r]) * inv;
-      store_acc_t<T>(torow, t, 32 * dt, h, 1.f);
+      for (int r = 0; r < 16; ++r) accg[dt][r] = accg[dt][r] - c * acc[dt][r];
     }
-    // LSE tangent: sum_j P_ij Sdot_ij (0 for a row with no visible key)
-    if (h == 0 && p.tlse) p.tlse[(int64_t)bh * p.M + qi] = c;
+    store_tile_rows<T, D>((T*)p.to + qbase + (int64_t)row0 * D, nrows, accg, inv, stage, lane);
   }
+  if (RAGGED && qi >= p.M) return;  // lanes past the last query row
+  if (h == 0) p.lse[(int64_t)bh * p.M + qi] = has ? (m_i + log2f(l)) * kLn2 : kNegInf;
+  // LSE tangent: sum_j P_ij Sdot_ij (0 for a row with no visible key)
+  if (kJvp && h == 0 && p.tlse) p.tlse[(int64_t)bh * p.M + qi] = c;
 }
 
 // ---------------------------------------------------------------------------
@@ -920,15 +930,17 @@ void attn_fwd_pipe_kernel(const FwdParams p) {
     if (jb + 3 < nblk) step(std::integral_constant<int, 3>{}, jb + 3, sb, sa);
   }
 
-  // Epilogue: O = acc / l, LSE = (m + log2 l) ln 2.
+  // Epilogue: O = acc / l, LSE = (m + log2 l) ln 2.  The ring is free after
+  // the last barrier: each wave stages its O tile through its own part of it
+  // and stores whole rows.
   if (!wave_valid) return;
   const float l = halves_sum(l_i);
   const bool has = l > 0.f;
   const float inv = has ? 1.f / l : 0.f;
+  static_assert(kWaves * RowStage<D>::kStageBytes <= (int)sizeof(Sm), "O staging fits in the ring");
+  store_tile_rows<T, D>((T*)p.o + qbase + (int64_t)row0 * D, RAGGED ? p.M - row0 : 32, acc, inv,
+                        reinterpret_cast<char*>(&smem) + wave * RowStage<D>::kStageBytes, lane);
   if (RAGGED && qi >= p.M) return;  // lanes past the last query row
-  T* orow = (T*)p.o + qbase + (int64_t)qi * D;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) store_acc_t<T>(orow, acc[dt], 32 * dt, h, inv);
   if (h == 0) p.lse[(int64_t)bh * p.M + qi] = has ? (m_i + log2f(l)) * kLn2 : kNegInf;
 }
 
@@ -1004,10 +1016,32 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
+// Compiled in parts (one per dtype) so that the build runs them in
+// parallel; FA_FWD_PART 0 holds the dispatch, an undefined FA_FWD_PART
+// builds everything in one unit.
+#ifndef FA_FWD_PART
+#define FA_FWD_ALL 1
+#define FA_FWD_PART 0
+#else
+#define FA_FWD_ALL 0
+#endif
+
+#if FA_FWD_ALL || FA_FWD_PART == 1
+hipError_t fwd_f16(const FwdArgs& a, hipStream_t s) { return launch_d<_Float16>(a, s); }
+#endif
+#if FA_FWD_ALL || FA_FWD_PART == 2
+hipError_t fwd_bf16(const FwdArgs& a, hipStream_t s) { return launch_d<__bf16>(a, s); }
+#endif
+
+#if FA_FWD_PART == 0
+hipError_t fwd_f16(const FwdArgs& a, hipStream_t s);
+hipError_t fwd_bf16(const FwdArgs& a, hipStream_t s);
+
 hipError_t launch_attn_fwd(const FwdArgs& a, hipStream_t s) {
-  if (a.dtype == 1) return launch_d<_Float16>(a, s);
-  if (a.dtype == 2) return launch_d<__bf16>(a, s);
+  if (a.dtype == 1) return fwd_f16(a, s);
+  if (a.dtype == 2) return fwd_bf16(a, s);
   return hipErrorInvalidValue;
 }
+#endif
 
 }  // namespace fa

@@ -10,9 +10,12 @@
 // e4m3 (one more mantissa bit than the tutorial's e5m2 P; P <= 2^8 under the
 // lazy rescale, inside e4m3's range).  The softmax runs in fp32; O and the
 // LSE are normalised by the sum of the unrounded P (summing the rounded
-// ones would cost a decode per score; the weights' rounding then moves O by
-// at most 2^-4 sum_j w_j |v_j| to first order).  O is written in fp16 or
-// bf16.
+// ones would cost a decode per score).  The weights' rounding moves each
+// p by at most 2^-4 p where p >= 2^-6 (e4m3 normal range) and by at most
+// 2^-10 in absolute terms below it (subnormal spacing 2^-9, values under
+// 2^-10 flush to 0); divided by the row sum, which is at least the sum
+// taken against the row's true maximum, that bounds the error of O.  O is
+// written in fp16 or bf16.
 //
 // CDNA4 mapping: 4 waves x 32 query rows, 64-key blocks through a 3-stage
 // LDS ring filled by direct global -> LDS loads.  The f8f6f4 product takes

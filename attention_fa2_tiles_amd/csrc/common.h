@@ -537,4 +537,52 @@ __device__ __forceinline__ void store_acc_t(T* row_ptr, const f32x16& acc, int d
   }
 }
 
+// One wave's 32 x D output tile, held transposed in MFMA accumulators
+// (acc[dt] holds X^t[d][c] with d = 32 dt + nat_row(r, h) and column c = this
+// lane's row li), stored as 32 rows of a row-major [., D] matrix.  Stored
+// straight from the accumulators, each 8-byte store instruction would touch
+// 32 rows; staged through LDS, each 16-byte store instruction writes whole
+// consecutive rows (64 / (D / 8) of them).
+//   lds: this wave's private region of kStageBytes (32 rows, pitch 2 D + 16
+//        bytes: the padding staggers the rows over the banks);
+//   g:   row 0 of the tile in global memory (row stride D);
+//   s:   this lane's scale (its row's);
+//   nrows: rows of the tile that exist (rows from nrows on are not stored).
+// The caller makes sure no other wave uses the region.
+template <int D>
+struct RowStage {
+  static constexpr int PITCH = 2 * D + 16;
+  static constexpr int kStageBytes = 32 * PITCH;
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void store_tile_rows(T* g, int nrows, const f32x16 (&acc)[D / 32], float s, char* lds,
+                                                int lane) {
+  constexpr int PITCH = RowStage<D>::PITCH;
+  constexpr int CPR = D / 8;        // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;     // rows per store instruction
+  const int li = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const int d = 32 * dt + 8 * gq + 4 * h;
+      T t0 = (T)(acc[dt][4 * gq] * s), t1 = (T)(acc[dt][4 * gq + 1] * s);
+      T t2 = (T)(acc[dt][4 * gq + 2] * s), t3 = (T)(acc[dt][4 * gq + 3] * s);
+      u32x2 w;
+      w[0] = (uint32_t)__builtin_bit_cast(uint16_t, t0) | ((uint32_t)__builtin_bit_cast(uint16_t, t1) << 16);
+      w[1] = (uint32_t)__builtin_bit_cast(uint16_t, t2) | ((uint32_t)__builtin_bit_cast(uint16_t, t3) << 16);
+      *reinterpret_cast<u32x2*>(lds + li * PITCH + 2 * d) = w;
+    }
+  }
+  // the region is this wave's own: its LDS writes complete in order before
+  // its reads, which wait for them
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int row = RPI * i + lane / CPR, c = lane % CPR;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * PITCH + 16 * c);
+    if (row < nrows) *reinterpret_cast<u32x4*>(g + (int64_t)row * D + 8 * c) = v;
+  }
+}
+
 }  // namespace fa

@@ -110,10 +110,18 @@ hipError_t launch_attn_delta(int dtype, const void* o, const void* dout, const f
 hipError_t launch_attn_dkdv(const BwdArgs& a, hipStream_t s);
 hipError_t launch_attn_dq(const BwdArgs& a, hipStream_t s);
 
-// fp32 (no MFMA) versions of the same operations.
-hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t s);
-hipError_t launch_attn_dkdv_f32(const BwdArgs& a, hipStream_t s);
-hipError_t launch_attn_dq_f32(const BwdArgs& a, hipStream_t s);
+// Generic (no MFMA) versions of the same operations: fp32 inputs, and the
+// 16-bit head dims the MFMA kernels do not cover (16; 256 outside the plain
+// forward).  Any dtype, D in {16, 32, 64, 128, 256}.
+hipError_t launch_attn_fwd_generic(const FwdArgs& a, hipStream_t s);
+hipError_t launch_attn_dkdv_generic(const BwdArgs& a, hipStream_t s);
+hipError_t launch_attn_dq_generic(const BwdArgs& a, hipStream_t s);
+
+// Whether a shape runs on the generic kernels rather than the MFMA ones.
+inline bool fwd_generic(int dtype, int variant, int D) {
+  return dtype == 0 || D == 16 || (D == 256 && variant != PLAIN);
+}
+inline bool bwd_generic(int dtype, int D) { return dtype == 0 || D == 16 || D == 256; }
 
 hipError_t launch_merge_fwd(const MergeArgs& a, hipStream_t s);
 int merge_bwd_partial_rows(int rows, int D);   // number of gq partial vectors

@@ -76,15 +76,14 @@ class Timer:
 
 def attn_setup(torch, wl, names):
     from attention_fa2_tiles_amd.inputs import attn_inputs
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from gpu_util import dev
+    from attention_fa2_tiles_amd.devbuf import dev
     t = attn_inputs(wl, names)
     return t, {n: dev(t[n]) for n in names}
 
 
 def attn_buffers(torch, wl, d, bwd=True):
     from attention_fa2_tiles_amd import lib
-    from gpu_util import empty, empty_f32
+    from attention_fa2_tiles_amd.devbuf import empty, empty_f32
     B, H, M, N, D = wl.B, wl.H, wl.M, wl.N, wl.D
     buf = {"o": empty((B, H, M, D), wl.dtype), "lse": empty_f32((B, H, M)), "delta": empty_f32((B, H, M))}
     if bwd:
@@ -130,6 +129,13 @@ def kernel_work(wl):
         "dq": ("mfma", 1 * g),
         "delta": ("hbm", 2.0 * wl.B * wl.H * wl.M * wl.D * es + 4.0 * wl.B * wl.H * wl.M),
     }
+
+
+KERNEL_LABELS = {
+    "fwd": "forward (fa_fwd)",
+    "dkdv": "dK/dV pass of the backward (4 of its 5 counted GEMM-equivalents)",
+    "dq": "dQ pass of the backward (forms Delta; 1 of its 5 counted GEMM-equivalents)",
+}
 
 
 def source_digest(paths):
@@ -185,6 +191,13 @@ def bench_headline(torch, args, timer):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # then the same clock ramp as every per-kernel loop (Timer.WARM_S): with a
+    # handful of warm-up steps the clocks are still low when timing starts
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < Timer.WARM_S:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
     progress(f"timing {args.steps} steps")
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -219,6 +232,8 @@ def bench_headline(torch, args, timer):
     achieved = amount / (per[dominant] * 1e-3) / 1e12
     roofline = {
         "kernel": dominant,
+        "scope": f"one kernel: the {KERNEL_LABELS[dominant]}, the longest of the step; "
+                 "the whole forward and backward are in step_fracs",
         "bound": "mfma",
         "achieved": round(achieved, 2),
         "peak": PEAK_BF16_TFLOPS,
@@ -231,6 +246,7 @@ def bench_headline(torch, args, timer):
     fwd_tf = wl.fwd_flops() / (per["fwd"] * 1e-3) / 1e12
     bwd_ms = timer.avg_ms(calls["bwd"], iters)
     bwd_tf = wl.bwd_flops() / (bwd_ms * 1e-3) / 1e12
+    roofline["step_fracs"] = {"fwd": round(fwd_tf / PEAK_BF16_TFLOPS, 4), "bwd": round(bwd_tf / PEAK_BF16_TFLOPS, 4)}
     summary = {
         "fwd_TFLOP/s": round(fwd_tf, 2), "fwd_frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
         "bwd_TFLOP/s": round(bwd_tf, 2), "bwd_frac_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
@@ -260,7 +276,7 @@ def bench_attention_other(torch, timer, name, iters):
 def bench_jvp(torch, timer, name, iters):
     from attention_fa2_tiles_amd import lib
     from attention_fa2_tiles_amd.inputs import WORKLOADS
-    from gpu_util import empty, empty_f32
+    from attention_fa2_tiles_amd.devbuf import empty, empty_f32
     wl = WORKLOADS[name]
     progress(f"component {name}")
     names = ("q", "k", "v", "tq", "tk", "tv")
@@ -280,7 +296,7 @@ def bench_fp8(torch, timer, iters):
     import numpy as np
     from attention_fa2_tiles_amd import lib
     from attention_fa2_tiles_amd.inputs import BF16, F8E5M2, WORKLOADS, AttnWorkload, attn_inputs
-    from gpu_util import empty, empty_f32
+    from attention_fa2_tiles_amd.devbuf import empty, empty_f32
     base = WORKLOADS[HEADLINE]
     wl = AttnWorkload("fp8_causal_b4h16_s2048_d128", F8E5M2, base.B, base.H, base.M, base.N, base.D, True,
                       base.seed)
@@ -301,7 +317,7 @@ def bench_fp8(torch, timer, iters):
 def bench_pw(torch, timer, iters):
     from attention_fa2_tiles_amd import lib
     from attention_fa2_tiles_amd.inputs import PIECEWISE_W, WORKLOADS
-    from gpu_util import empty, empty_f32
+    from attention_fa2_tiles_amd.devbuf import empty, empty_f32
     wl = WORKLOADS["piecewise_f16_b2h16_s4096_d64_w1024"]
     progress(f"component {wl.name}")
     names = ("q1", "k1", "q2", "k2", "v", "do")
@@ -326,7 +342,7 @@ def bench_pw(torch, timer, iters):
 def bench_merge(torch, timer, iters):
     from attention_fa2_tiles_amd import lib
     from attention_fa2_tiles_amd.inputs import MERGE_WORKLOAD, merge_inputs
-    from gpu_util import dev, empty, empty_f32
+    from attention_fa2_tiles_amd.devbuf import dev, empty, empty_f32
     wl = MERGE_WORKLOAD
     progress(f"component {wl.name}")
     t = merge_inputs(wl)
@@ -353,7 +369,7 @@ def bench_merge(torch, timer, iters):
 def bench_lse_merge(torch, timer, iters):
     from attention_fa2_tiles_amd import lib
     from attention_fa2_tiles_amd.inputs import LSE_MERGE_WORKLOAD, lse_merge_inputs
-    from gpu_util import dev, empty, empty_f32
+    from attention_fa2_tiles_amd.devbuf import dev, empty, empty_f32
     wl = LSE_MERGE_WORKLOAD
     progress(f"component {wl.name}")
     t = lse_merge_inputs(wl)
@@ -420,8 +436,7 @@ def profile_mode(torch):
     from attention_fa2_tiles_amd import lib
     from attention_fa2_tiles_amd.inputs import (LSE_MERGE_WORKLOAD, MERGE_WORKLOAD, WORKLOADS, lse_merge_inputs,
                                                 merge_inputs)
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from gpu_util import dev, empty, empty_f32
+    from attention_fa2_tiles_amd.devbuf import dev, empty, empty_f32
     wl = WORKLOADS[HEADLINE]
     _, d = attn_setup(torch, wl, ("q", "k", "v", "do"))
     b = attn_buffers(torch, wl, d)
@@ -538,6 +553,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "clock_warm_s": Timer.WARM_S,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -12,7 +12,8 @@ import numpy as np
 import pytest
 
 from attention_fa2_tiles_amd import lib
-from attention_fa2_tiles_amd.inputs import BF16, F16, F32
+from attention_fa2_tiles_amd.devbuf import dev, empty, empty_f32, torch_dtype  # noqa: F401 (re-exported)
+from attention_fa2_tiles_amd.inputs import F16, F32
 
 
 def need_gpu():
@@ -21,30 +22,6 @@ def need_gpu():
         pytest.skip("no GPU visible")
     lib.load()  # raises if the HIP library is missing: there is no fallback
     return torch
-
-
-def torch_dtype(dtype):
-    import torch
-    return {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}[dtype]
-
-
-def dev(t):
-    """inputs.Tensor -> device tensor holding exactly the stored values."""
-    import torch
-    s = np.ascontiguousarray(t.storage)
-    if t.dtype == BF16:
-        return torch.from_numpy(s.view(np.int16)).view(torch.bfloat16).cuda()
-    return torch.from_numpy(s).cuda()
-
-
-def empty(shape, dtype):
-    import torch
-    return torch.empty(shape, dtype=torch_dtype(dtype), device="cuda")
-
-
-def empty_f32(shape):
-    import torch
-    return torch.empty(shape, dtype=torch.float32, device="cuda")
 
 
 def filled(shape, dtype, value=float("nan")):

@@ -16,6 +16,17 @@ HEADER = os.path.join(ROOT, "include", "fa.h")
 if not os.path.exists(lib.LIB_PATH):
     pytest.skip("libfa2tiles.so not built; run python -m attention_fa2_tiles_amd.build", allow_module_level=True)
 
+# tests/test_abi_sanitized.py reruns this module against a copy of the library
+# whose host layer is built with AddressSanitizer and UBSan
+_SANITIZED = os.environ.get("FA2TILES_ABI_TEST_LIB")
+if _SANITIZED:
+    lib._lib = lib.load(_SANITIZED)
+
+
+def test_library_under_test():
+    # the sanitized rerun must exercise the sanitized copy, not the plain one
+    assert lib.load()._name == (_SANITIZED or lib.LIB_PATH)
+
 
 def declared_functions():
     text = open(HEADER).read()
@@ -78,7 +89,7 @@ def fwd_args(**kw):
     (dict(M=-64), -2),
     (dict(D=96), -6),
     (dict(D=48), -6),
-    (dict(D=16), -6),
+    (dict(D=8), -6),
     (dict(causal=2), -6),
     (dict(sm_scale=-1.0), -6),
     (dict(sm_scale=float("nan")), -6),
@@ -108,17 +119,19 @@ def test_bwd_rejects_small_workspace():
     assert status(lib.fa_bwd_dlse, *args) == -5
 
 
-def test_head_dim_256_support():
-    # 16-bit D = 256: plain forward only; the JVP and the backward reject it
+@pytest.mark.parametrize("D", [8, 48, 96, 512])
+def test_head_dims_outside_the_set_rejected(D):
+    # every entry point takes D in {16, 32, 64, 128, 256}, the tutorial's set
     assert status(lib.fa_fwd_jvp, 1, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8],
-                  1, 1, 64, 64, 256, 0, 0.0) == -6
+                  1, 1, 64, 64, D, 0, 0.0) == -6
     assert status(lib.fa_bwd_dq, 2, P[0], P[1], P[2], P[3], P[4], P[5], P[6],
-                  1, 1, 64, 64, 256, 0, 0.0) == -6
+                  1, 1, 64, 64, D, 0, 0.0) == -6
     assert status(lib.pw_fwd, 2, P[0], P[1], P[2], P[3], P[4], P[5], P[6],
-                  1, 1, 64, 64, 256, 1, 0.0, 10) == -6
+                  1, 1, 64, 64, D, 1, 0.0, 10) == -6
     args = [2, P[0], P[1], P[2], P[3], P[5], P[4], P[6], P[7], P[8], P[9], 1 << 20,
-            1, 2, 128, 128, 256, 1, 0.0, None]
+            1, 2, 128, 128, D, 1, 0.0, None]
     assert status(lib.fa_bwd, *args) == -6
+    assert status(lib.fa_bwd_delta, 1, P[0], P[1], None, P[2], 1, 1, 64, D) == -6
 
 
 def test_fp8_forward_rejects():
@@ -144,7 +157,7 @@ def test_step_entry_points_reject():
     assert status(f, *ok[:4], None, *ok[5:]) == -1                 # o missing
     assert status(f, *ok[:8], None, *ok[9:]) == -1                 # delta missing
     assert status(f, *ok[:7], P[8] + 2, *ok[8:]) == -4             # dlse misaligned
-    assert status(f, *ok[:14], 256, *ok[15:]) == -6                # 16-bit D = 256
+    assert status(f, *ok[:14], 24, *ok[15:]) == -6                 # head dim outside the set
     assert status(f, *ok[:15], 2, *ok[16:]) == -6                  # causal not 0/1
     assert status(f, 5, *ok[1:]) == -3
 
@@ -156,8 +169,6 @@ def test_jvp_and_pw_reject():
                   1, 1, 64, 64, 64, 0, 0.0) == -4
     assert status(lib.fa_fwd_jvp_tlse, 1, P[0], P[1], P[2], P[3], P[4], P[5], P[6], None, P[8], P[9],
                   1, 1, 64, 64, 64, 0, 0.0) == -1
-    assert status(lib.pw_fwd, 1, P[0], P[1], P[2], P[3], P[4], P[5], P[6],
-                  1, 1, 64, 64, 256, 1, 0.0, 10) == -6
     assert status(lib.pw_bwd, 1, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], P[9], P[10],
                   P[11], P[12], P[13], 0, 1, 1, 64, 64, 64, 1, 0.0, 10) == -5
     assert status(lib.pw_bwd_dlse, 1, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8] + 1, P[9], P[10],
