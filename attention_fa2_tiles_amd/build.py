@@ -18,7 +18,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa2tiles.so")
-SOURCES = ["attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip", "attn_generic.hip", "merge.hip", "lse_merge.hip", "api.cpp"]
+SOURCES = ["attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip", "attn_generic.hip", "merge.hip", "lse_merge.hip",
+           "noalloc.hip", "api.cpp"]
 # Sources compiled in several parts (each part instantiates a share of the
 # kernels, selected by a macro), so the parts compile in parallel.
 PARTS = {"attn_bwd.hip": ("FA_BWD_PART", 5), "attn_fwd.hip": ("FA_FWD_PART", 3)}

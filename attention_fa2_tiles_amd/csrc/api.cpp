@@ -196,11 +196,11 @@ size_t fa_bwd_workspace_size(int B, int H, int M, int N, int D, int dtype) {
   return delta_bytes(B, H, M);
 }
 
-static int bwd_common(int dtype, int variant, const void* q, const void* k, const void* q2, const void* k2,
-                      const void* v, const void* o, const void* dout, const float* lse, const float* dlse,
-                      void* dq, void* dk,
-                      void* dq2, void* dk2, void* dv, void* workspace, size_t workspace_bytes, int B, int H,
-                      int M, int N, int D, int causal, float sm_scale, int w, void* stream) {
+// Validation and arguments of the whole backward, before the Delta buffer.
+static int bwd_args(int dtype, int variant, const void* q, const void* k, const void* q2, const void* k2,
+                    const void* v, const void* o, const void* dout, const float* lse, const float* dlse, void* dq,
+                    void* dk, void* dq2, void* dk2, void* dv, int B, int H, int M, int N, int D, int causal,
+                    float sm_scale, int w, BwdArgs* out) {
   FA_TRY(check_dtype(dtype));
   FA_TRY(check_tensors({q, k, v, o, dout, dq, dk, dv}));
   if (variant == fa::PW) FA_TRY(check_tensors({q2, k2, dq2, dk2}));
@@ -210,9 +210,8 @@ static int bwd_common(int dtype, int variant, const void* q, const void* k, cons
   if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
   float scale;
   FA_TRY(resolve_scale(sm_scale, D, &scale));
-  if (!workspace || workspace_bytes < delta_bytes(B, H, M)) return FA_ERR_WORKSPACE;
-  if (!aligned(workspace, 4)) return FA_ERR_ALIGN;
-  BwdArgs a = {};
+  BwdArgs& a = *out;
+  a = BwdArgs{};
   a.dtype = dtype;
   a.variant = variant;
   a.q = q;
@@ -235,6 +234,18 @@ static int bwd_common(int dtype, int variant, const void* q, const void* k, cons
   a.causal = causal;
   a.sm_scale = scale;
   a.w = w;
+  return FA_OK;
+}
+
+static int bwd_common(int dtype, int variant, const void* q, const void* k, const void* q2, const void* k2,
+                      const void* v, const void* o, const void* dout, const float* lse, const float* dlse,
+                      void* dq, void* dk, void* dq2, void* dk2, void* dv, void* workspace, size_t workspace_bytes,
+                      int B, int H, int M, int N, int D, int causal, float sm_scale, int w, void* stream) {
+  BwdArgs a;
+  FA_TRY(bwd_args(dtype, variant, q, k, q2, k2, v, o, dout, lse, dlse, dq, dk, dq2, dk2, dv, B, H, M, N, D, causal,
+                  sm_scale, w, &a));
+  if (!workspace || workspace_bytes < delta_bytes(B, H, M)) return FA_ERR_WORKSPACE;
+  if (!aligned(workspace, 4)) return FA_ERR_ALIGN;
   return run_bwd(a, o, dlse, (float*)workspace, (hipStream_t)stream);
 }
 
@@ -251,6 +262,19 @@ int fa_bwd_dlse(int dtype, const void* q, const void* k, const void* v, const vo
                 void* stream) {
   return bwd_common(dtype, fa::PLAIN, q, k, nullptr, nullptr, v, o, dout, lse, dlse, dq, dk, nullptr, nullptr, dv,
                     workspace, workspace_bytes, B, H, M, N, D, causal, sm_scale, 0, stream);
+}
+
+int fa_bwd_noalloc(int dtype, const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int B, int H, int M, int N, int D, int causal,
+                   float sm_scale, void* stream) {
+  BwdArgs a;
+  FA_TRY(bwd_args(dtype, fa::PLAIN, q, k, nullptr, nullptr, v, o, dout, lse, nullptr, dq, dk, nullptr, nullptr, dv, B,
+                  H, M, N, D, causal, sm_scale, 0, &a));
+  const int64_t rows = (int64_t)B * H * M;
+  if (rows > fa::kNoAllocDeltaRows) return FA_ERR_UNSUPPORTED;
+  float* delta = nullptr;
+  FA_TRY(hip_status(fa::noalloc_delta_scratch((size_t)rows, &delta)));
+  return run_bwd(a, o, nullptr, delta, (hipStream_t)stream);
 }
 
 int fa_bwd_delta(int dtype, const void* o, const void* dout, const float* dlse, float* delta, int B, int H, int M,

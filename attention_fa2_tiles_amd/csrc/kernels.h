@@ -123,6 +123,13 @@ inline bool fwd_generic(int dtype, int variant, int D) {
 }
 inline bool bwd_generic(int dtype, int D) { return dtype == 0 || D == 16 || D == 256; }
 
+// The no-allocation backward's Delta rows live in a device array of this
+// many floats (8 MiB), one copy per GPU; noalloc_delta_scratch returns the
+// current device's copy (looked up once per device), or an error when rows
+// exceeds it.
+constexpr int64_t kNoAllocDeltaRows = (int64_t)1 << 21;
+hipError_t noalloc_delta_scratch(size_t rows, float** out);
+
 hipError_t launch_merge_fwd(const MergeArgs& a, hipStream_t s);
 int merge_bwd_partial_rows(int rows, int D);   // number of gq partial vectors
 hipError_t launch_merge_bwd(const MergeArgs& a, hipStream_t s);

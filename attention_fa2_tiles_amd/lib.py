@@ -43,6 +43,7 @@ _SIGNATURES = {
     "fa_fwd_fp8": ([_I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P], _I),
     "fa_bwd_workspace_size": ([_I, _I, _I, _I, _I, _I], _Z),
     "fa_bwd": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _I, _F, _P], _I),
+    "fa_bwd_noalloc": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P], _I),
     "fa_bwd_dlse": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _Z, _I, _I, _I, _I, _I, _I, _F, _P], _I),
     "fa_bwd_delta": ([_I, _P, _P, _P, _P, _I, _I, _I, _I, _P], _I),
     "fa_bwd_dkdv": ([_I, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P], _I),
@@ -144,6 +145,12 @@ def fa_bwd(dtype, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes,
     _check("fa_bwd", load().fa_bwd(dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                                    _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace_bytes,
                                    B, H, M, N, D, int(causal), sm_scale, _stream(stream)))
+
+
+def fa_bwd_noalloc(dtype, q, k, v, o, dout, lse, dq, dk, dv, B, H, M, N, D, causal, sm_scale, stream=None):
+    _check("fa_bwd_noalloc", load().fa_bwd_noalloc(dtype, _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                                   _ptr(dq), _ptr(dk), _ptr(dv), B, H, M, N, D, int(causal),
+                                                   sm_scale, _stream(stream)))
 
 
 def fa_bwd_dlse(dtype, q, k, v, o, dout, lse, dlse, dq, dk, dv, workspace, workspace_bytes,

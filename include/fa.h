@@ -146,6 +146,22 @@ int fa_bwd_dlse(int dtype, const void* q, const void* k, const void* v, const vo
                 void* workspace, size_t workspace_bytes,
                 int B, int H, int M, int N, int D, int causal, float sm_scale, void* stream);
 
+/*
+ * fa_bwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * computation and kernels, with Delta kept in a device array of the library
+ * instead of a caller workspace.  Arguments as fa_bwd without workspace and
+ * workspace_bytes.  B*H*M must not exceed 2^21 rows (the array holds 8 MiB of
+ * fp32; FA_ERR_UNSUPPORTED beyond).  The first call on a device looks the
+ * array's address up once (FA_ERR_HIP if that fails); no call allocates.
+ * Each GPU has one such array, shared by every call on it: calls that overlap
+ * on one GPU (different streams or host threads) race on it and give
+ * undefined results.
+ */
+int fa_bwd_noalloc(int dtype, const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   int B, int H, int M, int N, int D, int causal, float sm_scale, void* stream);
+
 /* The steps of fa_bwd, exposed separately so each can be timed. */
 /* delta [B,H,M] fp32 <- rowsum(o * dout) - dlse (dlse may be NULL)
  * [tutorial: _attn_bwd_preprocess] */

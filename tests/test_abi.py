@@ -119,6 +119,15 @@ def test_bwd_rejects_small_workspace():
     assert status(lib.fa_bwd_dlse, *args) == -5
 
 
+def test_noalloc_backward_rejects():
+    f = lib.fa_bwd_noalloc
+    ok = [2, P[0], P[1], P[2], P[3], P[4], P[5], P[6], P[7], P[8], 1, 2, 128, 128, 64, 1, 0.0]
+    assert status(f, *ok[:7], None, *ok[8:]) == -1                    # dq missing
+    assert status(f, *ok[:10], 1, 1024, 4096, 64, 64, 1, 0.0) == -6   # 2^22 rows: beyond the device array
+    assert status(f, *ok[:14], 24, *ok[15:]) == -6                    # head dim outside the set
+    assert status(f, 9, *ok[1:]) == -3
+
+
 @pytest.mark.parametrize("D", [8, 48, 96, 512])
 def test_head_dims_outside_the_set_rejected(D):
     # every entry point takes D in {16, 32, 64, 128, 256}, the tutorial's set
