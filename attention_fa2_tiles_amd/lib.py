@@ -85,6 +85,8 @@ def load(path=None):
         raise FAError("load", -7, f"{p} is missing; build it with python -m attention_fa2_tiles_amd.build")
     lib = ctypes.CDLL(p)
     for name, (args, res) in _SIGNATURES.items():
+        if path is not None and not hasattr(lib, name):
+            continue  # an explicitly named (e.g. older) build may lack newer entry points
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = res

@@ -245,6 +245,29 @@ def test_large_scale_peaky_softmax():
     compare(wl, t, run_fwd_bwd(wl, t))
 
 
+MANY_WG = [
+    # dtype, B, H, M, N, D, causal, heads checked (None: all)
+    (BF16, 8, 16, 1024, 1024, 128, True, [(0, 0), (3, 7), (7, 15)]),   # 512 workgroups: two rounds per CU
+    (F16, 1, 24, 2816, 512, 64, False, [(0, 0), (0, 13), (0, 23)]),    # heads not a multiple of 8
+    (BF16, 1, 3, 256, 768, 128, True, None),                            # causal with M < N
+    (F16, 2, 5, 512, 512, 64, True, None),
+]
+
+
+@pytest.mark.parametrize("case", MANY_WG, ids=lambda c: "-".join(map(str, c[:7])))
+def test_forward_workgroup_schedules(case):
+    """More workgroups than CUs, head counts that are and are not multiples
+    of 8, causal with M < N: every output finite, the listed heads against
+    the oracle."""
+    dtype, B, H, M, N, D, causal, heads = case
+    wl = AttnWorkload("sched", dtype, B, H, M, N, D, causal, seed=71 + M + H)
+    log(f"forward schedule {case[:7]}")
+    t = attn_inputs(wl, ("q", "k", "v", "do"))
+    got = run_fwd_bwd(wl, t, with_bwd=False, guard=True)
+    assert np.all(np.isfinite(got["o"])) and np.all(np.isfinite(got["lse"]))
+    compare(wl, t, got, heads=heads, with_bwd=False)
+
+
 _FULL = {}
 
 
