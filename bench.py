@@ -494,6 +494,116 @@ def profile_mode(torch):
 
 COPY_BYTES = 256 << 20
 
+# kernel-name fragments (mangled) of the launches profile_mode makes
+PROFILED = {
+    "fwd": ("causal_bf16_b4h16_s2048_d128", "attn_fwd_pipe_kernelIDF16bLi128ELi0ELb1ELb0"),
+    "dq": ("causal_bf16_b4h16_s2048_d128", "attn_dq_kernelIDF16bLi128ELi0ELb1ELb0"),
+    "dkdv": ("causal_bf16_b4h16_s2048_d128", "attn_dkdv_kernelIDF16bLi128ELi0ELb1ELb0"),
+    "merge_fwd": ("merge_bf16_rows32768_d4096", "N_116merge_fwd_kernelIDF16b"),
+    "merge_bwd": ("merge_bf16_rows32768_d4096", "N_116merge_bwd_kernelIDF16b"),
+    "lse_merge_fwd": ("lse_merge_bf16_s4_rows131072_d128", "lse_merge_fwd_kernelIDF16b"),
+    "lse_merge_bwd": ("lse_merge_bf16_s4_rows131072_d128", "lse_merge_bwd_kernelIDF16b"),
+    "copy": (None, "neg"),
+}
+XCDS, SIMDS = 8, 1024   # MI355X: GRBM_GUI_ACTIVE sums its 8 XCDs; 256 CUs x 4 SIMDs
+
+
+def read_counters(dirs):
+    """{key: {counter: [value per dispatch, in dispatch order]}} from the
+    counter_collection csv files of rocprofv3 --pmc runs of profile_mode."""
+    import csv
+    import glob
+    out = {}
+    for d in dirs:
+        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            per = {}
+            with open(f) as fh:
+                for row in csv.DictReader(fh):
+                    key = next((k for k, (_, pat) in PROFILED.items() if pat in row["Kernel_Name"]), None)
+                    if key is None:
+                        continue
+                    i = int(row["Dispatch_Id"])
+                    disp = per.setdefault((key, row["Counter_Name"]), {})
+                    disp[i] = disp.get(i, 0.0) + float(row["Counter_Value"])
+                    per.setdefault((key, "duration_ns"), {})[i] = float(row["End_Timestamp"]) - float(row["Start_Timestamp"])
+            for (key, name), disp in per.items():
+                out.setdefault(key, {})[name] = [disp[i] for i in sorted(disp)]
+    return out
+
+
+def steady(vals):
+    """Mean over dispatches, leaving out the first (cold clocks and caches)
+    when there are several."""
+    v = vals[1:] if len(vals) > 1 else vals
+    return sum(v) / len(v)
+
+
+def summarize_traffic(fetch_dir, write_dir):
+    """Scale FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by what they read
+    for the COPY_BYTES copy, and record HBM bytes per launch, with the digest
+    of each kernel's sources, in profiles/traffic.json."""
+    fetch = {k: steady(c["FETCH_SIZE"]) for k, c in read_counters([fetch_dir]).items() if "FETCH_SIZE" in c}
+    write = {k: steady(c["WRITE_SIZE"]) for k, c in read_counters([write_dir]).items() if "WRITE_SIZE" in c}
+    fs, ws = COPY_BYTES / (fetch["copy"] * 1024), COPY_BYTES / (write["copy"] * 1024)
+    print(f"calibration copy of {COPY_BYTES >> 20} MiB: FETCH_SIZE {fetch['copy']:.0f} KiB, "
+          f"WRITE_SIZE {write['copy']:.0f} KiB -> scale {fs:.4f} (fetch), {ws:.4f} (write)\n")
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            data = json.load(f)
+    print("| kernel | workload | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled HBM MiB / launch |")
+    print("|---|---|---|---|---|")
+    for key, (wl, _) in PROFILED.items():
+        if wl is None or key not in fetch or key not in write:
+            continue
+        b = fetch[key] * 1024 * fs + write[key] * 1024 * ws
+        data.setdefault(wl, {})[key] = {
+            "bytes_per_launch": int(round(b)), "fetch_kib": fetch[key], "write_kib": write[key],
+            "fetch_scale": fs, "write_scale": ws, "source_digest": source_digest(KERNEL_SOURCES[key])}
+        print(f"| {key} | {wl} | {fetch[key]:.0f} | {write[key]:.0f} | {b / 2**20:.1f} |")
+    with open(path, "w") as f:
+        json.dump(data, f, indent=1)
+
+
+def summarize_counters(dirs):
+    """Per kernel, the steady mean of every counter collected, and where the
+    counters are there: GPU cycles (GRBM_GUI_ACTIVE / 8 XCDs) and the clock
+    they imply over the dispatch's duration (duration_ns), the fraction
+    of SIMD-cycles the MFMA pipes were busy, and LDS instructions' share of
+    the waves' active cycles."""
+    data = read_counters(dirs)
+    for key, ctr in data.items():
+        if key == "copy":
+            continue
+        print(f"### {key}\n\n| counter | mean per dispatch |\n|---|---|")
+        for name in sorted(ctr):
+            print(f"| {name} | {steady(ctr[name]):.6g} |")
+        m = {n: steady(v) for n, v in ctr.items()}
+        if "GRBM_GUI_ACTIVE" in m:
+            cyc = m["GRBM_GUI_ACTIVE"] / XCDS
+            print(f"| (derived) GPU cycles per dispatch | {cyc:.6g} |")
+            print(f"| (derived) shader clock, GHz (cycles / dispatch duration) | {cyc / m['duration_ns']:.3f} |")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+                print(f"| (derived) MFMA busy, share of SIMD-cycles | {m['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * SIMDS):.4f} |")
+        if "SQ_LDS_BANK_CONFLICT" in m and "SQ_LDS_IDX_ACTIVE" in m and m["SQ_LDS_IDX_ACTIVE"]:
+            print(f"| (derived) LDS bank-conflict cycles / LDS active cycles | "
+                  f"{m['SQ_LDS_BANK_CONFLICT'] / m['SQ_LDS_IDX_ACTIVE']:.4f} |")
+        print()
+
+
+def summarize_trace(trace_dir):
+    """Markdown table of a rocprofv3 --kernel-trace --stats run's per-kernel
+    durations."""
+    import csv
+    import glob
+    f = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
+    print("| kernel | calls | avg us | min us | max us |\n|---|---|---|---|---|")
+    with open(f) as fh:
+        for row in csv.DictReader(fh):
+            print(f"| `{row['Name'][:100]}` | {row['Calls']} | {float(row['AverageNs']) / 1e3:.1f} | "
+                  f"{float(row['MinNs']) / 1e3:.1f} | {float(row['MaxNs']) / 1e3:.1f} |")
+
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -508,7 +618,22 @@ def main():
     ap.add_argument("--profile", action="store_true",
                     help="counter-collection mode: a few launches of each kernel of the step and of the merge, "
                          "then an elementwise copy of 256 MiB (the byte-count calibration), no timing output")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="host only: turn the FETCH_SIZE and WRITE_SIZE --pmc runs of --profile into "
+                         "profiles/traffic.json and print the table")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="host only: per-kernel table of the --pmc runs of --profile in DIR...")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="host only: per-kernel table of a rocprofv3 --kernel-trace --stats run")
     args = ap.parse_args()
+    if args.summarize_traffic or args.summarize_counters or args.summarize_trace:
+        if args.summarize_traffic:
+            summarize_traffic(*args.summarize_traffic)
+        if args.summarize_counters:
+            summarize_counters(args.summarize_counters)
+        if args.summarize_trace:
+            summarize_trace(args.summarize_trace)
+        return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(attention heads and merge rows would shard across GPUs with no exchange; "
