@@ -38,11 +38,12 @@
  *   attention backward's workspace 4 bytes; the merge backward's workspace
  *   16 bytes.
  * - Supported attention shapes: B, H, M, N >= 1 (any lengths; the kernels
- *   mask the last partial tile); D in {32, 64, 128, 256}, the head dims the
- *   tutorial's Function accepts apart from 16.  D = 256 in fp16/bf16 is
- *   supported by fa_fwd and fa_bwd_delta only (the fused JVP, piecewise
- *   attention and the backward need fp32 there); every other D, or D = 256
- *   on those entry points in fp16/bf16, gives FA_ERR_UNSUPPORTED.
+ *   mask the last partial tile); D in {16, 32, 64, 128, 256}, the head dims
+ *   the tutorial's Function accepts, on every attention entry point and in
+ *   every dtype (fa_fwd_fp8: D in {64, 128}).  16-bit D = 32, 64, 128 run
+ *   on the matrix cores, as does the plain 16-bit forward at D = 256; fp32,
+ *   D = 16 and the other D = 256 calls run a slower kernel without them.
+ *   Any other D gives FA_ERR_UNSUPPORTED.
  *
  * The seven entry points of the hot path (fa_fwd, fa_bwd, fa_fwd_jvp,
  * pw_fwd, pw_bwd, resmerge_fwd, resmerge_bwd) keep the pages' operations
