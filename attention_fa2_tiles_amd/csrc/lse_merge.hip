@@ -17,11 +17,15 @@
 // that the RPW = 64 / LPR rows of a wavefront are read and written as one
 // contiguous run per (input, chunk) instruction.  The S logits of a row are
 // read by its lanes directly (they hit the cache after the first lane).  The
-// backward keeps y and gy in registers, reads each y_s a second time for the
-// dot product gy . (y_s - y) (a cache hit for rows of a few KiB), reduces it
-// over the row's lanes with butterflies, and writes gy_s and glse_s.  Every
-// row is owned by one group of lanes, so nothing is shared between
-// wavefronts and results do not depend on timing.
+// backward keeps y and gy in registers, forms the dot products
+// gy . (y_s - y), reduces them over the row's lanes with butterflies, and
+// writes gy_s and glse_s.  Rows of at most 64 chunks with at most 8 partials
+// (the split-KV combine of attention heads) take kernels that issue every
+// load of the row first and keep the S chunks in registers; wider rows or
+// more partials read each y_s a second time for the dot product (a cache hit
+// for rows of a few KiB, mostly).  Every row is owned by one group of lanes,
+// so nothing is shared between wavefronts and results do not depend on
+// timing.
 #include "common.h"
 #include "kernels.h"
 
@@ -114,6 +118,56 @@ __global__ __launch_bounds__(64 * kLmWaves) void lse_merge_fwd_kernel(const T* _
   if (sub == 0) lse[row] = Z > 0.f ? mx + __logf(Z) : -__builtin_huge_valf();
 }
 
+// The forward for rows of at most 64 chunks and at most SM <= 8 partials:
+// every load of the row is issued before any arithmetic (the general kernel
+// above loads, waits and accumulates one partial at a time).  Same
+// operations in the same order, so the results are bitwise equal.
+template <typename T, int LPR, int SM>
+__global__ __launch_bounds__(64 * kLmWaves) void lse_merge_fwd_small_kernel(const T* __restrict__ ys,
+                                                                            const float* __restrict__ lses,
+                                                                            T* __restrict__ y, float* __restrict__ lse,
+                                                                            int S, int64_t rows, int D) {
+  constexpr int RPW = 64 / LPR;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = ((int64_t)blockIdx.x * kLmWaves + (threadIdx.x >> 6)) * RPW + lane / LPR;
+  const int sub = lane % LPR;
+  const bool has_ch = sub < D / 8;
+  if (row >= rows) return;
+  float ls[SM];
+  Ch8<T> cy[SM];
+#pragma unroll
+  for (int s = 0; s < SM; ++s) {
+    ls[s] = s < S ? lses[s * rows + row] : -__builtin_huge_valf();
+    if (s < S && has_ch) cy[s] = *reinterpret_cast<const Ch8<T>*>(ys + (s * rows + row) * (int64_t)D + sub * 8);
+  }
+  float mx = -__builtin_huge_valf();
+#pragma unroll
+  for (int s = 0; s < SM; ++s)
+    if (s < S) mx = fmaxf(mx, ls[s]);
+  const bool has = mx != -__builtin_huge_valf();
+  float Z = 0.f;
+  if (has) {
+#pragma unroll
+    for (int s = 0; s < SM; ++s)
+      if (s < S) Z += __expf(ls[s] - mx);
+  }
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  if (has && has_ch) {
+    const float inv = 1.f / Z;
+#pragma unroll
+    for (int s = 0; s < SM; ++s)
+      if (s < S) {
+        const float w = __expf(ls[s] - mx) * inv;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, (float)cy[s].e[i], acc[i]);
+      }
+  }
+  if (has_ch) store8(y + row * (int64_t)D + sub * 8, acc);
+  if (sub == 0) lse[row] = has ? mx + __logf(Z) : -__builtin_huge_valf();
+}
+
 template <int LPR>
 __device__ __forceinline__ float row_sum(float x) {
 #pragma unroll
@@ -196,6 +250,86 @@ __global__ __launch_bounds__(64 * kLmWaves) void lse_merge_bwd_kernel(
   }
 }
 
+// The backward for rows of at most 64 chunks (one chunk per lane) and at
+// most SM <= 8 partials: every load of the row (the S chunks, gy, the
+// logits) is issued before any arithmetic, the chunks stay in registers for
+// both the merged y and the dot products (no second read), and the S
+// butterflies run side by side.  Same operations in the same order as
+// lse_merge_bwd_kernel, so the results are bitwise equal.
+template <typename T, int LPR, int SM>
+__global__ __launch_bounds__(64 * kLmWaves) void lse_merge_bwd_small_kernel(
+    const T* __restrict__ ys, const float* __restrict__ lses, const T* __restrict__ gy,
+    const float* __restrict__ gl, T* __restrict__ gys, float* __restrict__ glses, int S, int64_t rows, int D) {
+  constexpr int RPW = 64 / LPR;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = ((int64_t)blockIdx.x * kLmWaves + (threadIdx.x >> 6)) * RPW + lane / LPR;
+  const int sub = lane % LPR;
+  const bool has_ch = sub < D / 8;
+  if (row >= rows) return;
+  float ls[SM];
+  Ch8<T> cy[SM], cg;
+#pragma unroll
+  for (int s = 0; s < SM; ++s) {
+    ls[s] = s < S ? lses[s * rows + row] : -__builtin_huge_valf();
+    if (s < S && has_ch) cy[s] = *reinterpret_cast<const Ch8<T>*>(ys + (s * rows + row) * (int64_t)D + sub * 8);
+  }
+  if (has_ch) cg = *reinterpret_cast<const Ch8<T>*>(gy + row * (int64_t)D + sub * 8);
+  const float glr = gl ? gl[row] : 0.f;
+  float mx = -__builtin_huge_valf();
+#pragma unroll
+  for (int s = 0; s < SM; ++s)
+    if (s < S) mx = fmaxf(mx, ls[s]);
+  const bool has = mx != -__builtin_huge_valf();
+  float Z = 0.f;
+  if (has) {
+#pragma unroll
+    for (int s = 0; s < SM; ++s)
+      if (s < S) Z += __expf(ls[s] - mx);
+  }
+  const float inv = has ? 1.f / Z : 0.f;
+  float w[SM], g[8], yv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    g[i] = has_ch ? (float)cg.e[i] : 0.f;
+    yv[i] = 0.f;
+  }
+#pragma unroll
+  for (int s = 0; s < SM; ++s) w[s] = (has && s < S) ? __expf(ls[s] - mx) * inv : 0.f;
+  if (has && has_ch) {
+#pragma unroll
+    for (int s = 0; s < SM; ++s)
+      if (s < S) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) yv[i] = fmaf(w[s], (float)cy[s].e[i], yv[i]);
+      }
+  }
+  float dot[SM];
+#pragma unroll
+  for (int s = 0; s < SM; ++s) {
+    dot[s] = 0.f;
+    if (has && has_ch && s < S) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dot[s] = fmaf(g[i], (float)cy[s].e[i] - yv[i], dot[s]);
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) {
+#pragma unroll
+    for (int s = 0; s < SM; ++s) dot[s] += __shfl_xor(dot[s], off, 64);
+  }
+#pragma unroll
+  for (int s = 0; s < SM; ++s) {
+    if (s >= S) continue;
+    if (has_ch) {
+      float o[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = w[s] * g[i];
+      store8(gys + (s * rows + row) * (int64_t)D + sub * 8, o);
+    }
+    if (sub == 0) glses[s * rows + row] = w[s] * (glr + dot[s]);
+  }
+}
+
 // Lanes per row and chunks per lane for rows of C chunks: rows of at most
 // 64 chunks take the next power of two of lanes and one chunk each; wider
 // rows take a whole wavefront and up to 8 chunks per lane.
@@ -208,6 +342,56 @@ hipError_t launch_lm(const LseMergeArgs& a, hipStream_t s) {
   const int64_t rpw = 64 / lpr;
   const int64_t rows_per_block = rpw * kLmWaves;
   dim3 grid((unsigned)((a.rows + rows_per_block - 1) / rows_per_block)), block(64 * kLmWaves);
+  if constexpr (!BWD) {
+    if (cpl == 1 && a.S <= 8) {
+#define FA_LM_SMALL(L)                                                                                      \
+  if (lpr == L) {                                                                                           \
+    if (a.S <= 2)                                                                                           \
+      hipLaunchKernelGGL((lse_merge_fwd_small_kernel<T, L, 2>), grid, block, 0, s, (const T*)a.ys, a.lses,  \
+                         (T*)a.y, a.lse, a.S, a.rows, a.D);                                                 \
+    else if (a.S <= 4)                                                                                      \
+      hipLaunchKernelGGL((lse_merge_fwd_small_kernel<T, L, 4>), grid, block, 0, s, (const T*)a.ys, a.lses,  \
+                         (T*)a.y, a.lse, a.S, a.rows, a.D);                                                 \
+    else                                                                                                    \
+      hipLaunchKernelGGL((lse_merge_fwd_small_kernel<T, L, 8>), grid, block, 0, s, (const T*)a.ys, a.lses,  \
+                         (T*)a.y, a.lse, a.S, a.rows, a.D);                                                 \
+    return hipGetLastError();                                                                               \
+  }
+      FA_LM_SMALL(1)
+      FA_LM_SMALL(2)
+      FA_LM_SMALL(4)
+      FA_LM_SMALL(8)
+      FA_LM_SMALL(16)
+      FA_LM_SMALL(32)
+      FA_LM_SMALL(64)
+#undef FA_LM_SMALL
+    }
+  }
+  if constexpr (BWD) {
+    if (cpl == 1 && a.S <= 8) {
+#define FA_LM_SMALL(L)                                                                                      \
+  if (lpr == L) {                                                                                           \
+    if (a.S <= 2)                                                                                           \
+      hipLaunchKernelGGL((lse_merge_bwd_small_kernel<T, L, 2>), grid, block, 0, s, (const T*)a.ys, a.lses,  \
+                         (const T*)a.gy, a.gl, (T*)a.gys, a.glses, a.S, a.rows, a.D);                       \
+    else if (a.S <= 4)                                                                                      \
+      hipLaunchKernelGGL((lse_merge_bwd_small_kernel<T, L, 4>), grid, block, 0, s, (const T*)a.ys, a.lses,  \
+                         (const T*)a.gy, a.gl, (T*)a.gys, a.glses, a.S, a.rows, a.D);                       \
+    else                                                                                                    \
+      hipLaunchKernelGGL((lse_merge_bwd_small_kernel<T, L, 8>), grid, block, 0, s, (const T*)a.ys, a.lses,  \
+                         (const T*)a.gy, a.gl, (T*)a.gys, a.glses, a.S, a.rows, a.D);                       \
+    return hipGetLastError();                                                                               \
+  }
+      FA_LM_SMALL(1)
+      FA_LM_SMALL(2)
+      FA_LM_SMALL(4)
+      FA_LM_SMALL(8)
+      FA_LM_SMALL(16)
+      FA_LM_SMALL(32)
+      FA_LM_SMALL(64)
+#undef FA_LM_SMALL
+    }
+  }
 #define FA_LM_CASE(L, CP)                                                                                   \
   if (lpr == L && cpl <= CP) {                                                                              \
     if constexpr (BWD)                                                                                      \

@@ -145,6 +145,8 @@ LSE_MERGE = [
     (BF16, 2, 300, 4096),   # 64 x 8
     (BF16, 5, 129, 1000),   # 64 x 2, partial last chunk round
     (F16, 8, 333, 8),       # 1 x 1
+    (BF16, 12, 200, 128),   # 16 x 1 with more than 8 inputs (the path that reads them twice)
+    (F32, 7, 90, 512),      # 64 x 1, the widest rows kept in registers
 ]
 
 
