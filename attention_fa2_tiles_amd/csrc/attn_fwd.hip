@@ -72,6 +72,8 @@ struct FwdParams {
   void* to;
   float* tlse;     // may be NULL
   int BH, M, N, nmb;
+  int fold;        // causal: row blocks 0 .. fold-1 of the grid run the longest
+                   // query blocks, longest first; the rest the shortest first
   float scale2;    // sm_scale * log2(e)
   float sm_scale;
   int w;
@@ -126,10 +128,13 @@ void attn_fwd_kernel(const FwdParams p) {
   // Workgroup -> (head, query block).  Heads vary fastest so every query
   // block of one head lands on the same XCD (the dispatcher deals workgroups
   // round-robin over the 8 XCDs and BH is a multiple of 8 in practice), which
-  // keeps that head's K/V in one L2.  Causal: longest query blocks first.
+  // keeps that head's K/V in one L2.  Causal: longest query blocks first;
+  // when the whole grid is resident at once (two workgroups per CU), the
+  // second half runs the shortest first, so that the workgroup dispatched
+  // beside the longest one on a CU is the shortest.
   const int bh = blockIdx.x % p.BH;
   int mb = blockIdx.x / p.BH;
-  if (CAUSAL) mb = p.nmb - 1 - mb;
+  if (CAUSAL) mb = mb < p.fold ? p.nmb - 1 - mb : mb - p.fold;
   const int m0 = mb * kBM;
   const int row0 = m0 + 32 * wave;
   const bool wave_valid = row0 < p.M;
@@ -964,6 +969,15 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
   p.N = a.N;
   const int bm = a.causal ? FwdShape<VAR, D, true>::BM : FwdShape<VAR, D, false>::BM;
   p.nmb = (a.M + bm - 1) / bm;
+  p.fold = p.nmb;
+  if constexpr (FwdShape<VAR, D, true>::kSmall) {
+    // two workgroups per CU: one round when the grid fits twice the CUs
+    int dev = 0, cus = 0;
+    if (a.causal && hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0 &&
+        (int64_t)p.nmb * p.BH <= 2 * (int64_t)cus)
+      p.fold = p.nmb / 2;
+  }
   p.scale2 = a.sm_scale * kLog2e;
   p.sm_scale = a.sm_scale;
   p.w = a.w;
