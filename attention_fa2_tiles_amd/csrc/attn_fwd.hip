@@ -815,16 +815,6 @@ void attn_fwd_pipe_kernel(const FwdParams p) {
       sc[e / 16][e % 16] = exp2_fast(fmaf(sc[e / 16][e % 16], p.scale2, neg_m));
     }
   };
-  // P of a block (already exponentiated in sc) -> packed operands and row sum.
-  auto pack_sum = [&](f32x16 (&sc)[ST], V8 (&pb)[PT]) {
-    float ls = 0.f;
-#pragma unroll
-    for (int t = 0; t < PT; ++t) {
-      pb[t] = pack8<T>(sc[t >> 1], 8 * (t & 1));
-      ls = add_sum8(ls, pb[t]);
-    }
-    l_i += ls;
-  };
   // Lazy rescale after the row max mloc (log2 units) of the next block.
   auto rescale = [&](float mloc) {
     if (__ballot(mloc > m_i + kRescaleSlack) != 0) {
@@ -906,14 +896,21 @@ void attn_fwd_pipe_kernel(const FwdParams p) {
         scores(std::integral_constant<int, SN>{}, jb + 1, sn, [&](auto ic) { exp_step(sc, neg_m, ic); });
       else
         static_for<NR>([&](auto ic) { exp_step(sc, neg_m, ic); });
+      // P of block jb packed into the operands of P V: slice 0 now, slice
+      // t + 1 after product t; the row sum over the packed P after products
+      // PT - 1 .. 2 PT - 2 (same order as a sum right after packing)
       V8 pb[PT];
-      pack_sum(sc, pb);
+      pb[0] = pack8<T>(sc[0], 0);
       if (a_n && needs_mask(jb + 1)) apply_mask(sn, jb + 1);
       // P V of block jb || row max of block jb + 1 (taken whether or not
       // that block is active; only used when it is)
       float mx[2] = {kNegInf, kNegInf};
+      float ls = 0.f;
       pv(stage_c, pb, [&](auto ic) {
         constexpr int I = decltype(ic)::value;
+        if constexpr (I + 1 < PT) pb[I + 1] = pack8<T>(sc[(I + 1) >> 1], 8 * ((I + 1) & 1));
+        if constexpr (I >= PT - 1 && I < 2 * PT - 1) ls = add_sum8(ls, pb[I - (PT - 1)]);
+        if constexpr (I == 2 * PT - 2) l_i += ls;
 #pragma unroll
         for (int u = 0; u < MPP; u += 2) {
           const int e = I * MPP + u;
