@@ -830,24 +830,38 @@ void attn_fwd_pipe_kernel(const FwdParams p) {
     }
   };
   // O^t += V^t P^t for the V tile of stage S; after product i, between(i).
+  // (V^t operands in a rolling window of kVWin: operand i + kVWin is read
+  // right after product i; each operand is two transposing reads, which
+  // complete in issue order)
+  constexpr int kVWin = 3;
   auto pv = [&](auto stage_c, const V8 (&pb)[PT], auto&& between) {
     constexpr int S = decltype(stage_c)::value;
     constexpr int IMM = S * kTileBytes;
-    TrOps<T, PT> va, vb2;
-    va.template issue_imm<D, IMM>(vaddr[0]);
-    va.wait();
-    static_for<DT>([&](auto dc) {
-      constexpr int DTI = decltype(dc)::value;
-      TrOps<T, PT>& cv = (DTI & 1) ? vb2 : va;
-      TrOps<T, PT>& nv = (DTI & 1) ? va : vb2;
-      if constexpr (DTI + 1 < DT) nv.template issue_imm<D, IMM>(vaddr[DTI + 1]);
-      static_for<PT>([&](auto tc) {
-        constexpr int TI = decltype(tc)::value;
-        acc[DTI] = mfma32x32x16(cv.op[TI], pb[TI], acc[DTI]);
-        between(std::integral_constant<int, DTI * PT + TI>{});
-        __builtin_amdgcn_sched_barrier(0);
-      });
-      if constexpr (DTI + 1 < DT) nv.wait();
+    u32x2 vr[NPV][2];
+    auto vread = [&](auto i_c) {
+      constexpr int I = decltype(i_c)::value, DTI = I / PT, TI = I % PT;
+      const uint32_t a0 = vaddr[DTI][0], a1 = vaddr[DTI][1];
+      u32x2 r0, r1;
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r0) : "v"(a0), "i"(IMM + TI * 16 * D * 2));
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r1) : "v"(a1), "i"(IMM + TI * 16 * D * 2));
+      vr[I][0] = r0;
+      vr[I][1] = r1;
+    };
+    static_for<kVWin>([&](auto ic) { vread(ic); });
+    static_for<NPV>([&](auto ic) {
+      constexpr int I = decltype(ic)::value, DTI = I / PT, TI = I % PT;
+      constexpr int AFTER = (NPV - 1 - I < kVWin - 1) ? (NPV - 1 - I) : (kVWin - 1);
+      u32x2 r0 = vr[I][0], r1 = vr[I][1];
+      asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(r0), "+v"(r1) : "n"(2 * AFTER));
+      u32x4 w;
+      w[0] = r0[0];
+      w[1] = r0[1];
+      w[2] = r1[0];
+      w[3] = r1[1];
+      acc[DTI] = mfma32x32x16(__builtin_bit_cast(V8, w), pb[TI], acc[DTI]);
+      if constexpr (I + kVWin < NPV) vread(std::integral_constant<int, I + kVWin>{});
+      between(ic);
+      __builtin_amdgcn_sched_barrier(0);
     });
   };
 
