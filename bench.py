@@ -13,7 +13,9 @@ forward).  The same JSON line carries:
 * ``components``: per-kernel times of the step and the other workloads of
   the hot path -- non-causal bf16 B1 H32 8192 D128, the fused JVP (fp16 B4 H16
   1024 D64, causal and not), piecewise attention (fp16 B2 H16 4096 D64, w =
-  1024) and the residual merge (bf16 32768 x 4096, in HBM GB/s against 8 TB/s);
+  1024), the FP8 forward, head dims 16 and 256 (causal bf16 B1 H16 2048), the
+  residual merge (bf16 32768 x 4096, in HBM GB/s against 8 TB/s) and the
+  N-way merge;
 * ``cpu_baseline``: the fp64 numpy oracle timed on the host on a bounded
   sample of the same workload (a few whole heads).
 
@@ -337,6 +339,44 @@ def bench_pw(torch, timer, iters):
     b_tf = wl.bwd_flops() / (b_ms * 1e-3) / 1e12
     return {"fwd_ms": round(f_ms, 4), "fwd_TFLOP/s": round(f_tf, 2), "bwd_ms": round(b_ms, 4),
             "bwd_TFLOP/s": round(b_tf, 2), "counted_flops": "one QK^T per score"}
+
+
+def bench_head_dims(torch, timer, iters):
+    """The head dims at the ends of the supported range, causal bf16 B1 H16
+    M=N=2048: D = 256 (forward on the matrix cores; backward and fused JVP
+    on the generic vector kernels) and D = 16 (every call on the generic
+    kernels).  Same flop convention as the headline."""
+    from attention_fa2_tiles_amd import lib
+    from attention_fa2_tiles_amd.inputs import BF16, AttnWorkload
+    from attention_fa2_tiles_amd.devbuf import empty, empty_f32
+    out = {}
+    for D in (256, 16):
+        wl = AttnWorkload(f"causal_bf16_b1h16_s2048_d{D}", BF16, 1, 16, 2048, 2048, D, True, seed=6)
+        progress(f"component {wl.name}")
+        names = ("q", "k", "v", "do")
+        _, d = attn_setup(torch, wl, names)
+        b = attn_buffers(torch, wl, d)
+        calls = attn_calls(wl, d, b)
+        B, H, M, N = wl.B, wl.H, wl.M, wl.N
+        to = empty((B, H, M, D), wl.dtype)
+        jvp = lambda: lib.fa_fwd_jvp(wl.dtype, d["q"], d["k"], d["v"], d["q"], d["k"], d["v"], b["o"], b["lse"], to,
+                                     B, H, M, N, D, wl.causal, wl.sm_scale)
+        calls["fwd"]()
+        n = max(3, iters // 4)
+        f_ms = timer.avg_ms(calls["fwd"], n)
+        b_ms = timer.avg_ms(calls["bwd"], n)
+        j_ms = timer.avg_ms(jvp, n)
+        tf = lambda flops, ms: flops / (ms * 1e-3) / 1e12
+        out[f"d{D}"] = {
+            "workload": wl.name,
+            "fwd_ms": round(f_ms, 4), "fwd_TFLOP/s": round(tf(wl.fwd_flops(), f_ms), 2),
+            "bwd_ms": round(b_ms, 4), "bwd_TFLOP/s": round(tf(wl.bwd_flops(), b_ms), 2),
+            "jvp_ms": round(j_ms, 4), "jvp_TFLOP/s": round(tf(3 * wl.fwd_flops(), j_ms), 2),
+            "kernels": "fwd: MFMA; bwd, jvp: generic (vector ALU)" if D == 256 else "generic (vector ALU)",
+        }
+        del d, b, calls, to
+        torch.cuda.empty_cache()
+    return out
 
 
 def bench_merge(torch, timer, iters):
@@ -666,6 +706,7 @@ def main():
         components["jvp_f16_b4h16_s1024_d64"] = bench_jvp(torch, timer, "jvp_f16_b4h16_s1024_d64", iters)
         components["piecewise_f16_b2h16_s4096_d64_w1024"] = bench_pw(torch, timer, iters)
         components["fp8_causal_b4h16_s2048_d128"] = bench_fp8(torch, timer, iters)
+        components["head_dims_causal_bf16_b1h16_s2048"] = bench_head_dims(torch, timer, iters)
         components["merge_bf16_rows32768_d4096"] = bench_merge(torch, timer, iters)
         components["lse_merge_bf16_s4_rows131072_d128"] = bench_lse_merge(torch, timer, iters)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
