@@ -541,8 +541,8 @@ PROFILED = {
     "dkdv": ("causal_bf16_b4h16_s2048_d128", "attn_dkdv_kernelIDF16bLi128ELi0ELb1ELb0"),
     "merge_fwd": ("merge_bf16_rows32768_d4096", "N_116merge_fwd_kernelIDF16b"),
     "merge_bwd": ("merge_bf16_rows32768_d4096", "N_116merge_bwd_kernelIDF16b"),
-    "lse_merge_fwd": ("lse_merge_bf16_s4_rows131072_d128", "lse_merge_fwd_kernelIDF16b"),
-    "lse_merge_bwd": ("lse_merge_bf16_s4_rows131072_d128", "lse_merge_bwd_kernelIDF16b"),
+    "lse_merge_fwd": ("lse_merge_bf16_s4_rows131072_d128", "lse_merge_fwd_small_kernelIDF16b"),
+    "lse_merge_bwd": ("lse_merge_bf16_s4_rows131072_d128", "lse_merge_bwd_small_kernelIDF16b"),
     "copy": (None, "neg"),
 }
 XCDS, SIMDS = 8, 1024   # MI355X: GRBM_GUI_ACTIVE sums its 8 XCDs; 256 CUs x 4 SIMDs
