@@ -551,6 +551,18 @@ void attn_fwd_kernel(const FwdParams p) {
 constexpr int kPipeNS = 4;
 constexpr int kPipeWaves = 8;
 
+// Transposing LDS read as inline asm, completed by an explicit lgkmcnt wait
+// tied to its result (the compiler would otherwise wait for the direct loads
+// of the ring that are still in flight).
+template <int IMM>
+__device__ __forceinline__ void tr_read_imm(std::integral_constant<int, IMM>, uint32_t a, u32x2& r) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(IMM));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait_pair(std::integral_constant<int, N>, u32x2& r0, u32x2& r1) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(r0), "+v"(r1) : "n"(N));
+}
+
 template <typename T, int D, int VAR>
 struct alignas(256) PipeSmem {
   using Tile = DTile<T, kBN, D, kPipeWaves>;
@@ -837,33 +849,32 @@ void attn_fwd_pipe_kernel(const FwdParams p) {
   auto pv = [&](auto stage_c, const V8 (&pb)[PT], auto&& between) {
     constexpr int S = decltype(stage_c)::value;
     constexpr int IMM = S * kTileBytes;
+    // product I: key slice TI = I / DT (P operand), d-tile DTI = I % DT, so
+    // consecutive products feed different accumulators and slice t's P is
+    // first needed by product t * DT
     u32x2 vr[NPV][2];
     auto vread = [&](auto i_c) {
-      constexpr int I = decltype(i_c)::value, DTI = I / PT, TI = I % PT;
-      const uint32_t a0 = vaddr[DTI][0], a1 = vaddr[DTI][1];
-      u32x2 r0, r1;
-      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r0) : "v"(a0), "i"(IMM + TI * 16 * D * 2));
-      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r1) : "v"(a1), "i"(IMM + TI * 16 * D * 2));
-      vr[I][0] = r0;
-      vr[I][1] = r1;
+      constexpr int I = decltype(i_c)::value, DTI = I % DT, TI = I / DT;
+      tr_read_imm(std::integral_constant<int, IMM + TI * 16 * D * 2>{}, vaddr[DTI][0], vr[I][0]);
+      tr_read_imm(std::integral_constant<int, IMM + TI * 16 * D * 2>{}, vaddr[DTI][1], vr[I][1]);
     };
     static_for<kVWin>([&](auto ic) { vread(ic); });
     static_for<NPV>([&](auto ic) {
-      constexpr int I = decltype(ic)::value, DTI = I / PT, TI = I % PT;
+      constexpr int I = decltype(ic)::value, DTI = I % DT, TI = I / DT;
       constexpr int AFTER = (NPV - 1 - I < kVWin - 1) ? (NPV - 1 - I) : (kVWin - 1);
-      u32x2 r0 = vr[I][0], r1 = vr[I][1];
-      asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(r0), "+v"(r1) : "n"(2 * AFTER));
+      lgkm_wait_pair(std::integral_constant<int, 2 * AFTER>{}, vr[I][0], vr[I][1]);
       u32x4 w;
-      w[0] = r0[0];
-      w[1] = r0[1];
-      w[2] = r1[0];
-      w[3] = r1[1];
+      w[0] = vr[I][0][0];
+      w[1] = vr[I][0][1];
+      w[2] = vr[I][1][0];
+      w[3] = vr[I][1][1];
       acc[DTI] = mfma32x32x16(__builtin_bit_cast(V8, w), pb[TI], acc[DTI]);
       if constexpr (I + kVWin < NPV) vread(std::integral_constant<int, I + kVWin>{});
       between(ic);
       __builtin_amdgcn_sched_barrier(0);
     });
   };
+
 
   // Prologue: blocks 0, 1, 2 are issued right behind the query operands;
   // blocks 0 and 1 (and the query operands) have landed; the scores of
