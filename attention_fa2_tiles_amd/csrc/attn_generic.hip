@@ -8,11 +8,13 @@
 // online-softmax forward and recompute backward, the JVP recurrences of its
 // ENABLE_JVP path, FlagAttention's piecewise score selection -- in fp32, with
 // P (and P * Sdot, dS) rounded to the storage dtype before the products that
-// consume them, as the 16-bit kernels do (a no-op for fp32).  One wavefront
-// owns one query row (forward, dQ) or one key row (dK/dV): lane l holds
-// head-dimension elements l, l + 64, ... (E of them; for D < 64 the lanes
-// past D hold none) and every dot product is a butterfly reduction across
-// the wavefront.  It is correct for any shape, not fast: the large 16-bit
+// consume them, as the 16-bit kernels do (a no-op for fp32).  A group of RL
+// lanes (RL = min(D, 64), at least 16) owns one query row (forward, dQ) or
+// one key row (dK/dV), so a wavefront holds 64 / RL rows; lane l of a group
+// holds head-dimension elements l, l + RL, ..., every dot product is a
+// butterfly reduction across the group, and keys (or queries) are taken
+// four at a time: four independent reductions, one online-softmax rescale
+// per four keys.  Correct for any shape, not fast: the large 16-bit
 // workloads run on the MFMA kernels.
 #include "common.h"
 #include "kernels.h"
@@ -20,31 +22,47 @@
 namespace fa {
 namespace {
 
-__device__ __forceinline__ float wave_sum(float x) {
+__device__ __forceinline__ bool near_pair(int dist, int w) { return dist <= w && dist >= -w; }
+
+// Lanes per row and elements per lane.
+template <int D>
+constexpr int row_lanes() {
+  return D >= 64 ? 64 : (D >= 32 ? 32 : 16);
+}
+template <int D>
+constexpr int per_lane() {
+  return D / row_lanes<D>();
+}
+constexpr int kChunk = 4;  // keys (or queries) per step
+
+// Sum over the RL lanes of this lane's group.
+template <int RL>
+__device__ __forceinline__ float group_sum(float x) {
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  for (int off = RL / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+// Maximum / minimum over the whole wavefront (a loop bound its groups share).
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = max(x, __shfl_xor(x, off, 64));
+  return x;
+}
+__device__ __forceinline__ int wave_min(int x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = min(x, __shfl_xor(x, off, 64));
   return x;
 }
 
-__device__ __forceinline__ bool near_pair(int dist, int w) { return dist <= w && dist >= -w; }
-
-// Head-dimension elements per lane, and whether lane holds element
-// lane + 64 e of a row of D (rows of 32 leave the upper half-wave idle).
-template <int D>
-constexpr int elems() {
-  return (D + 63) / 64;
-}
-template <int D>
-__device__ __forceinline__ bool has_col(int lane, int e) {
-  return D % 64 == 0 || lane + 64 * e < D;
+template <int D, typename T>
+__device__ __forceinline__ void load_row(const T* p, int sl, float (&x)[per_lane<D>()]) {
+#pragma unroll
+  for (int e = 0; e < per_lane<D>(); ++e) x[e] = (float)p[sl + row_lanes<D>() * e];
 }
 template <int D, typename T>
-__device__ __forceinline__ float ld_col(const T* p, int lane, int e) {
-  return has_col<D>(lane, e) ? (float)p[lane + 64 * e] : 0.f;
-}
-template <int D, typename T>
-__device__ __forceinline__ void st_col(T* p, int lane, int e, float v) {
-  if (has_col<D>(lane, e)) p[lane + 64 * e] = (T)v;
+__device__ __forceinline__ void store_row(T* p, int sl, const float (&x)[per_lane<D>()], float scale) {
+#pragma unroll
+  for (int e = 0; e < per_lane<D>(); ++e) p[sl + row_lanes<D>() * e] = (T)(x[e] * scale);
 }
 
 // x rounded to the storage dtype and back (the operand precision of the
@@ -54,172 +72,215 @@ __device__ __forceinline__ float rnd(float x) {
   return (float)(T)x;
 }
 
-template <int D, int E, typename T>
-__device__ __forceinline__ float dot_row(const float (&a)[E], const T* b, int lane) {
+// This lane's part of a . (row b) (the caller takes the group sum).
+template <int D, typename T>
+__device__ __forceinline__ float dot_part(const float (&a)[per_lane<D>()], const T* b, int sl) {
   float s = 0.f;
 #pragma unroll
-  for (int e = 0; e < E; ++e) s += a[e] * ld_col<D>(b, lane, e);
-  return wave_sum(s);
+  for (int e = 0; e < per_lane<D>(); ++e) s = fmaf(a[e], (float)b[sl + row_lanes<D>() * e], s);
+  return s;
 }
 
-// One wave per query row.
+// A group per query row.
 template <typename T, int D, int VAR>
 __global__ __launch_bounds__(256) void fwd_gen_kernel(FwdArgs a, float scale, int64_t rows) {
-  constexpr int E = elems<D>();
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  constexpr int RL = row_lanes<D>(), E = per_lane<D>(), RPW = 64 / RL;
+  const int lane = threadIdx.x & 63, sl = lane % RL;
+  const int64_t row_raw = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / RL;
+  const bool valid = row_raw < rows;
+  const int64_t row = valid ? row_raw : rows - 1;  // (a clamped row computes, never stores)
   const int bh = (int)(row / a.M), i = (int)(row % a.M);
   const int pshift = a.N - a.M;
   const int64_t qoff = row * D, kbase = (int64_t)bh * a.N * D;
-  const T* Q = (const T*)a.q + qoff;
   float q[E], q2[E], tq[E], acc[E], accg[E];
+  load_row<D>((const T*)a.q + qoff, sl, q);
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    q[e] = ld_col<D>(Q, lane, e);
-    q2[e] = VAR == PW ? ld_col<D>((const T*)a.q2 + qoff, lane, e) : 0.f;
-    tq[e] = VAR == JVP ? ld_col<D>((const T*)a.tq + qoff, lane, e) : 0.f;
-    acc[e] = 0.f;
-    accg[e] = 0.f;
-  }
+  for (int e = 0; e < E; ++e) q2[e] = tq[e] = acc[e] = accg[e] = 0.f;
+  if (VAR == PW) load_row<D>((const T*)a.q2 + qoff, sl, q2);
+  if (VAR == JVP) load_row<D>((const T*)a.tq + qoff, sl, tq);
   float m = kNegInf, l = 0.f, mu = 0.f;
-  const int jend = a.causal ? min(a.N, i + pshift + 1) : a.N;
-  for (int j = 0; j < jend; ++j) {
-    const int64_t ko = kbase + (int64_t)j * D;
-    float s;
-    if (VAR == PW && !near_pair(i + pshift - j, a.w))
-      s = dot_row<D>(q2, (const T*)a.k2 + ko, lane) * scale;
-    else
-      s = dot_row<D>(q, (const T*)a.k + ko, lane) * scale;
-    const float m_new = fmaxf(m, s);
-    const float alpha = expf(m - m_new);  // m = -inf on the first key -> 0
-    const float pv = rnd<T>(expf(s - m_new));
-    l = alpha * l + pv;
-    const T* V = (const T*)a.v + ko;
-    if (VAR == JVP) {
-      const float sd = dot_row<D>(tq, (const T*)a.k + ko, lane) + dot_row<D>(q, (const T*)a.tk + ko, lane);
-      const float ps = pv * sd * scale;
-      mu = alpha * mu + ps;
-      const float psr = rnd<T>(ps);
-      const T* TV = (const T*)a.tv + ko;
+  const int jend = a.causal ? max(0, min(a.N, i + pshift + 1)) : a.N;
+  const int jmax = wave_max(jend);
+  for (int j0 = 0; j0 < jmax; j0 += kChunk) {
+    float sc[kChunk], sd[kChunk];
+    const T* vr[kChunk];
+    const T* tvr[kChunk];
 #pragma unroll
-      for (int e = 0; e < E; ++e) accg[e] = alpha * accg[e] + psr * ld_col<D>(V, lane, e) + pv * ld_col<D>(TV, lane, e);
+    for (int c = 0; c < kChunk; ++c) {
+      const int j = j0 + c;
+      const int jc = j < a.N ? j : a.N - 1;  // (addresses stay inside the keys)
+      const int64_t ko = kbase + (int64_t)jc * D;
+      vr[c] = (const T*)a.v + ko;
+      tvr[c] = VAR == JVP ? (const T*)a.tv + ko : vr[c];
+      const bool far = VAR == PW && !near_pair(i + pshift - j, a.w);
+      const float part = far ? dot_part<D>(q2, (const T*)a.k2 + ko, sl) : dot_part<D>(q, (const T*)a.k + ko, sl);
+      sc[c] = group_sum<RL>(part);
+      sd[c] = 0.f;
+      if (VAR == JVP)
+        sd[c] = group_sum<RL>(dot_part<D>(tq, (const T*)a.k + ko, sl) + dot_part<D>(q, (const T*)a.tk + ko, sl));
+      sc[c] = j < jend ? sc[c] * scale : kNegInf;
+    }
+    float m_new = m;
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) m_new = fmaxf(m_new, sc[c]);
+    if (m_new == kNegInf) continue;  // nothing visible yet in this row
+    const float alpha = expf(m - m_new);  // m = -inf -> 0
+    l *= alpha;
+    mu *= alpha;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      acc[e] *= alpha;
+      accg[e] *= alpha;
     }
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = alpha * acc[e] + pv * ld_col<D>(V, lane, e);
+    for (int c = 0; c < kChunk; ++c) {
+      const float pv = rnd<T>(expf(sc[c] - m_new));  // a masked key: exp(-inf) = 0
+      l += pv;
+      if (VAR == JVP) {
+        const float ps = sc[c] == kNegInf ? 0.f : pv * sd[c] * scale;
+        mu += ps;
+        const float psr = rnd<T>(ps);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          accg[e] += psr * (float)vr[c][sl + RL * e] + pv * (float)tvr[c][sl + RL * e];
+      }
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = fmaf(pv, (float)vr[c][sl + RL * e], acc[e]);
+    }
     m = m_new;
   }
+  if (!valid) return;
   const bool has = l > 0.f;
   const float inv = has ? 1.f / l : 0.f;
-  T* O = (T*)a.o + qoff;
-#pragma unroll
-  for (int e = 0; e < E; ++e) st_col<D>(O, lane, e, acc[e] * inv);
-  if (lane == 0) a.lse[row] = has ? m + logf(l) : kNegInf;
+  store_row<D>((T*)a.o + qoff, sl, acc, inv);
+  if (sl == 0) a.lse[row] = has ? m + logf(l) : kNegInf;
   if (VAR == JVP) {
-    T* TO = (T*)a.to + qoff;
     const float c = mu * inv;
+    float tv[E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) st_col<D>(TO, lane, e, (accg[e] - c * acc[e]) * inv);
+    for (int e = 0; e < E; ++e) tv[e] = accg[e] - c * acc[e];
+    store_row<D>((T*)a.to + qoff, sl, tv, inv);
     // LSE tangent: sum_j P_ij Sdot_ij (0 for a row with no visible key)
-    if (lane == 0 && a.tlse) a.tlse[row] = c;
+    if (sl == 0 && a.tlse) a.tlse[row] = c;
   }
 }
 
-// One wave per query row: dQ (piecewise: dQ1 and dQ2).
+// A group per query row: dQ (piecewise: dQ1 and dQ2).
 template <typename T, int D, int VAR>
 __global__ __launch_bounds__(256) void dq_gen_kernel(BwdArgs a, int64_t rows) {
-  constexpr int E = elems<D>();
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  constexpr int RL = row_lanes<D>(), E = per_lane<D>(), RPW = 64 / RL;
+  const int lane = threadIdx.x & 63, sl = lane % RL;
+  const int64_t row_raw = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / RL;
+  const bool valid = row_raw < rows;
+  const int64_t row = valid ? row_raw : rows - 1;
   const int bh = (int)(row / a.M), i = (int)(row % a.M);
   const int pshift = a.N - a.M;
   const int64_t qoff = row * D, kbase = (int64_t)bh * a.N * D;
   float q[E], q2[E], dO[E], dq[E], dq2[E];
+  load_row<D>((const T*)a.q + qoff, sl, q);
+  load_row<D>((const T*)a.dout + qoff, sl, dO);
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    q[e] = ld_col<D>((const T*)a.q + qoff, lane, e);
-    q2[e] = VAR == PW ? ld_col<D>((const T*)a.q2 + qoff, lane, e) : 0.f;
-    dO[e] = ld_col<D>((const T*)a.dout + qoff, lane, e);
-    dq[e] = 0.f;
-    dq2[e] = 0.f;
-  }
+  for (int e = 0; e < E; ++e) q2[e] = dq[e] = dq2[e] = 0.f;
+  if (VAR == PW) load_row<D>((const T*)a.q2 + qoff, sl, q2);
   const float lse = a.lse[row], dl = a.delta[row];
-  const int jend = (lse == kNegInf) ? 0 : (a.causal ? min(a.N, i + pshift + 1) : a.N);
-  for (int j = 0; j < jend; ++j) {
-    const int64_t ko = kbase + (int64_t)j * D;
-    const bool far = VAR == PW && !near_pair(i + pshift - j, a.w);
-    const T* Kr = far ? (const T*)a.k2 + ko : (const T*)a.k + ko;
-    const float s = dot_row<D>(far ? q2 : q, Kr, lane) * a.sm_scale;
-    const float pv = expf(s - lse);
-    const float dp = dot_row<D>(dO, (const T*)a.v + ko, lane);
-    const float ds = rnd<T>(pv * (dp - dl));
+  const int jend = (lse == kNegInf) ? 0 : (a.causal ? max(0, min(a.N, i + pshift + 1)) : a.N);
+  const int jmax = wave_max(jend);
+  for (int j0 = 0; j0 < jmax; j0 += kChunk) {
+    float ds[kChunk];
+    bool far[kChunk];
+    const T* kr[kChunk];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      if (far)
-        dq2[e] += ds * ld_col<D>(Kr, lane, e);
-      else
-        dq[e] += ds * ld_col<D>(Kr, lane, e);
+    for (int c = 0; c < kChunk; ++c) {
+      const int j = j0 + c;
+      const int jc = j < a.N ? j : a.N - 1;
+      const int64_t ko = kbase + (int64_t)jc * D;
+      far[c] = VAR == PW && !near_pair(i + pshift - j, a.w);
+      kr[c] = far[c] ? (const T*)a.k2 + ko : (const T*)a.k + ko;
+      const float s = group_sum<RL>(dot_part<D>(far[c] ? q2 : q, kr[c], sl)) * a.sm_scale;
+      const float dp = group_sum<RL>(dot_part<D>(dO, (const T*)a.v + ko, sl));
+      ds[c] = j < jend ? rnd<T>(expf(s - lse) * (dp - dl)) : 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float kv = (float)kr[c][sl + RL * e];
+        if (VAR == PW && far[c])
+          dq2[e] = fmaf(ds[c], kv, dq2[e]);
+        else
+          dq[e] = fmaf(ds[c], kv, dq[e]);
+      }
     }
   }
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    st_col<D>((T*)a.dq + qoff, lane, e, dq[e] * a.sm_scale);
-    if (VAR == PW) st_col<D>((T*)a.dq2 + qoff, lane, e, dq2[e] * a.sm_scale);
-  }
+  if (!valid) return;
+  store_row<D>((T*)a.dq + qoff, sl, dq, a.sm_scale);
+  if (VAR == PW) store_row<D>((T*)a.dq2 + qoff, sl, dq2, a.sm_scale);
 }
 
-// One wave per key row: dK, dV (piecewise: dK1, dK2, dV).
+// A group per key row: dK, dV (piecewise: dK1, dK2, dV).
 template <typename T, int D, int VAR>
 __global__ __launch_bounds__(256) void dkdv_gen_kernel(BwdArgs a, int64_t rows) {
-  constexpr int E = elems<D>();
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  constexpr int RL = row_lanes<D>(), E = per_lane<D>(), RPW = 64 / RL;
+  const int lane = threadIdx.x & 63, sl = lane % RL;
+  const int64_t row_raw = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / RL;
+  const bool valid = row_raw < rows;
+  const int64_t row = valid ? row_raw : rows - 1;
   const int bh = (int)(row / a.N), j = (int)(row % a.N);
   const int pshift = a.N - a.M;
   const int64_t koff = row * D, qbase = (int64_t)bh * a.M * D, lbase = (int64_t)bh * a.M;
   float k[E], k2[E], v[E], dk[E], dk2[E], dv[E];
+  load_row<D>((const T*)a.k + koff, sl, k);
+  load_row<D>((const T*)a.v + koff, sl, v);
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    k[e] = ld_col<D>((const T*)a.k + koff, lane, e);
-    k2[e] = VAR == PW ? ld_col<D>((const T*)a.k2 + koff, lane, e) : 0.f;
-    v[e] = ld_col<D>((const T*)a.v + koff, lane, e);
-    dk[e] = dk2[e] = dv[e] = 0.f;
-  }
-  const int ibeg = a.causal ? max(0, j - pshift) : 0;
-  for (int i = ibeg; i < a.M; ++i) {
-    const int64_t qo = qbase + (int64_t)i * D;
-    const float lse = a.lse[lbase + i];
-    const bool far = VAR == PW && !near_pair(i + pshift - j, a.w);
-    const T* Qr = far ? (const T*)a.q2 + qo : (const T*)a.q + qo;
-    const float s = dot_row<D>(far ? k2 : k, Qr, lane) * a.sm_scale;
-    const float pv = (lse == kNegInf) ? 0.f : expf(s - lse);
-    const T* dOr = (const T*)a.dout + qo;
-    const float dp = dot_row<D>(v, dOr, lane);
-    const float ds = rnd<T>(pv * (dp - a.delta[lbase + i]));
-    const float pr = rnd<T>(pv);
+  for (int e = 0; e < E; ++e) k2[e] = dk[e] = dk2[e] = dv[e] = 0.f;
+  if (VAR == PW) load_row<D>((const T*)a.k2 + koff, sl, k2);
+  const int ibeg = a.causal ? min(a.M, max(0, j - pshift)) : 0;
+  const int imin = wave_min(ibeg) / kChunk * kChunk;
+  for (int i0 = imin; i0 < a.M; i0 += kChunk) {
+    float ds[kChunk], pr[kChunk];
+    bool far[kChunk];
+    const T* qr[kChunk];
+    const T* dor[kChunk];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      dv[e] += pr * ld_col<D>(dOr, lane, e);
-      if (far)
-        dk2[e] += ds * ld_col<D>(Qr, lane, e);
-      else
-        dk[e] += ds * ld_col<D>(Qr, lane, e);
+    for (int c = 0; c < kChunk; ++c) {
+      const int i = i0 + c;
+      const int ii = i < a.M ? i : a.M - 1;
+      const int64_t qo = qbase + (int64_t)ii * D;
+      const float lse = a.lse[lbase + ii];
+      far[c] = VAR == PW && !near_pair(i + pshift - j, a.w);
+      qr[c] = far[c] ? (const T*)a.q2 + qo : (const T*)a.q + qo;
+      dor[c] = (const T*)a.dout + qo;
+      const float s = group_sum<RL>(dot_part<D>(far[c] ? k2 : k, qr[c], sl)) * a.sm_scale;
+      const float dp = group_sum<RL>(dot_part<D>(v, dor[c], sl));
+      const bool on = i >= ibeg && i < a.M && lse != kNegInf;
+      const float pv = on ? expf(s - lse) : 0.f;
+      ds[c] = rnd<T>(pv * (dp - a.delta[lbase + ii]));
+      pr[c] = rnd<T>(pv);
+    }
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        dv[e] = fmaf(pr[c], (float)dor[c][sl + RL * e], dv[e]);
+        const float qv = (float)qr[c][sl + RL * e];
+        if (VAR == PW && far[c])
+          dk2[e] = fmaf(ds[c], qv, dk2[e]);
+        else
+          dk[e] = fmaf(ds[c], qv, dk[e]);
+      }
     }
   }
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    st_col<D>((T*)a.dv + koff, lane, e, dv[e]);
-    st_col<D>((T*)a.dk + koff, lane, e, dk[e] * a.sm_scale);
-    if (VAR == PW) st_col<D>((T*)a.dk2 + koff, lane, e, dk2[e] * a.sm_scale);
-  }
+  if (!valid) return;
+  store_row<D>((T*)a.dv + koff, sl, dv, 1.f);
+  store_row<D>((T*)a.dk + koff, sl, dk, a.sm_scale);
+  if (VAR == PW) store_row<D>((T*)a.dk2 + koff, sl, dk2, a.sm_scale);
 }
 
 template <typename T, int D>
 hipError_t fwd_e(const FwdArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.B * a.H * a.M;
-  dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  constexpr int RPB = 4 * (64 / row_lanes<D>());  // rows per workgroup
+  dim3 grid((unsigned)((rows + RPB - 1) / RPB)), block(256);
   switch (a.variant) {
     case PLAIN: hipLaunchKernelGGL((fwd_gen_kernel<T, D, PLAIN>), grid, block, 0, s, a, a.sm_scale, rows); break;
     case JVP: hipLaunchKernelGGL((fwd_gen_kernel<T, D, JVP>), grid, block, 0, s, a, a.sm_scale, rows); break;
@@ -232,7 +293,8 @@ hipError_t fwd_e(const FwdArgs& a, hipStream_t s) {
 template <typename T, int D>
 hipError_t dq_e(const BwdArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.B * a.H * a.M;
-  dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  constexpr int RPB = 4 * (64 / row_lanes<D>());
+  dim3 grid((unsigned)((rows + RPB - 1) / RPB)), block(256);
   if (a.variant == PW)
     hipLaunchKernelGGL((dq_gen_kernel<T, D, PW>), grid, block, 0, s, a, rows);
   else
@@ -243,7 +305,8 @@ hipError_t dq_e(const BwdArgs& a, hipStream_t s) {
 template <typename T, int D>
 hipError_t dkdv_e(const BwdArgs& a, hipStream_t s) {
   const int64_t rows = (int64_t)a.B * a.H * a.N;
-  dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  constexpr int RPB = 4 * (64 / row_lanes<D>());
+  dim3 grid((unsigned)((rows + RPB - 1) / RPB)), block(256);
   if (a.variant == PW)
     hipLaunchKernelGGL((dkdv_gen_kernel<T, D, PW>), grid, block, 0, s, a, rows);
   else
