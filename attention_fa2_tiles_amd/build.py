@@ -22,7 +22,13 @@ SOURCES = ["attn_fwd.hip", "attn_fwd_fp8.hip", "attn_bwd.hip", "attn_generic.hip
            "noalloc.hip", "api.cpp"]
 # Sources compiled in several parts (each part instantiates a share of the
 # kernels, selected by a macro), so the parts compile in parallel.
-PARTS = {"attn_bwd.hip": ("FA_BWD_PART", 5), "attn_fwd.hip": ("FA_FWD_PART", 3)}
+PARTS = {"attn_bwd.hip": ("FA_BWD_PART", 9), "attn_fwd.hip": ("FA_FWD_PART", 5)}
+# MFMA results in VGPRs: keeps loop-carried accumulators from being copied
+# between AGPRs and VGPRs on every iteration.  Every unit but the parts
+# listed in AGPR_PARTS, whose kernels run one wave per SIMD with more
+# accumulator registers than the 256 VGPRs (the D = 256 backward passes).
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+AGPR_PARTS = {"attn_bwd.hip": {5, 6, 7, 8}}
 
 
 def units():
@@ -31,9 +37,11 @@ def units():
     for src in SOURCES:
         if src in PARTS:
             macro, n = PARTS[src]
-            out += [(src, [f"-D{macro}={i}"], f"{src}.part{i}.o") for i in range(n)]
+            for i in range(n):
+                form = [] if i in AGPR_PARTS.get(src, ()) else VGPR_FORM
+                out.append((src, [f"-D{macro}={i}"] + form, f"{src}.part{i}.o"))
         else:
-            out.append((src, [], src + ".o"))
+            out.append((src, list(VGPR_FORM), src + ".o"))
     return out
 ARCH = "gfx950"
 
@@ -54,9 +62,6 @@ def compile_flags():
         "-Wall",
         "-Wno-unused-function",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        # MFMA results in VGPRs: keeps loop-carried accumulators from being
-        # copied between AGPRs and VGPRs on every iteration
-        "-mllvm", "-amdgpu-mfma-vgpr-form=1",
         f"-I{os.path.join(os.path.dirname(PKG), 'include')}",
     ]
 

@@ -82,11 +82,12 @@ int run_fwd(FwdArgs& a, hipStream_t s) {
                                                               : fa::launch_attn_fwd(a, s));
 }
 
-// The whole backward.  MFMA path (16-bit, D in {32, 64, 128}): the dQ pass
+// The whole backward.  MFMA path (16-bit, D in {32, 64, 128}, and plain
+// attention at D = 256): the dQ pass
 // forms Delta itself and writes it for the dK/dV pass that follows (two
 // launches); generic path: the Delta kernel, then the two passes.
 int run_bwd(BwdArgs& a, const void* o, const float* dlse, float* delta, hipStream_t s) {
-  if (fa::bwd_generic(a.dtype, a.D)) {
+  if (fa::bwd_generic(a.dtype, a.variant, a.D)) {
     FA_TRY(hip_status(fa::launch_attn_delta(a.dtype, o, a.dout, dlse, delta, (int64_t)a.B * a.H * a.M, a.D, s)));
     a.delta = delta;
     FA_TRY(hip_status(fa::launch_attn_dkdv_generic(a, s)));
@@ -106,7 +107,7 @@ int run_bwd(BwdArgs& a, const void* o, const float* dlse, float* delta, hipStrea
 // One pass of the backward (dK/dV or dQ) reading a given Delta.
 int run_bwd_pass(BwdArgs& a, const float* delta, hipStream_t s, bool dkdv) {
   a.delta = delta;
-  const bool gen = fa::bwd_generic(a.dtype, a.D);
+  const bool gen = fa::bwd_generic(a.dtype, a.variant, a.D);
   if (dkdv) return hip_status(gen ? fa::launch_attn_dkdv_generic(a, s) : fa::launch_attn_dkdv(a, s));
   return hip_status(gen ? fa::launch_attn_dq_generic(a, s) : fa::launch_attn_dq(a, s));
 }
@@ -364,7 +365,7 @@ int fa_bwd_dq_delta(int dtype, const void* q, const void* k, const void* v, cons
   a.causal = causal;
   a.sm_scale = scale;
   hipStream_t s = (hipStream_t)stream;
-  if (fa::bwd_generic(dtype, D)) {
+  if (fa::bwd_generic(dtype, fa::PLAIN, D)) {
     FA_TRY(hip_status(fa::launch_attn_delta(dtype, o, dout, dlse, delta, (int64_t)B * H * M, D, s)));
     a.delta = delta;
     return hip_status(fa::launch_attn_dq_generic(a, s));

@@ -38,6 +38,15 @@
 #include "kernels.h"
 
 namespace fa {
+
+// The 16-bit D = 256 passes, in translation units of their own: one wave per
+// SIMD with the accumulators in AGPRs (the other units keep MFMA results in
+// VGPRs).
+hipError_t bwd_dkdv_d256_f16(const BwdArgs& a, hipStream_t s);
+hipError_t bwd_dkdv_d256_bf16(const BwdArgs& a, hipStream_t s);
+hipError_t bwd_dq_d256_f16(const BwdArgs& a, hipStream_t s);
+hipError_t bwd_dq_d256_bf16(const BwdArgs& a, hipStream_t s);
+
 namespace {
 
 constexpr int kLdsBytes = kBwdLdsBytes;
@@ -96,12 +105,16 @@ hipError_t launch_delta_t(const void* o, const void* dout, const float* dlse, fl
 template <int D, int VAR>
 struct DkdvShape {
   // D = 32 tiles are too small to split their loads over 8 waves; the
-  // piecewise operand pairs fit 8 waves' registers only up to D = 64
-  static constexpr int WAVES = ((VAR == PW && D > 64) || D == 32) ? 4 : 8;
+  // piecewise operand pairs fit 8 waves' registers only up to D = 64.
+  // D = 256: the dV / dK accumulators alone take 256 registers, so one wave
+  // per SIMD holds them (in AGPRs), and the ring has two stages (three
+  // stages of 32 x 256 Q and dO tiles and the four waves' V rows would need
+  // 160.75 KiB).
+  static constexpr int WAVES = ((VAR == PW && D > 64) || D == 32 || D == 256) ? 4 : 8;
   static constexpr int NT = 64 * WAVES;
   static constexpr int KB = 32 * WAVES;                        // keys per workgroup
   static constexpr int QB = (D == 64 || D == 32) ? 64 : 32;    // query rows per streamed block
-  static constexpr int NS = 3;                    // ring stages
+  static constexpr int NS = D == 256 ? 2 : 3;                  // ring stages
 };
 
 template <typename T, int D, int VAR>
@@ -153,7 +166,7 @@ void attn_dkdv_kernel(const BwdParams p) {
   constexpr int PT = QB / 16;  // 16-query operand slices per block
   constexpr bool kPw = VAR == PW;
   static_assert(sizeof(Sm) <= kLdsBytes, "LDS budget");
-  static_assert(NS == 3, "the ring loop is unrolled by three");
+  static_assert(NS == 2 || NS == 3, "ring of two or three stages");
 
   __shared__ Sm smem;
 
@@ -268,9 +281,12 @@ void attn_dkdv_kernel(const BwdParams p) {
     return n;
   };
   // Wait until the loads of every block but the newest (n instructions)
-  // have landed.
+  // have landed.  (Two stages: the newest block is the one needed next, so
+  // every load is waited for.)
   auto wait_all_but = [&](int n) {
-    if constexpr (kPw)
+    if constexpr (NS == 2)
+      wait_vmcnt0();
+    else if constexpr (kPw)
       wait_vmcnt_any<3 * Dma::PER_WAVE + 1, 2 * Dma::PER_WAVE + 1>(n);
     else
       wait_vmcnt<2 * Dma::PER_WAVE + 1>();
@@ -410,16 +426,22 @@ void attn_dkdv_kernel(const BwdParams p) {
       } else {
         asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(xo[k & 1].op[0]), "+v"(yo[k & 1].op[0]));
       }
-      // elements of slot t + 1 placed after this step's two products
+      // elements of slot t + 1 placed after this step's two products (D =
+      // 256: one after each of the first eight products)
       constexpr int e0 = 2 * dt * kPer;
       dvt[dt] = mfma32x32x16(xo[k & 1].op[0], pb[t], dvt[dt]);
       if constexpr (t + 1 < PT) {
-        static_for<kPer>([&](auto uc) { element(ic<t + 1>{}, ic<e0 + decltype(uc)::value>{}); });
+        static_for<kPer>([&](auto uc) {
+          if constexpr (e0 + decltype(uc)::value < 8) element(ic<t + 1>{}, ic<e0 + decltype(uc)::value>{});
+        });
       }
       __builtin_amdgcn_sched_barrier(0);
       dks[dt] = mfma32x32x16(yo[k & 1].op[0], dsb[t], dks[dt]);
       if constexpr (t + 1 < PT) {
-        static_for<kPer>([&](auto uc) { element(ic<t + 1>{}, ic<e0 + kPer + decltype(uc)::value>{}); });
+        static_for<kPer>([&](auto uc) {
+          if constexpr (e0 + kPer + decltype(uc)::value < 8)
+            element(ic<t + 1>{}, ic<e0 + kPer + decltype(uc)::value>{});
+        });
       }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -472,9 +494,9 @@ void attn_dkdv_kernel(const BwdParams p) {
     lds_barrier();
   };
   for (int qb = 0; qb < nq; qb += NS) {
-    step(ic<0>{}, qb);
-    if (qb + 1 < nq) step(ic<1>{}, qb + 1);
-    if (qb + 2 < nq) step(ic<2>{}, qb + 2);
+    static_for<NS>([&](auto sc) {
+      if (qb + decltype(sc)::value < nq) step(sc, qb + decltype(sc)::value);
+    });
   }
 
   // The LDS is free after the last barrier: each wave stages its dV and dK
@@ -494,11 +516,13 @@ void attn_dkdv_kernel(const BwdParams p) {
 // =============================================================== dQ pass ==
 template <int D, int VAR>
 struct DqShape {
-  static constexpr int WAVES = ((VAR == PW && D > 64) || D == 32) ? 4 : 8;
+  // D = 256: Q, dO (128 registers) and the dQ accumulators (128) fill one
+  // wave per SIMD; two ring stages of 64 x 256 K and V tiles (128 KiB)
+  static constexpr int WAVES = ((VAR == PW && D > 64) || D == 32 || D == 256) ? 4 : 8;
   static constexpr int NT = 64 * WAVES;
   static constexpr int BM = 32 * WAVES;  // queries per workgroup
   static constexpr int BN = 64;          // keys per streamed block
-  static constexpr int NS = 3;           // ring stages
+  static constexpr int NS = D == 256 ? 2 : 3;  // ring stages
 };
 
 // Ring of K (K1), K2 and V tiles, grouped by kind so that the transposing
@@ -536,7 +560,7 @@ void attn_dq_kernel(const BwdParams p) {
   constexpr int PT = BN / 16;
   constexpr bool kPw = VAR == PW;
   static_assert(sizeof(Sm) <= kLdsBytes, "LDS budget");
-  static_assert(NS == 3, "the ring loop is unrolled by three");
+  static_assert(NS == 2 || NS == 3, "ring of two or three stages");
 
   __shared__ Sm smem;
 
@@ -627,8 +651,11 @@ void attn_dq_kernel(const BwdParams p) {
     tload(gv + off, smem.v[S], nr);
     return n;
   };
+  // (two stages: every load is waited for, as in the dK/dV pass)
   auto wait_all_but = [&](int n) {
-    if constexpr (kPw)
+    if constexpr (NS == 2)
+      wait_vmcnt0();
+    else if constexpr (kPw)
       wait_vmcnt_any<3 * Dma::PER_WAVE, 2 * Dma::PER_WAVE>(n);
     else
       wait_vmcnt<2 * Dma::PER_WAVE>();
@@ -812,9 +839,9 @@ void attn_dq_kernel(const BwdParams p) {
     lds_barrier();
   };
   for (int jb = 0; jb < nkb; jb += NS) {
-    step(ic<0>{}, jb);
-    if (jb + 1 < nkb) step(ic<1>{}, jb + 1);
-    if (jb + 2 < nkb) step(ic<2>{}, jb + 2);
+    static_for<NS>([&](auto sc) {
+      if (jb + decltype(sc)::value < nkb) step(sc, jb + decltype(sc)::value);
+    });
   }
 
   // The ring is free after the last barrier: each wave stages its dQ tile
@@ -908,6 +935,11 @@ hipError_t dispatch(const BwdArgs& a, hipStream_t s) {
     if constexpr (DKDV) return pw ? dkdv_t<T, 32, PW>(a, s) : dkdv_t<T, 32, PLAIN>(a, s);
     else return pw ? dq_t<T, 32, PW>(a, s) : dq_t<T, 32, PLAIN>(a, s);
   }
+  if (a.D == 256 && !pw) {
+    constexpr bool kF16 = std::is_same<T, _Float16>::value;
+    if constexpr (DKDV) return kF16 ? bwd_dkdv_d256_f16(a, s) : bwd_dkdv_d256_bf16(a, s);
+    else return kF16 ? bwd_dq_d256_f16(a, s) : bwd_dq_d256_bf16(a, s);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -935,6 +967,18 @@ hipError_t bwd_dq_f16(const BwdArgs& a, hipStream_t s) { return dispatch<_Float1
 #endif
 #if FA_BWD_ALL || FA_BWD_PART == 4
 hipError_t bwd_dq_bf16(const BwdArgs& a, hipStream_t s) { return dispatch<__bf16, false>(a, s); }
+#endif
+#if FA_BWD_ALL || FA_BWD_PART == 5
+hipError_t bwd_dkdv_d256_f16(const BwdArgs& a, hipStream_t s) { return dkdv_t<_Float16, 256, PLAIN>(a, s); }
+#endif
+#if FA_BWD_ALL || FA_BWD_PART == 6
+hipError_t bwd_dkdv_d256_bf16(const BwdArgs& a, hipStream_t s) { return dkdv_t<__bf16, 256, PLAIN>(a, s); }
+#endif
+#if FA_BWD_ALL || FA_BWD_PART == 7
+hipError_t bwd_dq_d256_f16(const BwdArgs& a, hipStream_t s) { return dq_t<_Float16, 256, PLAIN>(a, s); }
+#endif
+#if FA_BWD_ALL || FA_BWD_PART == 8
+hipError_t bwd_dq_d256_bf16(const BwdArgs& a, hipStream_t s) { return dq_t<__bf16, 256, PLAIN>(a, s); }
 #endif
 
 #if FA_BWD_PART == 0

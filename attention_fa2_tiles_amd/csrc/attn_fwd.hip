@@ -26,6 +26,12 @@
 #include "kernels.h"
 
 namespace fa {
+
+// The 16-bit D = 256 fused JVP, in translation units of their own (they
+// compile separately from the other kernels of each dtype).
+hipError_t fwd_jvp_d256_f16(const FwdArgs& a, hipStream_t s);
+hipError_t fwd_jvp_d256_bf16(const FwdArgs& a, hipStream_t s);
+
 namespace {
 
 template <int V>
@@ -50,12 +56,23 @@ constexpr int kLdsBytes = 160 * 1024;
 // two workgroups share a CU: twice as many, shorter query blocks balance
 // the causal triangle's uneven work better (12% faster at 1024, 4% slower
 // than 8 waves without the mask).  Each wave owns 32 query rows.
+//
+// JVP at D = 256: the output and tangent accumulators of all 256 columns
+// (256 registers) next to Q and the tangent Q (128) do not fit one wave's
+// 512, so the output columns are split over two workgroups (SPLIT), each
+// forming the full scores and accumulating 128 columns of O and its tangent
+// (one wave per SIMD, AGPRs holding what the VGPRs cannot); its blocks are
+// 32 keys (K and tK of 32 x 256, V and tV of 32 x 128: 48 KiB per ring
+// stage).
 template <int VAR, int D, bool CAUSAL>
 struct FwdShape {
   static constexpr bool kSmall = VAR == JVP && D == 64 && CAUSAL;
   static constexpr int WAVES = (D == 32 || D == 256 || (VAR == JVP && D == 128) || kSmall) ? 4 : 8;
   static constexpr int NT = 64 * WAVES;
   static constexpr int BM = 32 * WAVES;
+  static constexpr int BN = (VAR == JVP && D == 256) ? 32 : kBN;  // keys per K/V block
+  static constexpr int SPLIT = (VAR == JVP && D == 256) ? 2 : 1;  // workgroups per query block
+  static constexpr int DV = D / SPLIT;                            // output columns per workgroup
 };
 
 struct FwdParams {
@@ -81,11 +98,13 @@ struct FwdParams {
 
 template <typename T, int D, int VAR, bool CAUSAL>
 struct alignas(16) FwdStage {
-  using Tile = DTile<T, kBN, D, FwdShape<VAR, D, CAUSAL>::WAVES>;
+  using Sh = FwdShape<VAR, D, CAUSAL>;
+  using Tile = DTile<T, Sh::BN, D, Sh::WAVES>;
+  using VTile = DTile<T, Sh::BN, Sh::DV, Sh::WAVES, true, D>;  // this workgroup's V columns
   static constexpr int NK = (VAR == PLAIN) ? 1 : 2;  // K (+ tK or K2)
   static constexpr int NV = (VAR == JVP) ? 2 : 1;    // V (+ tV)
   T k[NK][Tile::ELEMS];
-  T v[NV][Tile::ELEMS];
+  T v[NV][VTile::ELEMS];
 };
 
 // K/V stages in the LDS ring: three (prefetch two blocks ahead) when they fit
@@ -107,15 +126,18 @@ template <typename T, int D, int VAR, bool CAUSAL, bool RAGGED>
 __global__ __launch_bounds__((FwdShape<VAR, D, CAUSAL>::NT))
 __attribute__((amdgpu_waves_per_eu(fwd_waves_per_eu<VAR, D, CAUSAL>(), fwd_waves_per_eu<VAR, D, CAUSAL>())))
 void attn_fwd_kernel(const FwdParams p) {
+  constexpr int BN = FwdShape<VAR, D, CAUSAL>::BN;
+  constexpr int SPLIT = FwdShape<VAR, D, CAUSAL>::SPLIT;
+  constexpr int DV = FwdShape<VAR, D, CAUSAL>::DV;
   constexpr int kWaves = FwdShape<VAR, D, CAUSAL>::WAVES;
   constexpr int kBM = FwdShape<VAR, D, CAUSAL>::BM;
   constexpr int NS = fwd_stages<T, D, VAR, CAUSAL>();
   using V8 = typename Vec8<T>::type;
   using St = FwdStage<T, D, VAR, CAUSAL>;
   constexpr int KK = D / 16;     // 16-wide k steps over the head dim
-  constexpr int DT = D / 32;     // 32-wide tiles of the output's head dim
-  constexpr int ST = kBN / 32;   // 32-key score tiles per block
-  constexpr int PT = kBN / 16;   // 16-key operand slices per block
+  constexpr int DT = DV / 32;    // 32-wide tiles of this workgroup's output columns
+  constexpr int ST = BN / 32;   // 32-key score tiles per block
+  constexpr int PT = BN / 16;   // 16-key operand slices per block
   constexpr bool kJvp = VAR == JVP;
   constexpr bool kPw = VAR == PW;
 
@@ -132,8 +154,12 @@ void attn_fwd_kernel(const FwdParams p) {
   // when the whole grid is resident at once (two workgroups per CU), the
   // second half runs the shortest first, so that the workgroup dispatched
   // beside the longest one on a CU is the shortest.
-  const int bh = blockIdx.x % p.BH;
-  int mb = blockIdx.x / p.BH;
+  // (SPLIT > 1: the workgroups of one query block are adjacent; half is
+  // the share of the output columns this one accumulates)
+  const int half = SPLIT > 1 ? (int)(blockIdx.x % SPLIT) : 0;
+  const int wg = SPLIT > 1 ? (int)(blockIdx.x / SPLIT) : (int)blockIdx.x;
+  const int bh = wg % p.BH;
+  int mb = wg / p.BH;
   if (CAUSAL) mb = mb < p.fold ? p.nmb - 1 - mb : mb - p.fold;
   const int m0 = mb * kBM;
   const int row0 = m0 + 32 * wave;
@@ -146,20 +172,24 @@ void attn_fwd_kernel(const FwdParams p) {
   // Direct loads of this head's K/V (and tK/tV or K2): uniform block base
   // pointer plus in-tile lane offsets computed once.
   const T* gk = (const T*)p.k + kbase;
-  const T* gv = (const T*)p.v + kbase;
+  const T* gv = (const T*)p.v + kbase + half * DV;
   const T* gk2 = kPw ? (const T*)p.k2 + kbase : kJvp ? (const T*)p.tk + kbase : gk;
-  const T* gv2 = kJvp ? (const T*)p.tv + kbase : gv;
-  DmaTile<T, kBN, D, kWaves> dma;
+  const T* gv2 = kJvp ? (const T*)p.tv + kbase + half * DV : gv;
+  using DmaK = DmaTile<T, BN, D, kWaves>;
+  using DmaV = DmaTile<T, BN, DV, kWaves, true, D>;
+  DmaK dma;
   dma.lane_offsets(wave, lane);
+  DmaV dmav;
+  if constexpr (SPLIT > 1) dmav.lane_offsets(wave, lane);
 
   int n_end = p.N;
   const int wg_last_row = min(p.M, m0 + kBM) - 1;
   if (CAUSAL) n_end = min(p.N, wg_last_row + pshift + 1);
-  const int nblk = n_end > 0 ? (n_end + kBN - 1) / kBN : 0;
+  const int nblk = n_end > 0 ? (n_end + BN - 1) / BN : 0;
   // Non-causal with a partial last key block: that block is visited first,
   // in a peeled iteration, so that the loop never needs the mask (causal:
   // the diagonal mask already hides every key past the last one).
-  const bool tail_first = RAGGED && !CAUSAL && p.N % kBN != 0;
+  const bool tail_first = RAGGED && !CAUSAL && p.N % BN != 0;
   auto key_block = [&](int jb) { return tail_first ? (jb == 0 ? nblk - 1 : jb - 1) : jb; };
 
   // Query-side operands stay in registers for the whole pass.
@@ -208,35 +238,44 @@ void attn_fwd_kernel(const FwdParams p) {
     for (int s2 = 0; s2 < 2; ++s2) {
       const int m = swap23(8 * tl.hh + 4 * s2 + tl.r);
       const int d = 32 * dt + tl.dcol;
-      vofs[dt][s2] = (uint32_t)((m * D + (((d >> 3) ^ swz<D>(m)) * 8) + (d & 7)) * 2);
+      vofs[dt][s2] = (uint32_t)((m * DV + (((d >> 3) ^ swz<DV>(m)) * 8) + (d & 7)) * 2);
     }
   }
 
   // Piecewise: which score pairs a block needs, for a row range.
   auto pw_class = [&](int r_lo, int r_hi, int n0, bool& all_near, bool& all_far) {
     const int dmax = r_hi + pshift - n0;
-    const int dmin = r_lo + pshift - (n0 + kBN - 1);
+    const int dmin = r_lo + pshift - (n0 + BN - 1);
     all_near = (dmax <= p.w) && (dmin >= -p.w);
     all_far = (p.w < 0) || (dmin > p.w) || (dmax < -p.w);
   };
 
   // Issue the direct loads of K/V block jb into stage st (completion:
   // vmcnt); returns the number of load instructions this wave issued.
-  constexpr int kTileLoads = DmaTile<T, kBN, D, kWaves>::PER_WAVE;
+  constexpr int kTileLoads = DmaK::PER_WAVE;
+  constexpr int kVLoads = DmaV::PER_WAVE;
   auto tload = [&](const T* g, T* lds, int nr) {
     if constexpr (RAGGED)
       dma.load_rows(g, lds, wave, lane, nr);
     else
       dma.load(g, lds, wave);
   };
+  auto vload = [&](const T* g, T* lds, int nr) {
+    if constexpr (SPLIT == 1)
+      tload(g, lds, nr);
+    else if constexpr (RAGGED)
+      dmav.load_rows(g, lds, wave, lane, nr);
+    else
+      dmav.load(g, lds, wave);
+  };
   auto issue = [&](St& st, int jb) -> int {
     const int kb = key_block(jb);
-    const int64_t off = (int64_t)kb * kBN * D;
-    const int nr = p.N - kb * kBN;  // rows of this block that exist
-    int n = kTileLoads * St::NV;
+    const int64_t off = (int64_t)kb * BN * D;
+    const int nr = p.N - kb * BN;  // rows of this block that exist
+    int n = kVLoads * St::NV;
     if constexpr (kPw) {
       bool an, af;
-      pw_class(m0, wg_last_row, kb * kBN, an, af);
+      pw_class(m0, wg_last_row, kb * BN, an, af);
       if (!af) {
         tload(gk + off, st.k[0], nr);
         n += kTileLoads;
@@ -250,8 +289,8 @@ void attn_fwd_kernel(const FwdParams p) {
       if constexpr (kJvp) tload(gk2 + off, st.k[1], nr);
       n += kTileLoads * St::NK;
     }
-    tload(gv + off, st.v[0], nr);
-    if constexpr (kJvp) tload(gv2 + off, st.v[1], nr);
+    vload(gv + off, st.v[0], nr);
+    if constexpr (kJvp) vload(gv2 + off, st.v[1], nr);
     return n;
   };
   // Wait until every load but the newest n (one block's) has landed; loads
@@ -260,7 +299,7 @@ void attn_fwd_kernel(const FwdParams p) {
     if constexpr (kPw)
       wait_vmcnt_any<3 * kTileLoads, 2 * kTileLoads>(n);
     else
-      wait_vmcnt<kTileLoads * (St::NK + St::NV)>();
+      wait_vmcnt<kTileLoads * St::NK + kVLoads * St::NV>();
   };
 
   // Prologue: blocks 0 .. NS-2 are issued right behind the query operands;
@@ -344,7 +383,7 @@ void attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) s[st] = mfma32x32x16(krow8(cur.k[0], st, kk), qf[kk], s[st]);
       }
-    } else {
+    } else if constexpr (SPLIT == 1) {
 #pragma unroll
       for (int st = 0; st < ST; ++st) {
         s[st] = zero16();
@@ -358,6 +397,32 @@ void attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) sd[st] = mfma32x32x16(krow8(cur.k[1], st, kk), qf[kk], sd[st]);
       }
+    } else {
+      // (one 32-key tile) the K rows, then the tK rows, read in a rolling
+      // window of four: row i + 4 is read right after the products of row
+      // i, so that few reads hold registers (Q and the tangent Q take 128)
+      static_assert(ST == 1, "one score tile");
+      constexpr int kW = 4;
+      auto kread = [&](auto i_c) -> V8 {
+        constexpr int I = decltype(i_c)::value;
+        return krow8(cur.k[I / KK], 0, I % KK);
+      };
+      V8 kr[kW];
+      static_for<kW>([&](auto ic) { kr[decltype(ic)::value] = kread(ic); });
+      s[0] = zero16();
+      sd[0] = zero16();
+      static_for<2 * KK>([&](auto ic) {
+        constexpr int I = decltype(ic)::value, kk = I % KK;
+        const V8 a = kr[I % kW];
+        if constexpr (I < KK) {
+          s[0] = mfma32x32x16(a, qf[kk], s[0]);
+          sd[0] = mfma32x32x16(a, tqf[kk], sd[0]);
+        } else {
+          sd[0] = mfma32x32x16(a, qf[kk], sd[0]);
+        }
+        if constexpr (I + kW < 2 * KK) kr[I % kW] = kread(std::integral_constant<int, I + kW>{});
+        __builtin_amdgcn_sched_barrier(0);
+      });
     }
     // ---- online softmax ---------------------------------------------------
     if constexpr (MASK) {
@@ -434,8 +499,8 @@ void attn_fwd_kernel(const FwdParams p) {
     const uint32_t vbase2 = kJvp ? lds_addr(cur.v[kJvp ? 1 : 0]) : 0u;
     TrOps<T, PT> va, vb;
     TrOps<T, kJvp ? PT : 1> ta, tb;
-    va.template issue_at<D>(vbase, vofs[0]);
-    if constexpr (kJvp) ta.template issue_at<D>(vbase2, vofs[0]);
+    va.template issue_at<DV>(vbase, vofs[0]);
+    if constexpr (kJvp) ta.template issue_at<DV>(vbase2, vofs[0]);
     va.wait();
     if constexpr (kJvp) ta.wait();
 #pragma unroll
@@ -445,8 +510,8 @@ void attn_fwd_kernel(const FwdParams p) {
       TrOps<T, kJvp ? PT : 1>& ct = (dt & 1) ? tb : ta;
       TrOps<T, kJvp ? PT : 1>& nt = (dt & 1) ? ta : tb;
       if (dt + 1 < DT) {
-        nv.template issue_at<D>(vbase, vofs[dt + 1]);
-        if constexpr (kJvp) nt.template issue_at<D>(vbase2, vofs[dt + 1]);
+        nv.template issue_at<DV>(vbase, vofs[dt + 1]);
+        if constexpr (kJvp) nt.template issue_at<DV>(vbase2, vofs[dt + 1]);
       }
 #pragma unroll
       for (int t = 0; t < PT; ++t) {
@@ -476,10 +541,10 @@ void attn_fwd_kernel(const FwdParams p) {
     if (ld_stage >= NS) ld_stage -= NS;
     const bool issued = ahead < nblk;
     if (issued) n_new = issue(smem[ld_stage], ahead);
-    const int n0 = key_block(jb) * kBN;
+    const int n0 = key_block(jb) * BN;
     const bool active = wave_valid && (!CAUSAL || n0 <= row0 + 31 + pshift);
     if (active) {
-      if (decltype(tail_tag)::value || (CAUSAL && (n0 + kBN - 1 > row0 + pshift)))
+      if (decltype(tail_tag)::value || (CAUSAL && (n0 + BN - 1 > row0 + pshift)))
         block(smem[cur_stage], n0, std::true_type{});
       else
         block(smem[cur_stage], n0, std::false_type{});
@@ -508,10 +573,11 @@ void attn_fwd_kernel(const FwdParams p) {
   const float l = halves_sum(l_i);
   const bool has = l > 0.f;
   const float inv = has ? 1.f / l : 0.f;
-  static_assert(kWaves * RowStage<D>::kStageBytes <= (int)sizeof(smem), "output staging fits in the ring");
-  char* stage = reinterpret_cast<char*>(&smem[0]) + wave * RowStage<D>::kStageBytes;
+  static_assert(kWaves * RowStage<DV>::kStageBytes <= (int)sizeof(smem), "output staging fits in the ring");
+  char* stage = reinterpret_cast<char*>(&smem[0]) + wave * RowStage<DV>::kStageBytes;
   const int nrows = RAGGED ? p.M - row0 : 32;
-  store_tile_rows<T, D>((T*)p.o + qbase + (int64_t)row0 * D, nrows, acc, inv, stage, lane);
+  const int64_t orow = qbase + (int64_t)row0 * D + half * DV;
+  store_tile_rows<T, DV, D>((T*)p.o + orow, nrows, acc, inv, stage, lane);
   float c = 0.f;
   if constexpr (kJvp) {
     const float mu = halves_sum(mu_i);
@@ -521,9 +587,10 @@ void attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) accg[dt][r] = accg[dt][r] - c * acc[dt][r];
     }
-    store_tile_rows<T, D>((T*)p.to + qbase + (int64_t)row0 * D, nrows, accg, inv, stage, lane);
+    store_tile_rows<T, DV, D>((T*)p.to + orow, nrows, accg, inv, stage, lane);
   }
   if (RAGGED && qi >= p.M) return;  // lanes past the last query row
+  if (half != 0) return;            // (every share forms the same row statistics)
   if (h == 0) p.lse[(int64_t)bh * p.M + qi] = has ? (m_i + log2f(l)) * kLn2 : kNegInf;
   // LSE tangent: sum_j P_ij Sdot_ij (0 for a row with no visible key)
   if (kJvp && h == 0 && p.tlse) p.tlse[(int64_t)bh * p.M + qi] = c;
@@ -1003,7 +1070,9 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
   p.scale2 = a.sm_scale * kLog2e;
   p.sm_scale = a.sm_scale;
   p.w = a.w;
-  dim3 grid(p.nmb * p.BH), block(a.causal ? FwdShape<VAR, D, true>::NT : FwdShape<VAR, D, false>::NT);
+  static_assert(FwdShape<VAR, D, true>::SPLIT == FwdShape<VAR, D, false>::SPLIT, "one split per variant");
+  dim3 grid(p.nmb * p.BH * FwdShape<VAR, D, true>::SPLIT),
+      block(a.causal ? FwdShape<VAR, D, true>::NT : FwdShape<VAR, D, false>::NT);
   const bool ragged = a.M % 64 != 0 || a.N % 64 != 0;
   if constexpr ((VAR == PLAIN && (D == 64 || D == 128)) || (VAR == PW && D == 64)) {
     static_assert(FwdShape<VAR, D, true>::NT == 64 * kPipeWaves && FwdShape<VAR, D, false>::NT == 64 * kPipeWaves,
@@ -1044,9 +1113,11 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
   if (a.D == 64) return launch_var<T, 64>(a, s);
   if (a.D == 128) return launch_var<T, 128>(a, s);
   if (a.D == 32) return launch_var<T, 32>(a, s);
-  // D = 256: plain attention only (two K/V stages of the JVP and piecewise
-  // variants do not fit in the CU's LDS)
-  if (a.D == 256) return a.variant == PLAIN ? launch_t<T, 256, PLAIN>(a, s) : hipErrorInvalidValue;
+  // D = 256: plain attention here, the JVP in its own translation units
+  // (piecewise runs on the generic kernels)
+  if (a.D == 256 && a.variant == PLAIN) return launch_t<T, 256, PLAIN>(a, s);
+  if (a.D == 256 && a.variant == JVP)
+    return std::is_same<T, _Float16>::value ? fwd_jvp_d256_f16(a, s) : fwd_jvp_d256_bf16(a, s);
   return hipErrorInvalidValue;
 }
 
@@ -1067,6 +1138,12 @@ hipError_t fwd_f16(const FwdArgs& a, hipStream_t s) { return launch_d<_Float16>(
 #endif
 #if FA_FWD_ALL || FA_FWD_PART == 2
 hipError_t fwd_bf16(const FwdArgs& a, hipStream_t s) { return launch_d<__bf16>(a, s); }
+#endif
+#if FA_FWD_ALL || FA_FWD_PART == 3
+hipError_t fwd_jvp_d256_f16(const FwdArgs& a, hipStream_t s) { return launch_t<_Float16, 256, JVP>(a, s); }
+#endif
+#if FA_FWD_ALL || FA_FWD_PART == 4
+hipError_t fwd_jvp_d256_bf16(const FwdArgs& a, hipStream_t s) { return launch_t<__bf16, 256, JVP>(a, s); }
 #endif
 
 #if FA_FWD_PART == 0

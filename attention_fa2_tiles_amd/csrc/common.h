@@ -273,7 +273,9 @@ __device__ __forceinline__ constexpr int tile_row(int m, bool perm) { return per
 static __device__ __attribute__((aligned(16))) uint32_t kZero16[4] = {0u, 0u, 0u, 0u};
 static __device__ float kPosInfF = __builtin_huge_valf();
 
-template <typename T, int R, int D, int NW, bool PERM = true>
+// G: the row stride of the tensor the tile is loaded from, in elements (a
+// tile of D columns out of G-wide rows; normally G = D).
+template <typename T, int R, int D, int NW, bool PERM = true, int G = D>
 struct DTile {
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
   static constexpr int ROWS_PER_INSTR = 64 / CPR;   // rows per wave instruction
@@ -290,7 +292,7 @@ struct DTile {
       const int ins = wave * PER_WAVE + j;
       const int p = ins * 64 + lane;
       const int m = p / CPR, slot = p % CPR;
-      const T* src = g + tile_row(m, PERM) * D + ((slot ^ swz<D>(m)) * 8);
+      const T* src = g + tile_row(m, PERM) * G + ((slot ^ swz<D>(m)) * 8);
       __builtin_amdgcn_global_load_lds(
           (const void __attribute__((address_space(1)))*)src,
           (void __attribute__((address_space(3)))*)(lds + ins * 512), 16, 0, 0);
@@ -308,7 +310,7 @@ struct DTile {
       const int p = ins * 64 + lane;
       const int m = p / CPR, slot = p % CPR;
       const int src = tile_row(m, PERM);
-      const T* src_ptr = src < nrows ? g + src * D + ((slot ^ swz<D>(m)) * 8) : reinterpret_cast<const T*>(kZero16);
+      const T* src_ptr = src < nrows ? g + src * G + ((slot ^ swz<D>(m)) * 8) : reinterpret_cast<const T*>(kZero16);
       __builtin_amdgcn_global_load_lds(
           (const void __attribute__((address_space(1)))*)src_ptr,
           (void __attribute__((address_space(3)))*)(lds + ins * 512), 16, 0, 0);
@@ -325,9 +327,9 @@ struct DTile {
 // inside the tile (computed once by lane_offsets): a tile is issued from a
 // uniform base pointer plus those 32-bit offsets, which the compiler can
 // encode with a scalar base register, so issuing costs no vector arithmetic.
-template <typename T, int R, int D, int NW, bool PERM = true>
+template <typename T, int R, int D, int NW, bool PERM = true, int G = D>
 struct DmaTile {
-  using Tile = DTile<T, R, D, NW, PERM>;
+  using Tile = DTile<T, R, D, NW, PERM, G>;
   static constexpr int PER_WAVE = Tile::PER_WAVE;
   uint32_t voff[PER_WAVE];
 
@@ -337,10 +339,10 @@ struct DmaTile {
       const int ins = wave * PER_WAVE + j;
       const int p = ins * 64 + lane;
       const int m = p / Tile::CPR, slot = p % Tile::CPR;
-      voff[j] = (uint32_t)((tile_row(m, PERM) * D + ((slot ^ swz<D>(m)) * 8)) * 2);
+      voff[j] = (uint32_t)((tile_row(m, PERM) * G + ((slot ^ swz<D>(m)) * 8)) * 2);
     }
   }
-  // Load the tile whose first row is at g (row stride D) into lds.
+  // Load the tile whose first row is at g (row stride G) into lds.
   __device__ __forceinline__ void load(const T* g, T* lds, int wave) const {
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
@@ -545,7 +547,7 @@ __device__ __forceinline__ void store_acc_t(T* row_ptr, const f32x16& acc, int d
 // consecutive rows (64 / (D / 8) of them).
 //   lds: this wave's private region of kStageBytes (32 rows, pitch 2 D + 16
 //        bytes: the padding staggers the rows over the banks);
-//   g:   row 0 of the tile in global memory (row stride D);
+//   g:   row 0 of the tile in global memory (row stride G, normally D);
 //   s:   this lane's scale (its row's);
 //   nrows: rows of the tile that exist (rows from nrows on are not stored).
 // The caller makes sure no other wave uses the region.
@@ -555,7 +557,7 @@ struct RowStage {
   static constexpr int kStageBytes = 32 * PITCH;
 };
 
-template <typename T, int D>
+template <typename T, int D, int G = D>
 __device__ __forceinline__ void store_tile_rows(T* g, int nrows, const f32x16 (&acc)[D / 32], float s, char* lds,
                                                 int lane) {
   constexpr int PITCH = RowStage<D>::PITCH;
@@ -581,7 +583,7 @@ __device__ __forceinline__ void store_tile_rows(T* g, int nrows, const f32x16 (&
   for (int i = 0; i < 32 / RPI; ++i) {
     const int row = RPI * i + lane / CPR, c = lane % CPR;
     const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * PITCH + 16 * c);
-    if (row < nrows) *reinterpret_cast<u32x4*>(g + (int64_t)row * D + 8 * c) = v;
+    if (row < nrows) *reinterpret_cast<u32x4*>(g + (int64_t)row * G + 8 * c) = v;
   }
 }
 

@@ -123,7 +123,7 @@ SMALL = [
     (F32, 1, 2, 100, 77, 32, True),
     (F32, 1, 1, 64, 96, 256, True),
     (F32, 1, 1, 70, 50, 256, False),
-    # head dim 16 (every dtype) and 16-bit 256 backward: the generic kernels
+    # head dim 16 (every dtype, the generic kernels) and 16-bit 256
     (BF16, 1, 2, 100, 130, 16, True),
     (F16, 2, 1, 64, 64, 16, False),
     (F32, 1, 2, 77, 50, 16, True),
@@ -133,17 +133,30 @@ SMALL = [
 
 
 @pytest.mark.parametrize("case", [(BF16, 2, 2, 200, 300, 256, True), (F16, 1, 2, 256, 256, 256, False),
-                                  (BF16, 1, 2, 128, 128, 256, True), (F16, 1, 1, 33, 65, 256, False)],
+                                  (BF16, 1, 2, 128, 128, 256, True), (F16, 1, 1, 33, 65, 256, False),
+                                  (BF16, 1, 2, 512, 512, 256, True), (F16, 1, 2, 300, 150, 256, True),
+                                  (BF16, 1, 1, 384, 640, 256, False)],
                          ids=lambda c: "-".join(map(str, c)))
-def test_head_dim_256_forward(case):
-    """fp16/bf16 D = 256 forward on the MFMA kernel (the backward of this
-    head dim runs on the generic kernels and is in SMALL)."""
+def test_head_dim_256(case):
+    """fp16/bf16 D = 256 forward and backward on the MFMA kernels (the
+    backward passes run one wave per SIMD with two-stage rings): several
+    query and key blocks, ragged lengths, M > N causal rows that see no
+    key."""
     dtype, B, H, M, N, D, causal = case
     wl = AttnWorkload("d256", dtype, B, H, M, N, D, causal, seed=13 + M + N)
-    log(f"fa d256 forward parity {case}")
+    log(f"fa d256 forward + backward parity {case}")
     t = attn_inputs(wl)
-    got = run_fwd_bwd(wl, t, with_bwd=False, guard=True)
-    compare(wl, t, got, with_bwd=False)
+    got = run_fwd_bwd(wl, t, guard=True)
+    compare(wl, t, got)
+
+
+def test_head_dim_256_steps():
+    """D = 256 through the separate Delta, dK/dV and dQ entry points."""
+    wl = AttnWorkload("d256_steps", BF16, 1, 2, 256, 320, 256, True, seed=17)
+    log("fa d256 backward steps parity")
+    t = attn_inputs(wl)
+    got = run_fwd_bwd(wl, t, steps=True, guard=True)
+    compare(wl, t, got)
 
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "-".join(map(str, c)))

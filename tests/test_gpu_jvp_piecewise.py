@@ -58,10 +58,14 @@ JVP_SMALL = [
     (F16, 1, 2, 150, 100, 32, True),      # head dims 32 and (fp32) 256
     (BF16, 2, 2, 128, 128, 32, False),
     (F32, 1, 1, 64, 80, 256, True),
-    (F16, 1, 2, 100, 120, 16, True),      # head dim 16 and 16-bit 256: the generic kernels
+    (F16, 1, 2, 100, 120, 16, True),      # head dim 16: the generic kernels
     (BF16, 1, 1, 64, 64, 16, False),
-    (F16, 1, 2, 90, 70, 256, True),
+    (F16, 1, 2, 90, 70, 256, True),       # 16-bit 256: output columns split over two workgroups
     (BF16, 1, 1, 64, 96, 256, False),
+    (BF16, 2, 2, 256, 256, 256, True),
+    (F16, 1, 2, 384, 384, 256, False),
+    (BF16, 1, 2, 300, 170, 256, True),    # M > N: rows that see no key
+    (F16, 1, 1, 130, 450, 256, False),
 ]
 
 
@@ -113,7 +117,7 @@ def ramp_tangent_inputs(M, N, D, dtype, seed):
     j = np.arange(N)
     k[0, 0, :, 0] = np.where(j < 64, 0.0, 7.9 * (j - 64) / (N - 65)) / (c * log2e * 4.0)
     tk = np.zeros((1, 1, N, D), np.float32)
-    tk[..., 0] = 600.0 * np.where(rng.standard_normal(N) > 0, 1.0, -1.0)
+    tk[..., 0] = (75.0 / c) * np.where(rng.standard_normal(N) > 0, 1.0, -1.0)  # tangent scores +-300
     arrays = {"q": q, "k": k, "v": rng.standard_normal((1, 1, N, D)).astype(np.float32),
               "tq": rng.standard_normal((1, 1, M, D)).astype(np.float32), "tk": tk,
               "tv": rng.standard_normal((1, 1, N, D)).astype(np.float32)}
@@ -124,13 +128,14 @@ def ramp_tangent_inputs(M, N, D, dtype, seed):
     return out
 
 
-def test_jvp_large_tangent_fp16():
+@pytest.mark.parametrize("D", [64, 256])
+def test_jvp_large_tangent_fp16(D):
     """fp16 JVP whose later keys raise the row maximum by almost 8 (log2)
     while the tangent scores are near 300: the tangent output stays finite
     and meets the bar."""
-    wl = AttnWorkload("jvp_ramp", F16, 1, 1, 256, 256, 64, False, seed=5)
-    log("jvp large tangents, fp16")
-    t = ramp_tangent_inputs(256, 256, 64, F16, seed=5)
+    wl = AttnWorkload("jvp_ramp", F16, 1, 1, 256, 256, D, False, seed=5)
+    log(f"jvp large tangents, fp16, D = {D}")
+    t = ramp_tangent_inputs(256, 256, D, F16, seed=5)
     got = run_jvp(wl, t)
     assert np.all(np.isfinite(got["to"])), "tangent output overflowed"
     f = [t[n].f64 for n in JVP_NAMES]
