@@ -323,6 +323,21 @@ def test_full_size_noncausal_sampled_heads():
     _FULL.clear()
 
 
+@pytest.mark.parametrize("D", [256, 16])
+def test_head_dims_bench_shape_sampled_heads(D):
+    """The head-dim workloads the benchmark times (causal bf16 B1 H16
+    2048^2, D = 256 on the matrix cores, D = 16 on the generic kernels):
+    every output finite, three heads against the oracle (O, LSE, dQ, dK,
+    dV)."""
+    wl = AttnWorkload(f"causal_bf16_b1h16_s2048_d{D}", BF16, 1, 16, 2048, 2048, D, True, seed=6)
+    log(f"fa head-dim bench shape D = {D}")
+    t = attn_inputs(wl)
+    got = run_fwd_bwd(wl, t)
+    for n, x in got.items():
+        assert np.all(np.isfinite(x)), f"{n}: non-finite values"
+    compare(wl, t, got, heads=[(0, 0), (0, 7), (0, 15)])
+
+
 def test_full_size_tiny_f32():
     """The tiny fp32 workload (B1 H2 128x128 D64, non-causal) against the
     literal fp32 bar: max-abs error <= 1e-4 on O, LSE, dQ, dK and dV."""

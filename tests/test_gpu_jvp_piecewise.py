@@ -104,6 +104,19 @@ def test_jvp_full_size(name):
     compare_jvp(wl, t, run_jvp(wl, t))  # every head
 
 
+@pytest.mark.parametrize("D", [256, 16])
+def test_jvp_head_dims_bench_shape_sampled_heads(D):
+    """The fused JVP at the head-dim workloads the benchmark times (causal
+    bf16 B1 H16 2048^2, D = 256 and 16): three heads against the oracle."""
+    wl = AttnWorkload(f"jvp_causal_bf16_b1h16_s2048_d{D}", BF16, 1, 16, 2048, 2048, D, True, seed=6)
+    log(f"jvp head-dim bench shape D = {D}")
+    t = attn_inputs(wl, JVP_NAMES)
+    got = run_jvp(wl, t)
+    for n, x in got.items():
+        assert np.all(np.isfinite(x)), f"{n}: non-finite values"
+    compare_jvp(wl, t, got, heads=[(0, 0), (0, 7), (0, 15)])
+
+
 def ramp_tangent_inputs(M, N, D, dtype, seed):
     """Scores that stay flat over the first 64 keys and then rise by almost
     8 (log2 units) towards the last key, with tangent scores near 300: an
