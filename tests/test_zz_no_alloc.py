@@ -34,11 +34,18 @@ def grads(wl, t, noalloc):
     return out
 
 
-@pytest.mark.parametrize("dtype", [BF16, F32], ids=["bf16", "f32"])
-def test_noalloc_backward_matches_fa_bwd(dtype):
-    # a larger call, then a smaller one (the array keeps the first call's rows)
-    shapes = [(2, 3, 512, 512, 128, True), (1, 2, 100, 130, 64, False)] if dtype == BF16 else \
-             [(1, 2, 192, 192, 64, True), (1, 1, 70, 50, 32, False)]
+# per case: a larger call, then a smaller one (the array keeps the first
+# call's rows); head dim 256 runs the one-wave-per-SIMD backward passes
+CASES = {
+    "bf16": (BF16, [(2, 3, 512, 512, 128, True), (1, 2, 100, 130, 64, False)]),
+    "f32": (F32, [(1, 2, 192, 192, 64, True), (1, 1, 70, 50, 32, False)]),
+    "bf16_d256": (BF16, [(1, 2, 384, 320, 256, True), (1, 1, 100, 70, 256, False)]),
+}
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_noalloc_backward_matches_fa_bwd(case):
+    dtype, shapes = CASES[case]
     for i, (B, H, M, N, D, causal) in enumerate(shapes):
         wl = AttnWorkload("noalloc", dtype, B, H, M, N, D, causal, seed=60 + i)
         log(f"fa_bwd_noalloc vs fa_bwd: dtype {dtype} shape {(B, H, M, N, D, causal)}")
