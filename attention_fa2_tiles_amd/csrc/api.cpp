@@ -82,7 +82,7 @@ int run_fwd(FwdArgs& a, hipStream_t s) {
                                                               : fa::launch_attn_fwd(a, s));
 }
 
-// The whole backward.  MFMA path (16-bit, D in {32, 64, 128}, and plain
+// The whole backward.  MFMA path (16-bit, D in {16, 32, 64, 128}, and plain
 // attention at D = 256): the dQ pass
 // forms Delta itself and writes it for the dK/dV pass that follows (two
 // launches); generic path: the Delta kernel, then the two passes.

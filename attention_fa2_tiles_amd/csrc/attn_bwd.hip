@@ -144,8 +144,10 @@ constexpr int dkdv_waves_per_eu() {
 }
 
 // RAGGED: M or N is not a multiple of 64 (the tail handling is compiled only
-// into these instantiations).
-template <typename T, int D, int VAR, bool CAUSAL, bool RAGGED>
+// into these instantiations).  G: the row length of the tensors (normally D;
+// head dim 16 runs the D = 32 tiles with G = 16, the upper 16 columns zero
+// in every operand and not stored).
+template <typename T, int D, int VAR, bool CAUSAL, bool RAGGED, int G = D>
 __global__ __launch_bounds__((DkdvShape<D, VAR>::NT))
 __attribute__((amdgpu_waves_per_eu(dkdv_waves_per_eu<D, VAR>(), dkdv_waves_per_eu<D, VAR>())))
 void attn_dkdv_kernel(const BwdParams p) {
@@ -158,8 +160,9 @@ void attn_dkdv_kernel(const BwdParams p) {
   using Sm = DkdvSmem<T, D, VAR>;
   using St = DkdvStage<T, D, VAR>;
   using Tile = typename St::Tile;
-  using VTile = typename Sm::VTile;
-  using Dma = DmaTile<T, QB, D, kWaves>;
+  using VTile = DTile<T, 32, D, 1, false, G>;  // the layout of Sm::VTile, loaded from G-wide rows
+  using Dma = DmaTile<T, QB, D, kWaves, true, G>;
+  static_assert(G <= D, "rows no longer than the tile");
   constexpr int KK = D / 16;   // 16-wide k steps over the head dim
   constexpr int DT = D / 32;   // 32-wide d tiles of dK^t / dV^t
   constexpr int ST = QB / 32;  // 32-query score tiles per block
@@ -184,8 +187,8 @@ void attn_dkdv_kernel(const BwdParams p) {
   const bool wave_valid = kw0 < p.N;
   const int kj = kw0 + li;  // this lane's key
   const int pshift = p.N - p.M;
-  const int64_t qbase = (int64_t)bh * p.M * D;
-  const int64_t kbase = (int64_t)bh * p.N * D;
+  const int64_t qbase = (int64_t)bh * p.M * G;
+  const int64_t kbase = (int64_t)bh * p.N * G;
   const int64_t lbase = (int64_t)bh * p.M;
 
   // Resident operands: this wave's 32 rows of V (piecewise: and of K2) in
@@ -193,8 +196,8 @@ void attn_dkdv_kernel(const BwdParams p) {
   // last one read the last key; their columns are not stored.
   V8 kf[KK];
   if (wave_valid) {
-    const T* vsrc = (const T*)p.v + kbase + (int64_t)kw0 * D;
-    const T* k2src = kPw ? (const T*)p.k2 + kbase + (int64_t)kw0 * D : vsrc;
+    const T* vsrc = (const T*)p.v + kbase + (int64_t)kw0 * G;
+    const T* k2src = kPw ? (const T*)p.k2 + kbase + (int64_t)kw0 * G : vsrc;
     T* k2dst = smem.k2 + (kPw ? wave * VTile::ELEMS : 0);
     if (!RAGGED || p.N - kw0 >= 32) {
       VTile::load(smem.v[wave], vsrc, 0, lane);
@@ -203,9 +206,10 @@ void attn_dkdv_kernel(const BwdParams p) {
       VTile::load_lim(smem.v[wave], vsrc, 0, lane, p.N - kw0);
       if constexpr (kPw) VTile::load_lim(k2dst, k2src, 0, lane, p.N - kw0);
     }
-    const int64_t off = kbase + (int64_t)(RAGGED ? min(kj, p.N - 1) : kj) * D + 8 * h;
+    const int64_t off = kbase + (int64_t)(RAGGED ? min(kj, p.N - 1) : kj) * G + 8 * h;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) kf[kk] = *reinterpret_cast<const V8*>((const T*)p.k + off + 16 * kk);
+    for (int kk = 0; kk < KK; ++kk)  // (G < D: zero past the row's G columns)
+      kf[kk] = (G >= D || 16 * kk + 8 * h < G) ? *reinterpret_cast<const V8*>((const T*)p.k + off + 16 * kk) : V8{};
   }
 
   f32x16 dvt[DT], dkt[DT], dk2t[kPw ? DT : 1];
@@ -250,7 +254,7 @@ void attn_dkdv_kernel(const BwdParams p) {
   };
   auto issue = [&](St& st, int qb) -> int {
     const int i0 = q_begin + qb * QB;
-    const int64_t off = (int64_t)i0 * D;
+    const int64_t off = (int64_t)i0 * G;
     int n = Dma::PER_WAVE + 1;
     const int nr = p.M - i0;  // rows of this block that exist
     if constexpr (kPw) {
@@ -507,10 +511,10 @@ void attn_dkdv_kernel(const BwdParams p) {
   static_assert(kWaves * RowStage<D>::kStageBytes <= (int)sizeof(Sm), "output staging fits in the LDS");
   char* stage = reinterpret_cast<char*>(&smem) + wave * RowStage<D>::kStageBytes;
   const int nrows = RAGGED ? p.N - kw0 : 32;
-  const int64_t orow = kbase + (int64_t)kw0 * D;
-  store_tile_rows<T, D>((T*)p.dv + orow, nrows, dvt, 1.f, stage, lane);
-  store_tile_rows<T, D>((T*)p.dk + orow, nrows, dkt, dk_scale, stage, lane);
-  if constexpr (kPw) store_tile_rows<T, D>((T*)p.dk2 + orow, nrows, dk2t, dk_scale, stage, lane);
+  const int64_t orow = kbase + (int64_t)kw0 * G;
+  store_tile_rows<T, D, G>((T*)p.dv + orow, nrows, dvt, 1.f, stage, lane);
+  store_tile_rows<T, D, G>((T*)p.dk + orow, nrows, dkt, dk_scale, stage, lane);
+  if constexpr (kPw) store_tile_rows<T, D, G>((T*)p.dk2 + orow, nrows, dk2t, dk_scale, stage, lane);
 }
 
 // =============================================================== dQ pass ==
@@ -541,7 +545,7 @@ constexpr int dq_waves_per_eu() {
   return DqShape<D, VAR>::WAVES / 4;
 }
 
-template <typename T, int D, int VAR, bool CAUSAL, bool RAGGED>
+template <typename T, int D, int VAR, bool CAUSAL, bool RAGGED, int G = D>
 __global__ __launch_bounds__((DqShape<D, VAR>::NT))
 __attribute__((amdgpu_waves_per_eu(dq_waves_per_eu<D, VAR>(), dq_waves_per_eu<D, VAR>())))
 void attn_dq_kernel(const BwdParams p) {
@@ -553,7 +557,8 @@ void attn_dq_kernel(const BwdParams p) {
   using V8 = typename Vec8<T>::type;
   using Sm = DqSmem<T, D, VAR>;
   using Tile = typename Sm::Tile;
-  using Dma = DmaTile<T, BN, D, kWaves>;
+  using Dma = DmaTile<T, BN, D, kWaves, true, G>;
+  static_assert(G <= D, "rows no longer than the tile");
   constexpr int KK = D / 16;
   constexpr int DT = D / 32;
   constexpr int ST = BN / 32;
@@ -577,8 +582,8 @@ void attn_dq_kernel(const BwdParams p) {
   const bool wave_valid = row0 < p.M;
   const int qi = row0 + li;
   const int pshift = p.N - p.M;
-  const int64_t qbase = (int64_t)bh * p.M * D;
-  const int64_t kbase = (int64_t)bh * p.N * D;
+  const int64_t qbase = (int64_t)bh * p.M * G;
+  const int64_t kbase = (int64_t)bh * p.N * G;
 
   const T* gk = (const T*)p.k + kbase;
   const T* gk2 = kPw ? (const T*)p.k2 + kbase : gk;
@@ -592,18 +597,23 @@ void attn_dq_kernel(const BwdParams p) {
   V8 of[KK];  // this row's O chunks, when the pass forms Delta
   float lse2 = __builtin_huge_valf(), dl = 0.f;
   const int qr = RAGGED ? min(qi, p.M - 1) : qi;
+  // chunk 2 kk + h of a row (G < D: zero past the row's G columns)
+  auto chunk = [&](const void* base, int64_t off, int kk) -> V8 {
+    if (G >= D || 16 * kk + 8 * h < G) return *reinterpret_cast<const V8*>((const T*)base + off + 16 * kk);
+    return V8{};
+  };
   if (wave_valid) {
-    const int64_t off = qbase + (int64_t)qr * D + 8 * h;
+    const int64_t off = qbase + (int64_t)qr * G + 8 * h;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      qf[kk] = *reinterpret_cast<const V8*>((const T*)p.q + off + 16 * kk);
-      dof[kk] = *reinterpret_cast<const V8*>((const T*)p.dout + off + 16 * kk);
-      if constexpr (kPw) q2f[kk] = *reinterpret_cast<const V8*>((const T*)p.q2 + off + 16 * kk);
+      qf[kk] = chunk(p.q, off, kk);
+      dof[kk] = chunk(p.dout, off, kk);
+      if constexpr (kPw) q2f[kk] = chunk(p.q2, off, kk);
     }
     lse2 = lse_to_log2(p.lse[(int64_t)bh * p.M + qr]);
     if (p.delta_out) {
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) of[kk] = *reinterpret_cast<const V8*>((const T*)p.o + off + 16 * kk);
+      for (int kk = 0; kk < KK; ++kk) of[kk] = chunk(p.o, off, kk);
     } else {
       dl = p.delta[(int64_t)bh * p.M + qr];
     }
@@ -630,7 +640,7 @@ void attn_dq_kernel(const BwdParams p) {
       dma.load(g, lds, wave);
   };
   auto issue = [&](int S, int jb) -> int {
-    const int64_t off = (int64_t)jb * BN * D;
+    const int64_t off = (int64_t)jb * BN * G;
     const int nr = p.N - jb * BN;  // rows of this block that exist
     int n = Dma::PER_WAVE;
     if constexpr (kPw) {
@@ -851,9 +861,9 @@ void attn_dq_kernel(const BwdParams p) {
   static_assert(kWaves * RowStage<D>::kStageBytes <= (int)sizeof(Sm), "output staging fits in the LDS");
   char* stage = reinterpret_cast<char*>(&smem) + wave * RowStage<D>::kStageBytes;
   const int nrows = RAGGED ? p.M - row0 : 32;
-  const int64_t orow = qbase + (int64_t)row0 * D;
-  store_tile_rows<T, D>((T*)p.dq + orow, nrows, dqt, p.sm_scale, stage, lane);
-  if constexpr (kPw) store_tile_rows<T, D>((T*)p.dq2 + orow, nrows, dq2t, p.sm_scale, stage, lane);
+  const int64_t orow = qbase + (int64_t)row0 * G;
+  store_tile_rows<T, D, G>((T*)p.dq + orow, nrows, dqt, p.sm_scale, stage, lane);
+  if constexpr (kPw) store_tile_rows<T, D, G>((T*)p.dq2 + orow, nrows, dq2t, p.sm_scale, stage, lane);
 }
 
 BwdParams make_params(const BwdArgs& a) {
@@ -884,7 +894,7 @@ BwdParams make_params(const BwdArgs& a) {
   return p;
 }
 
-template <typename T, int D, int VAR>
+template <typename T, int D, int VAR, int G = D>
 hipError_t dkdv_t(const BwdArgs& a, hipStream_t s) {
   using Sh = DkdvShape<D, VAR>;
   BwdParams p = make_params(a);
@@ -892,17 +902,17 @@ hipError_t dkdv_t(const BwdArgs& a, hipStream_t s) {
   dim3 grid(p.nblk * p.BH), block(Sh::NT);
   const bool ragged = a.M % 64 != 0 || a.N % 64 != 0;
   if (a.causal && ragged)
-    hipLaunchKernelGGL((attn_dkdv_kernel<T, D, VAR, true, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((attn_dkdv_kernel<T, D, VAR, true, true, G>), grid, block, 0, s, p);
   else if (a.causal)
-    hipLaunchKernelGGL((attn_dkdv_kernel<T, D, VAR, true, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((attn_dkdv_kernel<T, D, VAR, true, false, G>), grid, block, 0, s, p);
   else if (ragged)
-    hipLaunchKernelGGL((attn_dkdv_kernel<T, D, VAR, false, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((attn_dkdv_kernel<T, D, VAR, false, true, G>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((attn_dkdv_kernel<T, D, VAR, false, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((attn_dkdv_kernel<T, D, VAR, false, false, G>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
-template <typename T, int D, int VAR>
+template <typename T, int D, int VAR, int G = D>
 hipError_t dq_t(const BwdArgs& a, hipStream_t s) {
   using Sh = DqShape<D, VAR>;
   BwdParams p = make_params(a);
@@ -910,13 +920,13 @@ hipError_t dq_t(const BwdArgs& a, hipStream_t s) {
   dim3 grid(p.nblk * p.BH), block(Sh::NT);
   const bool ragged = a.M % 64 != 0 || a.N % 64 != 0;
   if (a.causal && ragged)
-    hipLaunchKernelGGL((attn_dq_kernel<T, D, VAR, true, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((attn_dq_kernel<T, D, VAR, true, true, G>), grid, block, 0, s, p);
   else if (a.causal)
-    hipLaunchKernelGGL((attn_dq_kernel<T, D, VAR, true, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((attn_dq_kernel<T, D, VAR, true, false, G>), grid, block, 0, s, p);
   else if (ragged)
-    hipLaunchKernelGGL((attn_dq_kernel<T, D, VAR, false, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((attn_dq_kernel<T, D, VAR, false, true, G>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((attn_dq_kernel<T, D, VAR, false, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((attn_dq_kernel<T, D, VAR, false, false, G>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
@@ -934,6 +944,10 @@ hipError_t dispatch(const BwdArgs& a, hipStream_t s) {
   if (a.D == 32) {
     if constexpr (DKDV) return pw ? dkdv_t<T, 32, PW>(a, s) : dkdv_t<T, 32, PLAIN>(a, s);
     else return pw ? dq_t<T, 32, PW>(a, s) : dq_t<T, 32, PLAIN>(a, s);
+  }
+  if (a.D == 16) {  // the D = 32 kernels over zero-padded tiles
+    if constexpr (DKDV) return pw ? dkdv_t<T, 32, PW, 16>(a, s) : dkdv_t<T, 32, PLAIN, 16>(a, s);
+    else return pw ? dq_t<T, 32, PW, 16>(a, s) : dq_t<T, 32, PLAIN, 16>(a, s);
   }
   if (a.D == 256 && !pw) {
     constexpr bool kF16 = std::is_same<T, _Float16>::value;

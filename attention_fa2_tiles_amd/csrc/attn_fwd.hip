@@ -121,8 +121,10 @@ constexpr int fwd_waves_per_eu() {
 }
 
 // RAGGED: M or N is not a multiple of 64 (the tail handling is compiled only
-// into these instantiations, so the common case runs none of it).
-template <typename T, int D, int VAR, bool CAUSAL, bool RAGGED>
+// into these instantiations, so the common case runs none of it).  G: the
+// row length of the tensors (normally D; head dim 16 runs the D = 32 tiles
+// with G = 16, the upper 16 columns zero in every operand and not stored).
+template <typename T, int D, int VAR, bool CAUSAL, bool RAGGED, int G = D>
 __global__ __launch_bounds__((FwdShape<VAR, D, CAUSAL>::NT))
 __attribute__((amdgpu_waves_per_eu(fwd_waves_per_eu<VAR, D, CAUSAL>(), fwd_waves_per_eu<VAR, D, CAUSAL>())))
 void attn_fwd_kernel(const FwdParams p) {
@@ -166,8 +168,8 @@ void attn_fwd_kernel(const FwdParams p) {
   const bool wave_valid = row0 < p.M;
   const int qi = row0 + li;
   const int pshift = p.N - p.M;
-  const int64_t qbase = (int64_t)bh * p.M * D;
-  const int64_t kbase = (int64_t)bh * p.N * D;
+  const int64_t qbase = (int64_t)bh * p.M * G;
+  const int64_t kbase = (int64_t)bh * p.N * G;
 
   // Direct loads of this head's K/V (and tK/tV or K2): uniform block base
   // pointer plus in-tile lane offsets computed once.
@@ -175,8 +177,9 @@ void attn_fwd_kernel(const FwdParams p) {
   const T* gv = (const T*)p.v + kbase + half * DV;
   const T* gk2 = kPw ? (const T*)p.k2 + kbase : kJvp ? (const T*)p.tk + kbase : gk;
   const T* gv2 = kJvp ? (const T*)p.tv + kbase + half * DV : gv;
-  using DmaK = DmaTile<T, BN, D, kWaves>;
-  using DmaV = DmaTile<T, BN, DV, kWaves, true, D>;
+  static_assert(SPLIT == 1 || G == D, "split output columns of full rows");
+  using DmaK = DmaTile<T, BN, D, kWaves, true, G>;
+  using DmaV = DmaTile<T, BN, DV, kWaves, true, G>;
   DmaK dma;
   dma.lane_offsets(wave, lane);
   DmaV dmav;
@@ -196,19 +199,24 @@ void attn_fwd_kernel(const FwdParams p) {
   // (lanes past the last query row read that row; their results are not stored)
   V8 qf[KK], q2f[kPw ? KK : 1], tqf[kJvp ? KK : 1];
   const int qr = RAGGED ? min(qi, p.M - 1) : qi;
+  // chunk 2 kk + h of a row (G < D: zero past the row's G columns)
+  auto qchunk = [&](const T* row, int kk) -> V8 {
+    if (G >= D || 16 * kk + 8 * h < G) return *reinterpret_cast<const V8*>(row + 16 * kk);
+    return V8{};
+  };
   if (wave_valid) {
-    const T* qrow = (const T*)p.q + qbase + (int64_t)qr * D + 8 * h;
+    const T* qrow = (const T*)p.q + qbase + (int64_t)qr * G + 8 * h;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qf[kk] = *reinterpret_cast<const V8*>(qrow + 16 * kk);
+    for (int kk = 0; kk < KK; ++kk) qf[kk] = qchunk(qrow, kk);
     if constexpr (kPw) {
-      const T* q2row = (const T*)p.q2 + qbase + (int64_t)qr * D + 8 * h;
+      const T* q2row = (const T*)p.q2 + qbase + (int64_t)qr * G + 8 * h;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) q2f[kk] = *reinterpret_cast<const V8*>(q2row + 16 * kk);
+      for (int kk = 0; kk < KK; ++kk) q2f[kk] = qchunk(q2row, kk);
     }
     if constexpr (kJvp) {
-      const T* tqrow = (const T*)p.tq + qbase + (int64_t)qr * D + 8 * h;
+      const T* tqrow = (const T*)p.tq + qbase + (int64_t)qr * G + 8 * h;
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) tqf[kk] = *reinterpret_cast<const V8*>(tqrow + 16 * kk);
+      for (int kk = 0; kk < KK; ++kk) tqf[kk] = qchunk(tqrow, kk);
     }
   }
 
@@ -270,7 +278,7 @@ void attn_fwd_kernel(const FwdParams p) {
   };
   auto issue = [&](St& st, int jb) -> int {
     const int kb = key_block(jb);
-    const int64_t off = (int64_t)kb * BN * D;
+    const int64_t off = (int64_t)kb * BN * G;
     const int nr = p.N - kb * BN;  // rows of this block that exist
     int n = kVLoads * St::NV;
     if constexpr (kPw) {
@@ -576,8 +584,8 @@ void attn_fwd_kernel(const FwdParams p) {
   static_assert(kWaves * RowStage<DV>::kStageBytes <= (int)sizeof(smem), "output staging fits in the ring");
   char* stage = reinterpret_cast<char*>(&smem[0]) + wave * RowStage<DV>::kStageBytes;
   const int nrows = RAGGED ? p.M - row0 : 32;
-  const int64_t orow = qbase + (int64_t)row0 * D + half * DV;
-  store_tile_rows<T, DV, D>((T*)p.o + orow, nrows, acc, inv, stage, lane);
+  const int64_t orow = qbase + (int64_t)row0 * G + half * DV;
+  store_tile_rows<T, DV, G>((T*)p.o + orow, nrows, acc, inv, stage, lane);
   float c = 0.f;
   if constexpr (kJvp) {
     const float mu = halves_sum(mu_i);
@@ -587,7 +595,7 @@ void attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) accg[dt][r] = accg[dt][r] - c * acc[dt][r];
     }
-    store_tile_rows<T, DV, D>((T*)p.to + orow, nrows, accg, inv, stage, lane);
+    store_tile_rows<T, DV, G>((T*)p.to + orow, nrows, accg, inv, stage, lane);
   }
   if (RAGGED && qi >= p.M) return;  // lanes past the last query row
   if (half != 0) return;            // (every share forms the same row statistics)
@@ -1038,7 +1046,7 @@ void attn_fwd_pipe_kernel(const FwdParams p) {
   if (h == 0) p.lse[(int64_t)bh * p.M + qi] = has ? (m_i + log2f(l)) * kLn2 : kNegInf;
 }
 
-template <typename T, int D, int VAR>
+template <typename T, int D, int VAR, int G = D>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
   FwdParams p;
   p.q = a.q;
@@ -1074,7 +1082,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
   dim3 grid(p.nmb * p.BH * FwdShape<VAR, D, true>::SPLIT),
       block(a.causal ? FwdShape<VAR, D, true>::NT : FwdShape<VAR, D, false>::NT);
   const bool ragged = a.M % 64 != 0 || a.N % 64 != 0;
-  if constexpr ((VAR == PLAIN && (D == 64 || D == 128)) || (VAR == PW && D == 64)) {
+  if constexpr (G == D && ((VAR == PLAIN && (D == 64 || D == 128)) || (VAR == PW && D == 64))) {
     static_assert(FwdShape<VAR, D, true>::NT == 64 * kPipeWaves && FwdShape<VAR, D, false>::NT == 64 * kPipeWaves,
                   "same launch shape");
     if (a.causal && ragged)
@@ -1087,23 +1095,23 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((attn_fwd_pipe_kernel<T, D, VAR, false, false>), grid, block, 0, s, p);
   } else {
     if (a.causal && ragged)
-      hipLaunchKernelGGL((attn_fwd_kernel<T, D, VAR, true, true>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((attn_fwd_kernel<T, D, VAR, true, true, G>), grid, block, 0, s, p);
     else if (a.causal)
-      hipLaunchKernelGGL((attn_fwd_kernel<T, D, VAR, true, false>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((attn_fwd_kernel<T, D, VAR, true, false, G>), grid, block, 0, s, p);
     else if (ragged)
-      hipLaunchKernelGGL((attn_fwd_kernel<T, D, VAR, false, true>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((attn_fwd_kernel<T, D, VAR, false, true, G>), grid, block, 0, s, p);
     else
-      hipLaunchKernelGGL((attn_fwd_kernel<T, D, VAR, false, false>), grid, block, 0, s, p);
+      hipLaunchKernelGGL((attn_fwd_kernel<T, D, VAR, false, false, G>), grid, block, 0, s, p);
   }
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, int G = D>
 hipError_t launch_var(const FwdArgs& a, hipStream_t s) {
   switch (a.variant) {
-    case PLAIN: return launch_t<T, D, PLAIN>(a, s);
-    case JVP: return launch_t<T, D, JVP>(a, s);
-    case PW: return launch_t<T, D, PW>(a, s);
+    case PLAIN: return launch_t<T, D, PLAIN, G>(a, s);
+    case JVP: return launch_t<T, D, JVP, G>(a, s);
+    case PW: return launch_t<T, D, PW, G>(a, s);
   }
   return hipErrorInvalidValue;
 }
@@ -1113,6 +1121,9 @@ hipError_t launch_d(const FwdArgs& a, hipStream_t s) {
   if (a.D == 64) return launch_var<T, 64>(a, s);
   if (a.D == 128) return launch_var<T, 128>(a, s);
   if (a.D == 32) return launch_var<T, 32>(a, s);
+  // D = 16: the D = 32 kernels over zero-padded tiles (a 16-wide row is one
+  // 32-byte piece, below the 16 x 32 operand of the products)
+  if (a.D == 16) return launch_var<T, 32, 16>(a, s);
   // D = 256: plain attention here, the JVP in its own translation units
   // (piecewise runs on the generic kernels)
   if (a.D == 256 && a.variant == PLAIN) return launch_t<T, 256, PLAIN>(a, s);

@@ -2,8 +2,8 @@
 // cores: every storage dtype, every head dim the pages allow.
 //
 // It serves fp32 inputs, which are computed in true fp32 arithmetic end to
-// end (no reduced-precision MFMA), and the 16-bit shapes the MFMA kernels do
-// not cover: head dim 16, and head dim 256 outside the plain forward.  The
+// end (no reduced-precision MFMA), and the one 16-bit shape the MFMA kernels
+// do not cover: piecewise attention at head dim 256.  The
 // computation is the same as the MFMA kernels' -- the Triton tutorial's
 // online-softmax forward and recompute backward, the JVP recurrences of its
 // ENABLE_JVP path, FlagAttention's piecewise score selection -- in fp32, with

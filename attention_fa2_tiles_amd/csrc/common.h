@@ -273,8 +273,10 @@ __device__ __forceinline__ constexpr int tile_row(int m, bool perm) { return per
 static __device__ __attribute__((aligned(16))) uint32_t kZero16[4] = {0u, 0u, 0u, 0u};
 static __device__ float kPosInfF = __builtin_huge_valf();
 
-// G: the row stride of the tensor the tile is loaded from, in elements (a
-// tile of D columns out of G-wide rows; normally G = D).
+// G: the row stride of the tensor the tile is loaded from, in elements.
+// Normally G = D; G > D: a tile of D columns out of wider rows; G < D: rows
+// of G elements zero-padded to the tile's D columns (chunks from column G on
+// are loaded from kZero16).
 template <typename T, int R, int D, int NW, bool PERM = true, int G = D>
 struct DTile {
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
@@ -282,17 +284,21 @@ struct DTile {
   static constexpr int INSTR = R / ROWS_PER_INSTR;  // wave instructions per tile
   static constexpr int PER_WAVE = INSTR / NW;
   static constexpr int ELEMS = R * D;
+  static constexpr int DATA_CHUNKS = (G < D ? G : D) / 8;  // chunks of a row that exist in memory
   static_assert(INSTR % NW == 0, "tile must split evenly over the waves");
+  static_assert(G % 8 == 0, "rows of whole 16-byte chunks");
 
   // Issue this wave's share of the direct loads of the R x D tile at g
-  // (row stride D elements) into lds.  Completion is tracked by vmcnt.
+  // (row stride G elements) into lds.  Completion is tracked by vmcnt.
   __device__ static __forceinline__ void load(T* lds, const T* g, int wave, int lane) {
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
       const int ins = wave * PER_WAVE + j;
       const int p = ins * 64 + lane;
       const int m = p / CPR, slot = p % CPR;
-      const T* src = g + tile_row(m, PERM) * G + ((slot ^ swz<D>(m)) * 8);
+      const int c = slot ^ swz<D>(m);
+      const T* src = (G >= D || c < DATA_CHUNKS) ? g + tile_row(m, PERM) * G + c * 8
+                                                 : reinterpret_cast<const T*>(kZero16);
       __builtin_amdgcn_global_load_lds(
           (const void __attribute__((address_space(1)))*)src,
           (void __attribute__((address_space(3)))*)(lds + ins * 512), 16, 0, 0);
@@ -310,7 +316,9 @@ struct DTile {
       const int p = ins * 64 + lane;
       const int m = p / CPR, slot = p % CPR;
       const int src = tile_row(m, PERM);
-      const T* src_ptr = src < nrows ? g + src * G + ((slot ^ swz<D>(m)) * 8) : reinterpret_cast<const T*>(kZero16);
+      const int c = slot ^ swz<D>(m);
+      const T* src_ptr = (src < nrows && (G >= D || c < DATA_CHUNKS)) ? g + src * G + c * 8
+                                                                      : reinterpret_cast<const T*>(kZero16);
       __builtin_amdgcn_global_load_lds(
           (const void __attribute__((address_space(1)))*)src_ptr,
           (void __attribute__((address_space(3)))*)(lds + ins * 512), 16, 0, 0);
@@ -332,6 +340,7 @@ struct DmaTile {
   using Tile = DTile<T, R, D, NW, PERM, G>;
   static constexpr int PER_WAVE = Tile::PER_WAVE;
   uint32_t voff[PER_WAVE];
+  uint32_t live = ~0u;  // G < D: bit j set when this lane's chunk of load j exists in memory
 
   __device__ __forceinline__ void lane_offsets(int wave, int lane) {
 #pragma unroll
@@ -339,16 +348,23 @@ struct DmaTile {
       const int ins = wave * PER_WAVE + j;
       const int p = ins * 64 + lane;
       const int m = p / Tile::CPR, slot = p % Tile::CPR;
-      voff[j] = (uint32_t)((tile_row(m, PERM) * G + ((slot ^ swz<D>(m)) * 8)) * 2);
+      const int c = slot ^ swz<D>(m);
+      voff[j] = (uint32_t)((tile_row(m, PERM) * G + c * 8) * 2);
+      if constexpr (G < D) {
+        if (c >= Tile::DATA_CHUNKS) live &= ~(1u << j);
+      }
     }
   }
-  // Load the tile whose first row is at g (row stride G) into lds.
+  // Load the tile whose first row is at g (row stride G) into lds (G < D:
+  // the padding chunks from kZero16).
   __device__ __forceinline__ void load(const T* g, T* lds, int wave) const {
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
       const int ins = wave * PER_WAVE + j;
+      const char* src = reinterpret_cast<const char*>(g) + voff[j];
+      if constexpr (G < D) src = ((live >> j) & 1u) ? src : reinterpret_cast<const char*>(kZero16);
       __builtin_amdgcn_global_load_lds(
-          (const void __attribute__((address_space(1)))*)(reinterpret_cast<const char*>(g) + voff[j]),
+          (const void __attribute__((address_space(1)))*)src,
           (void __attribute__((address_space(3)))*)(lds + ins * 512), 16, 0, 0);
     }
   }
@@ -547,7 +563,8 @@ __device__ __forceinline__ void store_acc_t(T* row_ptr, const f32x16& acc, int d
 // consecutive rows (64 / (D / 8) of them).
 //   lds: this wave's private region of kStageBytes (32 rows, pitch 2 D + 16
 //        bytes: the padding staggers the rows over the banks);
-//   g:   row 0 of the tile in global memory (row stride G, normally D);
+//   g:   row 0 of the tile in global memory (row stride G, normally D; G
+//        < D: only the first G columns are stored);
 //   s:   this lane's scale (its row's);
 //   nrows: rows of the tile that exist (rows from nrows on are not stored).
 // The caller makes sure no other wave uses the region.
@@ -560,6 +577,7 @@ struct RowStage {
 template <typename T, int D, int G = D>
 __device__ __forceinline__ void store_tile_rows(T* g, int nrows, const f32x16 (&acc)[D / 32], float s, char* lds,
                                                 int lane) {
+  static_assert(G % 8 == 0, "rows of whole 16-byte chunks");
   constexpr int PITCH = RowStage<D>::PITCH;
   constexpr int CPR = D / 8;        // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;     // rows per store instruction
@@ -583,7 +601,7 @@ __device__ __forceinline__ void store_tile_rows(T* g, int nrows, const f32x16 (&
   for (int i = 0; i < 32 / RPI; ++i) {
     const int row = RPI * i + lane / CPR, c = lane % CPR;
     const u32x4 v = *reinterpret_cast<const u32x4*>(lds + row * PITCH + 16 * c);
-    if (row < nrows) *reinterpret_cast<u32x4*>(g + (int64_t)row * G + 8 * c) = v;
+    if (row < nrows && (G >= D || 8 * c < G)) *reinterpret_cast<u32x4*>(g + (int64_t)row * G + 8 * c) = v;
   }
 }
 

@@ -119,10 +119,10 @@ hipError_t launch_attn_dq_generic(const BwdArgs& a, hipStream_t s);
 
 // Whether a shape runs on the generic kernels rather than the MFMA ones.
 inline bool fwd_generic(int dtype, int variant, int D) {
-  return dtype == 0 || D == 16 || (D == 256 && variant == PW);
+  return dtype == 0 || (D == 256 && variant == PW);
 }
 inline bool bwd_generic(int dtype, int variant, int D) {
-  return dtype == 0 || D == 16 || (D == 256 && variant != PLAIN);
+  return dtype == 0 || (D == 256 && variant != PLAIN);
 }
 
 // The no-allocation backward's Delta rows live in a device array of this

@@ -343,9 +343,9 @@ def bench_pw(torch, timer, iters):
 
 def bench_head_dims(torch, timer, iters):
     """The head dims at the ends of the supported range, causal bf16 B1 H16
-    M=N=2048: D = 256 (every call on the matrix cores; the backward passes
-    and the fused JVP run one wave per SIMD) and D = 16 (every call on the
-    generic kernels).  Same flop convention as the headline."""
+    M=N=2048: D = 256 (the backward passes and the fused JVP run one wave
+    per SIMD) and D = 16 (the D = 32 kernels over zero-padded rows), every
+    call on the matrix cores.  Same flop convention as the headline."""
     from attention_fa2_tiles_amd import lib
     from attention_fa2_tiles_amd.inputs import BF16, AttnWorkload
     from attention_fa2_tiles_amd.devbuf import empty, empty_f32
@@ -372,7 +372,7 @@ def bench_head_dims(torch, timer, iters):
             "fwd_ms": round(f_ms, 4), "fwd_TFLOP/s": round(tf(wl.fwd_flops(), f_ms), 2),
             "bwd_ms": round(b_ms, 4), "bwd_TFLOP/s": round(tf(wl.bwd_flops(), b_ms), 2),
             "jvp_ms": round(j_ms, 4), "jvp_TFLOP/s": round(tf(3 * wl.fwd_flops(), j_ms), 2),
-            "kernels": "MFMA" if D == 256 else "generic (vector ALU)",
+            "kernels": "MFMA" if D == 256 else "MFMA (D = 32 tiles over zero-padded rows)",
         }
         del d, b, calls, to
         torch.cuda.empty_cache()

@@ -40,10 +40,11 @@
  * - Supported attention shapes: B, H, M, N >= 1 (any lengths; the kernels
  *   mask the last partial tile); D in {16, 32, 64, 128, 256}, the head dims
  *   the tutorial's Function accepts, on every attention entry point and in
- *   every dtype (fa_fwd_fp8: D in {64, 128}).  16-bit D = 32, 64, 128 run
- *   on the matrix cores, as do the 16-bit forward, backward and fused JVP
- *   at D = 256; fp32, D = 16 and piecewise attention at D = 256 run a
- *   slower kernel without them.  Any other D gives FA_ERR_UNSUPPORTED.
+ *   every dtype (fa_fwd_fp8: D in {64, 128}).  16-bit D = 16, 32, 64, 128
+ *   run on the matrix cores (D = 16 as zero-padded D = 32 tiles), as do the
+ *   16-bit forward, backward and fused JVP at D = 256; fp32 and piecewise
+ *   attention at D = 256 run a slower kernel without them.  Any other D
+ *   gives FA_ERR_UNSUPPORTED.
  *
  * The seven entry points of the hot path (fa_fwd, fa_bwd, fa_fwd_jvp,
  * pw_fwd, pw_bwd, resmerge_fwd, resmerge_bwd) keep the pages' operations

@@ -123,10 +123,14 @@ SMALL = [
     (F32, 1, 2, 100, 77, 32, True),
     (F32, 1, 1, 64, 96, 256, True),
     (F32, 1, 1, 70, 50, 256, False),
-    # head dim 16 (every dtype, the generic kernels) and 16-bit 256
+    # head dim 16 (16-bit: the D = 32 kernels over zero-padded rows; fp32:
+    # the generic kernels) and 16-bit 256
     (BF16, 1, 2, 100, 130, 16, True),
     (F16, 2, 1, 64, 64, 16, False),
     (F32, 1, 2, 77, 50, 16, True),
+    (BF16, 2, 3, 512, 384, 16, True),     # several blocks, M > N: rows that see no key
+    (F16, 1, 2, 200, 1000, 16, False),    # M < N, ragged, partial key block first
+    (BF16, 1, 1, 1, 1, 16, True),         # a single score
     (BF16, 1, 2, 130, 100, 256, True),
     (F16, 1, 1, 64, 96, 256, False),
 ]

@@ -58,8 +58,10 @@ JVP_SMALL = [
     (F16, 1, 2, 150, 100, 32, True),      # head dims 32 and (fp32) 256
     (BF16, 2, 2, 128, 128, 32, False),
     (F32, 1, 1, 64, 80, 256, True),
-    (F16, 1, 2, 100, 120, 16, True),      # head dim 16: the generic kernels
+    (F16, 1, 2, 100, 120, 16, True),      # head dim 16: the D = 32 kernels over zero-padded rows
     (BF16, 1, 1, 64, 64, 16, False),
+    (BF16, 2, 2, 384, 256, 16, True),     # M > N, several workgroups
+    (F32, 1, 2, 70, 90, 16, False),       # fp32 head dim 16: the generic kernels
     (F16, 1, 2, 90, 70, 256, True),       # 16-bit 256: output columns split over two workgroups
     (BF16, 1, 1, 64, 96, 256, False),
     (BF16, 2, 2, 256, 256, 256, True),
@@ -222,9 +224,11 @@ PW_SMALL = [
     (F16, 1, 2, 200, 170, 32, True, 50),       # head dims 32 and (fp32) 256
     (BF16, 1, 2, 256, 256, 32, False, 100),
     (F32, 1, 1, 64, 96, 256, True, 20),
-    (F16, 1, 2, 100, 130, 16, True, 30),      # head dim 16 and 16-bit 256: the generic kernels
+    (F16, 1, 2, 100, 130, 16, True, 30),      # head dim 16: the D = 32 kernels over zero-padded rows
     (BF16, 1, 1, 96, 64, 16, False, 20),
-    (BF16, 1, 2, 90, 110, 256, True, 25),
+    (BF16, 1, 2, 512, 448, 16, True, 70),     # several workgroups, M > N
+    (F32, 1, 1, 80, 70, 16, True, 15),        # fp32 head dim 16: the generic kernels
+    (BF16, 1, 2, 90, 110, 256, True, 25),     # 16-bit 256: the generic kernels
     (F16, 1, 1, 64, 64, 256, False, 10),
 ]
 
