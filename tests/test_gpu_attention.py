@@ -255,9 +255,14 @@ def test_noncausal_bwd_sees_all_queries():
     assert np.abs(got["dk"][:, :, :64] - gotc["dk"][:, :, :64]).max() > 0.1
 
 
-def test_large_scale_peaky_softmax():
-    """sm_scale 1.0 at D = 128 makes rows nearly one-hot (large logits)."""
-    wl = AttnWorkload("peaky", BF16, 1, 2, 256, 256, 128, True, seed=9, sm_scale=1.0)
+@pytest.mark.parametrize("D", [128, 256, 16, 32])
+def test_large_scale_peaky_softmax(D):
+    """sm_scale 1.0 makes rows nearly one-hot (large logits, many lazy
+    rescales), on each head-dim path: the pipelined D = 128 forward, the
+    one-wave-per-SIMD D = 256 passes, the D = 32 kernels and D = 16 over
+    zero-padded rows."""
+    wl = AttnWorkload("peaky", BF16, 1, 2, 256, 256, D, True, seed=9, sm_scale=1.0)
+    log(f"peaky softmax D = {D}")
     t = attn_inputs(wl)
     compare(wl, t, run_fwd_bwd(wl, t))
 
