@@ -25,7 +25,8 @@ def _dense(wl, names=("q", "k", "v", "do")):
 
 
 @pytest.mark.parametrize("case", [(BF16, 1, 2, 256, 256, 128, True), (F16, 1, 2, 150, 77, 64, False),
-                                  (F32, 1, 2, 128, 128, 64, True)], ids=lambda c: "-".join(map(str, c)))
+                                  (F32, 1, 2, 128, 128, 64, True), (BF16, 1, 2, 200, 170, 256, True),
+                                  (F16, 1, 2, 130, 190, 16, False)], ids=lambda c: "-".join(map(str, c)))
 def test_attention_backward_both_outputs(case):
     torch = need_gpu()
     from attention_fa2_tiles_amd.autograd import attention
@@ -63,7 +64,8 @@ def test_attention_backward_lse_only():
     assert np.all(host(v.grad) == 0.0)
 
 
-JVP_CASES = [(F16, 1, 2, 192, 192, 64, True), (BF16, 1, 2, 150, 100, 128, False), (F32, 1, 2, 128, 192, 64, True)]
+JVP_CASES = [(F16, 1, 2, 192, 192, 64, True), (BF16, 1, 2, 150, 100, 128, False), (F32, 1, 2, 128, 192, 64, True),
+             (BF16, 1, 2, 160, 224, 256, True), (F16, 1, 2, 192, 96, 16, False)]
 
 
 @pytest.mark.parametrize("case", JVP_CASES, ids=lambda c: "-".join(map(str, c)))
