@@ -16,17 +16,20 @@
 // per side with the other side's pairs masked (dV collects P from both).
 //
 // Layout on CDNA4 (both passes stream tiles through a three-stage LDS ring
-// filled by direct global -> LDS loads, prefetching two blocks ahead):
-//  * dK/dV pass: 32 keys per wave, 8 waves (4 for piecewise at D = 128)
-//    per workgroup.
+// filled by direct global -> LDS loads, prefetching two blocks ahead; a
+// two-stage ring at D = 256, whose passes run one wave per SIMD with the
+// accumulators in AGPRs; head dim 16 runs the D = 32 kernels over rows
+// zero-padded to 32 columns, template parameter G = 16):
+//  * dK/dV pass: 32 keys per wave, 8 waves (4 for piecewise at D = 128 and
+//    for D = 32, 256) per workgroup.
 //    K stays in registers (B operand of S = Q K^t), each wave's 32 rows of V
 //    stay in LDS (B operand of dP = dO V^t).  Query blocks of Q, dO and their
 //    LSE / Delta rows stream through the ring.  Each lane owns one key, so P
 //    and dS leave the score products already laid out as the B operands of
 //    dV^t += dO^t P and dK^t += Q^t dS, whose A operands (dO^t, Q^t) are
 //    transposing LDS reads of the same row-major tiles.
-//  * dQ pass: 32 queries per wave, 8 waves (4 for piecewise at D = 128)
-//    per workgroup,
+//  * dQ pass: 32 queries per wave, 8 waves (4 for piecewise at D = 128 and
+//    for D = 32, 256) per workgroup,
 //    Q and dO resident in registers; 64-key blocks of K and V stream through
 //    the ring.  S^t = K Q^t and dP^t = V dO^t put one query per lane (LSE and
 //    Delta are per-lane scalars) and dQ^t += K^t dS^t reads K^t with

@@ -10,9 +10,12 @@
 // (q2, k2) by query-key distance (FlagAttention piecewise.py, _fwd_kernel).
 //
 // How it maps to CDNA4: 8 waves per workgroup (4 for the JVP variant at
-// D = 128 and for causal JVP at D = 64), 32 query rows per wave, K/V blocks of 64 keys streamed through a
-// three-stage LDS ring (two blocks prefetched) filled by direct global -> LDS
-// loads (no staging registers).  Scores are formed
+// D = 128, for causal JVP at D = 64, and for D = 32 and 256), 32 query rows
+// per wave, K/V blocks of 64 keys (32 for the D = 256 JVP, which splits the
+// output columns over two workgroups) streamed through a three-stage LDS
+// ring (two blocks prefetched) filled by direct global -> LDS loads (no
+// staging registers).  Head dim 16 runs the D = 32 kernels over rows
+// zero-padded to 32 columns (template parameter G = 16).  Scores are formed
 // transposed, S^t = K Q^t, so that each lane owns one query row: row max and
 // row sum are in-lane reductions plus one exchange with the other half-wave,
 // and the rescale of the output accumulator is lane-local because that
