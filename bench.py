@@ -675,7 +675,7 @@ def main():
             summarize_trace(args.summarize_trace)
         return
     if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(attention heads and merge rows would shard across GPUs with no exchange; "
               "see the design notes).", file=sys.stderr)
         sys.exit(2)
