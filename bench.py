@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense fp8 MFMA
 HEADLINE = "causal_bf16_b4h16_s2048_d128"
@@ -273,6 +274,29 @@ def bench_attention_other(torch, timer, name, iters):
     torch.cuda.empty_cache()
     return {"fwd_ms": round(f_ms, 4), "fwd_TFLOP/s": round(f_tf, 2), "fwd_frac_peak": round(f_tf / PEAK_BF16_TFLOPS, 4),
             "bwd_ms": round(b_ms, 4), "bwd_TFLOP/s": round(b_tf, 2), "bwd_frac_peak": round(b_tf / PEAK_BF16_TFLOPS, 4)}
+
+
+def bench_tiny_f32(torch, timer, iters):
+    """The tiny fp32 workload (B1 H2 128^2 D64, non-causal), reported without
+    a target: fp32 runs the generic vector-ALU kernels in true fp32, and at
+    8.4 MFLOP per forward the launch is latency-bound.  Rates are against
+    the fp32 vector peak."""
+    from attention_fa2_tiles_amd.inputs import WORKLOADS
+    wl = WORKLOADS["tiny_f32"]
+    progress("component tiny_f32")
+    _, d = attn_setup(torch, wl, ("q", "k", "v", "do"))
+    b = attn_buffers(torch, wl, d)
+    calls = attn_calls(wl, d, b)
+    calls["fwd"]()
+    f_ms = timer.avg_ms(calls["fwd"], iters)
+    b_ms = timer.avg_ms(calls["bwd"], iters)
+    f_tf = wl.fwd_flops() / (f_ms * 1e-3) / 1e12
+    b_tf = wl.bwd_flops() / (b_ms * 1e-3) / 1e12
+    del d, b
+    return {"workload": "fp32 B1 H2 M=N=128 D64 non-causal", "fwd_us": round(f_ms * 1e3, 2),
+            "fwd_TFLOP/s": round(f_tf, 4), "bwd_us": round(b_ms * 1e3, 2), "bwd_TFLOP/s": round(b_tf, 4),
+            "frac_fp32_vector_peak": [round(f_tf / PEAK_FP32_TFLOPS, 5), round(b_tf / PEAK_FP32_TFLOPS, 5)],
+            "kernels": "generic (vector ALU, fp32)"}
 
 
 def bench_jvp(torch, timer, name, iters):
@@ -707,6 +731,7 @@ def main():
         components["piecewise_f16_b2h16_s4096_d64_w1024"] = bench_pw(torch, timer, iters)
         components["fp8_causal_b4h16_s2048_d128"] = bench_fp8(torch, timer, iters)
         components["head_dims_causal_bf16_b1h16_s2048"] = bench_head_dims(torch, timer, iters)
+        components["tiny_f32_b1h2_s128_d64"] = bench_tiny_f32(torch, timer, iters)
         components["merge_bf16_rows32768_d4096"] = bench_merge(torch, timer, iters)
         components["lse_merge_bf16_s4_rows131072_d128"] = bench_lse_merge(torch, timer, iters)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds)
