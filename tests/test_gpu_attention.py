@@ -232,8 +232,22 @@ def test_dq_delta_equals_steps(case):
     assert np.array_equal(host(q1), host(q2)), "dq"
 
 
-def test_deterministic():
-    wl = AttnWorkload("det", F16, 1, 4, 256, 256, 64, False, seed=6)
+DET_CASES = [
+    # dtype, B, H, M, N, D, causal: one case per kernel family
+    (F16, 1, 4, 256, 256, 64, False),     # pipelined forward at D = 64
+    (BF16, 1, 4, 1024, 1024, 128, True),  # the pipelined causal D = 128 forward and its passes, several workgroups
+    (BF16, 1, 2, 576, 512, 256, True),    # head dim 256 (one wave per SIMD), M > N
+    (BF16, 1, 2, 333, 517, 16, False),    # head dim 16 (zero-padded D = 32 tiles), ragged
+    (F32, 1, 2, 200, 170, 64, True),      # the generic fp32 kernels
+]
+
+
+@pytest.mark.parametrize("case", DET_CASES, ids=lambda c: "-".join(map(str, c)))
+def test_deterministic(case):
+    """No float atomics anywhere: two runs on the same inputs give bitwise-equal outputs."""
+    dtype, B, H, M, N, D, causal = case
+    wl = AttnWorkload("det", dtype, B, H, M, N, D, causal, seed=6 + M + D)
+    log(f"determinism {case}")
     t = attn_inputs(wl)
     a = run_fwd_bwd(wl, t)
     b = run_fwd_bwd(wl, t)

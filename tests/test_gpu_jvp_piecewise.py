@@ -253,6 +253,29 @@ def test_pw_lse_gradient(case):
     compare_pw(wl, t, run_pw(wl, t, w, dlse=dev(g)), w, dlse=g.f64)
 
 
+@pytest.mark.parametrize("case", [(F16, 2, 2, 1024, 1024, 64, True), (BF16, 1, 2, 384, 320, 128, False),
+                                  (BF16, 1, 2, 256, 256, 256, True)], ids=lambda c: "-".join(map(str, c)))
+def test_jvp_deterministic(case):
+    """Two fused-JVP runs on the same inputs give bitwise-equal outputs."""
+    dtype, B, H, M, N, D, causal = case
+    wl = AttnWorkload("jvp_det", dtype, B, H, M, N, D, causal, seed=51 + M + D)
+    log(f"jvp determinism {case}")
+    t = attn_inputs(wl, JVP_NAMES)
+    a, b = run_jvp(wl, t), run_jvp(wl, t)
+    for n in a:
+        assert np.array_equal(a[n], b[n]), n
+
+
+def test_pw_deterministic():
+    """Two piecewise forward + backward runs give bitwise-equal outputs."""
+    wl = AttnWorkload("pw_det", F16, 1, 2, 640, 704, 64, True, seed=61)
+    log("pw determinism")
+    t = attn_inputs(wl, PW_NAMES)
+    a, b = run_pw(wl, t, 150), run_pw(wl, t, 150)
+    for n in a:
+        assert np.array_equal(a[n], b[n]), n
+
+
 _PW_FULL = {}
 
 
