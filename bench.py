@@ -279,7 +279,8 @@ def bench_attention_other(torch, timer, name, iters):
 def bench_tiny_f32(torch, timer, iters):
     """The tiny fp32 workload (B1 H2 128^2 D64, non-causal), reported without
     a target: fp32 runs the generic vector-ALU kernels in true fp32, and at
-    8.4 MFLOP per forward the launch is latency-bound.  Rates are against
+    8.4 MFLOP per forward the kernels are latency-bound (each of the 256
+    query rows is walked key by key by one lane group).  Rates are against
     the fp32 vector peak."""
     from attention_fa2_tiles_amd.inputs import WORKLOADS
     wl = WORKLOADS["tiny_f32"]
