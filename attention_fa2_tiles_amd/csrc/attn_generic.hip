@@ -35,11 +35,32 @@ constexpr int per_lane() {
 }
 constexpr int kChunk = 4;  // keys (or queries) per step
 
-// Sum over the RL lanes of this lane's group.
+// x of the lane that DPP control CTRL names (all rows and banks enabled).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the RL lanes of this lane's group, in every lane of the group,
+// without the LDS crossbar: the pair and quad partners inside each group of
+// four lanes (DPP quad permutations), the quads of a 16-lane row (rotations
+// of the row by 4 and 8 lanes), then the partner rows (16 lanes apart) and
+// halves (32 apart) by the register swaps across rows.
 template <int RL>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-  for (int off = RL / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  static_assert(RL == 16 || RL == 32 || RL == 64, "group of 16, 32 or 64 lanes");
+  x += dpp<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp<0x124>(x);  // row_ror:4
+  x += dpp<0x128>(x);  // row_ror:8
+  if constexpr (RL >= 32) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x), false, false);
+    x = __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+  }
+  if constexpr (RL >= 64) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x), false, false);
+    x = __builtin_bit_cast(float, (int)r[0]) + __builtin_bit_cast(float, (int)r[1]);
+  }
   return x;
 }
 // Maximum / minimum over the whole wavefront (a loop bound its groups share).
