@@ -494,10 +494,11 @@ def cpu_baseline(target_s):
 
 
 def profile_mode(torch):
-    """Launch each kernel of the headline step, the residual merge and the
-    N-way merge a few times, then copy 256 MiB device-to-device; rocprofv3
-    --pmc runs wrap this to count HBM bytes per dispatch, and the copy's
-    counter value per byte is the calibration."""
+    """Launch each kernel of the headline step, the residual merge, the N-way
+    merge and the other attention workloads a few times, then copy 256 MiB
+    device-to-device; rocprofv3 --pmc runs wrap this to count HBM bytes and
+    other counters per dispatch, and the copy's counter value per byte is
+    the calibration."""
     from attention_fa2_tiles_amd import lib
     from attention_fa2_tiles_amd.inputs import (LSE_MERGE_WORKLOAD, MERGE_WORKLOAD, WORKLOADS, lse_merge_inputs,
                                                 merge_inputs)
@@ -546,6 +547,7 @@ def profile_mode(torch):
     torch.cuda.synchronize()
     progress("profiled lse_merge bwd")
     del ys, lses, gy, gl, y, lse, gys, glses
+    profile_other_attention(torch)
     torch.cuda.empty_cache()
     # calibration: an elementwise copy (dst = -src) of COPY_BYTES, launched
     # over the whole device like the kernels above
@@ -559,6 +561,58 @@ def profile_mode(torch):
 
 COPY_BYTES = 256 << 20
 
+
+def profile_other_attention(torch):
+    """profile_mode's launches of the other attention workloads, for their
+    counters: the fused JVP (fp16 B4 H16 1024^2 D64, causal and not),
+    piecewise attention forward and backward (fp16 B2 H16 4096^2 D64,
+    w = 1024, causal) and the FP8 forward (causal B4 H16 2048^2 D128)."""
+    import numpy as np
+    from attention_fa2_tiles_amd import lib
+    from attention_fa2_tiles_amd.inputs import BF16, F8E5M2, PIECEWISE_W, WORKLOADS, AttnWorkload, attn_inputs
+    from attention_fa2_tiles_amd.devbuf import empty, empty_f32
+    names = ("q", "k", "v", "tq", "tk", "tv")
+    for name in ("jvp_f16_b4h16_s1024_d64_causal", "jvp_f16_b4h16_s1024_d64"):
+        wl = WORKLOADS[name]
+        _, d = attn_setup(torch, wl, names)
+        B, H, M, N, D = wl.B, wl.H, wl.M, wl.N, wl.D
+        o, to, lse = empty((B, H, M, D), wl.dtype), empty((B, H, M, D), wl.dtype), empty_f32((B, H, M))
+        for _ in range(3):
+            lib.fa_fwd_jvp(wl.dtype, *[d[n] for n in names], o, lse, to, B, H, M, N, D, wl.causal, wl.sm_scale)
+        torch.cuda.synchronize()
+        progress(f"profiled {name}")
+        del d, o, to, lse
+    wl = WORKLOADS["piecewise_f16_b2h16_s4096_d64_w1024"]
+    names = ("q1", "k1", "q2", "k2", "v", "do")
+    _, d = attn_setup(torch, wl, names)
+    B, H, M, N, D = wl.B, wl.H, wl.M, wl.N, wl.D
+    o, lse = empty((B, H, M, D), wl.dtype), empty_f32((B, H, M))
+    g = [empty((B, H, M, D), wl.dtype) for _ in range(5)]
+    nb = lib.pw_bwd_workspace_size(B, H, M, N, D, wl.dtype)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    args = (B, H, M, N, D, wl.causal, wl.sm_scale, PIECEWISE_W)
+    for _ in range(3):
+        lib.pw_fwd(wl.dtype, *[d[n] for n in names[:5]], o, lse, *args)
+    for _ in range(3):
+        lib.pw_bwd(wl.dtype, *[d[n] for n in names[:5]], o, d["do"], lse, *g, ws, nb, *args)
+    torch.cuda.synchronize()
+    progress(f"profiled {wl.name}")
+    del d, o, lse, g, ws
+    base = WORKLOADS[HEADLINE]
+    wl = AttnWorkload("fp8_causal_b4h16_s2048_d128", F8E5M2, base.B, base.H, base.M, base.N, base.D, True, base.seed)
+    t = attn_inputs(wl, ("q", "k", "v"))
+    q = torch.from_numpy(t["q"].storage).cuda()
+    k = torch.from_numpy(t["k"].storage).cuda()
+    vt = torch.from_numpy(np.ascontiguousarray(np.swapaxes(t["v"].storage, 2, 3))).cuda()
+    del t
+    B, H, M, N, D = wl.B, wl.H, wl.M, wl.N, wl.D
+    o, lse = empty((B, H, M, D), BF16), empty_f32((B, H, M))
+    for _ in range(3):
+        lib.fa_fwd_fp8(BF16, q, k, vt, o, lse, B, H, M, N, D, 1, 0.0)
+    torch.cuda.synchronize()
+    progress(f"profiled {wl.name}")
+    del q, k, vt, o, lse
+
 # kernel-name fragments (mangled) of the launches profile_mode makes
 PROFILED = {
     "fwd": ("causal_bf16_b4h16_s2048_d128", "attn_fwd_pipe_kernelIDF16bLi128ELi0ELb1ELb0"),
@@ -568,6 +622,13 @@ PROFILED = {
     "merge_bwd": ("merge_bf16_rows32768_d4096", "N_116merge_bwd_kernelIDF16b"),
     "lse_merge_fwd": ("lse_merge_bf16_s4_rows131072_d128", "lse_merge_fwd_small_kernelIDF16b"),
     "lse_merge_bwd": ("lse_merge_bf16_s4_rows131072_d128", "lse_merge_bwd_small_kernelIDF16b"),
+    # counters only (no traffic record)
+    "jvp_causal": (None, "attn_fwd_kernelIDF16_Li64ELi1ELb1ELb0"),
+    "jvp": (None, "attn_fwd_kernelIDF16_Li64ELi1ELb0ELb0"),
+    "pw_fwd": (None, "attn_fwd_pipe_kernelIDF16_Li64ELi2ELb1ELb0"),
+    "pw_dq": (None, "attn_dq_kernelIDF16_Li64ELi2ELb1ELb0"),
+    "pw_dkdv": (None, "attn_dkdv_kernelIDF16_Li64ELi2ELb1ELb0"),
+    "fp8_fwd": (None, "attn_fwd_fp8_kernelIDF16bLi128ELb1ELb0"),
     "copy": (None, "neg"),
 }
 XCDS, SIMDS = 8, 1024   # MI355X: GRBM_GUI_ACTIVE sums its 8 XCDs; 256 CUs x 4 SIMDs
