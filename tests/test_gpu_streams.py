@@ -1,0 +1,89 @@
+"""Every entry point launches on the stream it is given.
+
+The binding passes torch's current stream when no stream is named, so the
+calls below run on a side stream of their own.  That stream is first kept
+busy by a device-side sleep, then the outputs are filled with NaN on it, then
+the library is called: launched on that stream, its kernels run after the
+fill and leave the same results as a run on the default stream (the kernels
+are deterministic, so bitwise); launched on any other stream they would run
+during the sleep and the fill would leave NaN behind.  (PyTorch's side
+streams do not synchronise with the legacy default stream.)
+"""
+
+import numpy as np
+import pytest
+
+from attention_fa2_tiles_amd import lib
+from attention_fa2_tiles_amd.inputs import (BF16, F16, AttnWorkload, MergeWorkload, attn_inputs, lse_merge_inputs,
+                                            merge_inputs, LseMergeWorkload)
+from gpu_util import dev, empty_f32, filled, host, log, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+SLEEP_CYCLES = 40_000_000  # ~20 ms of one wave spinning at the shader clock
+
+
+def _calls(torch):
+    """(outputs, launch) per entry point: launch() enqueues the call on the
+    current stream and writes the outputs."""
+    out = []
+    wl = AttnWorkload("stream_attn", BF16, 1, 2, 384, 320, 128, True, seed=81)
+    t = attn_inputs(wl)
+    q, k, v, do = (dev(t[n]) for n in ("q", "k", "v", "do"))
+    B, H, M, N, D = wl.B, wl.H, wl.M, wl.N, wl.D
+    o, lse = filled((B, H, M, D), BF16), empty_f32((B, H, M))
+    dq, dk, dv = filled(q.shape, BF16), filled(k.shape, BF16), filled(v.shape, BF16)
+    nb = lib.fa_bwd_workspace_size(B, H, M, N, D, BF16)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+
+    def attn():
+        lib.fa_fwd(BF16, q, k, v, o, lse, B, H, M, N, D, 1, 0.0)
+        lib.fa_bwd(BF16, q, k, v, o, do, lse, dq, dk, dv, ws, nb, B, H, M, N, D, 1, 0.0)
+    out.append(("fa_fwd + fa_bwd", [o, lse, dq, dk, dv], attn))
+
+    wj = AttnWorkload("stream_jvp", F16, 1, 2, 256, 256, 64, True, seed=82)
+    names = ("q", "k", "v", "tq", "tk", "tv")
+    tj = attn_inputs(wj, names)
+    dj = [dev(tj[n]) for n in names]
+    jo, jto, jl = filled((1, 2, 256, 64), F16), filled((1, 2, 256, 64), F16), empty_f32((1, 2, 256))
+    out.append(("fa_fwd_jvp", [jo, jl, jto],
+                lambda: lib.fa_fwd_jvp(F16, *dj, jo, jl, jto, 1, 2, 256, 256, 64, 1, 0.0)))
+
+    mw = MergeWorkload("stream_merge", BF16, 96, 1024, 1e-6, 83)
+    tm = merge_inputs(mw)
+    x, y0, mq, l0 = (dev(tm[n]) for n in ("x", "y0", "q", "l0"))
+    y, mlse = filled((mw.rows, mw.D), BF16), empty_f32((mw.rows,))
+    out.append(("resmerge_fwd", [y, mlse],
+                lambda: lib.resmerge_fwd(BF16, x, mq, y0, l0, y, mlse, mw.rows, mw.D, mw.eps)))
+
+    lw = LseMergeWorkload("stream_lse_merge", BF16, 3, 200, 128, 84)
+    tl = lse_merge_inputs(lw)
+    ys, lses = dev(tl["ys"]), dev(tl["lses"])
+    ly, llse = filled((lw.rows, lw.D), BF16), empty_f32((lw.rows,))
+    out.append(("lse_merge_fwd", [ly, llse],
+                lambda: lib.lse_merge_fwd(BF16, ys, lses, ly, llse, lw.S, lw.rows, lw.D)))
+    return out
+
+
+def test_launches_follow_the_current_stream():
+    torch = need_gpu()
+    calls = _calls(torch)
+    # reference: every call on the default stream
+    for _, outs, launch in calls:
+        launch()
+    torch.cuda.synchronize()
+    ref = [[host(x).copy() for x in outs] for _, outs, _ in calls]
+    side = torch.cuda.Stream()
+    for (name, outs, launch), r in zip(calls, ref):
+        log(f"stream order: {name}")
+        torch.cuda.synchronize()
+        with torch.cuda.stream(side):
+            torch.cuda._sleep(SLEEP_CYCLES)
+            for x in outs:
+                x.fill_(float("nan"))
+            launch()
+        side.synchronize()
+        for i, (x, want) in enumerate(zip(outs, r)):
+            got = host(x)
+            assert np.all(np.isfinite(got) | ~np.isfinite(want)), f"{name} output {i}: NaN left by the fill"
+            assert np.array_equal(got, want, equal_nan=True), f"{name} output {i} differs from the default stream's"
