@@ -14,8 +14,8 @@ import numpy as np
 import pytest
 
 from attention_fa2_tiles_amd import lib
-from attention_fa2_tiles_amd.inputs import (BF16, F16, AttnWorkload, MergeWorkload, attn_inputs, lse_merge_inputs,
-                                            merge_inputs, LseMergeWorkload)
+from attention_fa2_tiles_amd.inputs import (BF16, F16, F8E5M2, AttnWorkload, LseMergeWorkload, MergeWorkload,
+                                            attn_inputs, lse_merge_inputs, merge_inputs)
 from gpu_util import dev, empty_f32, filled, host, log, need_gpu
 
 pytestmark = pytest.mark.gpu
@@ -40,6 +40,32 @@ def _calls(torch):
         lib.fa_fwd(BF16, q, k, v, o, lse, B, H, M, N, D, 1, 0.0)
         lib.fa_bwd(BF16, q, k, v, o, do, lse, dq, dk, dv, ws, nb, B, H, M, N, D, 1, 0.0)
     out.append(("fa_fwd + fa_bwd", [o, lse, dq, dk, dv], attn))
+
+    nq, nk, nv = filled(q.shape, BF16), filled(k.shape, BF16), filled(v.shape, BF16)
+    out.append(("fa_bwd_noalloc", [nq, nk, nv],
+                lambda: lib.fa_bwd_noalloc(BF16, q, k, v, o, do, lse, nq, nk, nv, B, H, M, N, D, 1, 0.0)))
+
+    wp = AttnWorkload("stream_pw", F16, 1, 2, 256, 256, 64, True, seed=85)
+    pn = ("q1", "k1", "q2", "k2", "v", "do")
+    tp = attn_inputs(wp, pn)
+    dp = [dev(tp[n]) for n in pn]
+    po, pl = filled((1, 2, 256, 64), F16), empty_f32((1, 2, 256))
+    pg = [filled((1, 2, 256, 64), F16) for _ in range(5)]
+    pnb = lib.pw_bwd_workspace_size(1, 2, 256, 256, 64, F16)
+    pws = torch.empty(pnb, dtype=torch.uint8, device="cuda")
+
+    def pw():
+        lib.pw_fwd(F16, *dp[:5], po, pl, 1, 2, 256, 256, 64, 1, 0.0, 40)
+        lib.pw_bwd(F16, *dp[:5], po, dp[5], pl, *pg, pws, pnb, 1, 2, 256, 256, 64, 1, 0.0, 40)
+    out.append(("pw_fwd + pw_bwd", [po, pl] + pg, pw))
+
+    wf = AttnWorkload("stream_fp8", F8E5M2, 1, 2, 256, 256, 128, True, seed=86)
+    tf = attn_inputs(wf, ("q", "k", "v"))
+    fq, fk = (torch.from_numpy(tf[n].storage).cuda() for n in ("q", "k"))
+    fvt = torch.from_numpy(np.ascontiguousarray(np.swapaxes(tf["v"].storage, 2, 3))).cuda()
+    fo, fl = filled((1, 2, 256, 128), BF16), empty_f32((1, 2, 256))
+    out.append(("fa_fwd_fp8", [fo, fl],
+                lambda: lib.fa_fwd_fp8(BF16, fq, fk, fvt, fo, fl, 1, 2, 256, 256, 128, 1, 0.0)))
 
     wj = AttnWorkload("stream_jvp", F16, 1, 2, 256, 256, 64, True, seed=82)
     names = ("q", "k", "v", "tq", "tk", "tv")
