@@ -23,11 +23,11 @@ pytestmark = pytest.mark.gpu
 SLEEP_CYCLES = 40_000_000  # ~20 ms of one wave spinning at the shader clock
 
 
-def _calls(torch):
+def _calls(torch, seed=0):
     """(outputs, launch) per entry point: launch() enqueues the call on the
     current stream and writes the outputs."""
     out = []
-    wl = AttnWorkload("stream_attn", BF16, 1, 2, 384, 320, 128, True, seed=81)
+    wl = AttnWorkload("stream_attn", BF16, 1, 2, 384, 320, 128, True, seed=81 + seed)
     t = attn_inputs(wl)
     q, k, v, do = (dev(t[n]) for n in ("q", "k", "v", "do"))
     B, H, M, N, D = wl.B, wl.H, wl.M, wl.N, wl.D
@@ -45,7 +45,7 @@ def _calls(torch):
     out.append(("fa_bwd_noalloc", [nq, nk, nv],
                 lambda: lib.fa_bwd_noalloc(BF16, q, k, v, o, do, lse, nq, nk, nv, B, H, M, N, D, 1, 0.0)))
 
-    wp = AttnWorkload("stream_pw", F16, 1, 2, 256, 256, 64, True, seed=85)
+    wp = AttnWorkload("stream_pw", F16, 1, 2, 256, 256, 64, True, seed=85 + seed)
     pn = ("q1", "k1", "q2", "k2", "v", "do")
     tp = attn_inputs(wp, pn)
     dp = [dev(tp[n]) for n in pn]
@@ -59,7 +59,7 @@ def _calls(torch):
         lib.pw_bwd(F16, *dp[:5], po, dp[5], pl, *pg, pws, pnb, 1, 2, 256, 256, 64, 1, 0.0, 40)
     out.append(("pw_fwd + pw_bwd", [po, pl] + pg, pw))
 
-    wf = AttnWorkload("stream_fp8", F8E5M2, 1, 2, 256, 256, 128, True, seed=86)
+    wf = AttnWorkload("stream_fp8", F8E5M2, 1, 2, 256, 256, 128, True, seed=86 + seed)
     tf = attn_inputs(wf, ("q", "k", "v"))
     fq, fk = (torch.from_numpy(tf[n].storage).cuda() for n in ("q", "k"))
     fvt = torch.from_numpy(np.ascontiguousarray(np.swapaxes(tf["v"].storage, 2, 3))).cuda()
@@ -67,7 +67,7 @@ def _calls(torch):
     out.append(("fa_fwd_fp8", [fo, fl],
                 lambda: lib.fa_fwd_fp8(BF16, fq, fk, fvt, fo, fl, 1, 2, 256, 256, 128, 1, 0.0)))
 
-    wj = AttnWorkload("stream_jvp", F16, 1, 2, 256, 256, 64, True, seed=82)
+    wj = AttnWorkload("stream_jvp", F16, 1, 2, 256, 256, 64, True, seed=82 + seed)
     names = ("q", "k", "v", "tq", "tk", "tv")
     tj = attn_inputs(wj, names)
     dj = [dev(tj[n]) for n in names]
@@ -75,14 +75,14 @@ def _calls(torch):
     out.append(("fa_fwd_jvp", [jo, jl, jto],
                 lambda: lib.fa_fwd_jvp(F16, *dj, jo, jl, jto, 1, 2, 256, 256, 64, 1, 0.0)))
 
-    mw = MergeWorkload("stream_merge", BF16, 96, 1024, 1e-6, 83)
+    mw = MergeWorkload("stream_merge", BF16, 96, 1024, 1e-6, 83 + seed)
     tm = merge_inputs(mw)
     x, y0, mq, l0 = (dev(tm[n]) for n in ("x", "y0", "q", "l0"))
     y, mlse = filled((mw.rows, mw.D), BF16), empty_f32((mw.rows,))
     out.append(("resmerge_fwd", [y, mlse],
                 lambda: lib.resmerge_fwd(BF16, x, mq, y0, l0, y, mlse, mw.rows, mw.D, mw.eps)))
 
-    lw = LseMergeWorkload("stream_lse_merge", BF16, 3, 200, 128, 84)
+    lw = LseMergeWorkload("stream_lse_merge", BF16, 3, 200, 128, 84 + seed)
     tl = lse_merge_inputs(lw)
     ys, lses = dev(tl["ys"]), dev(tl["lses"])
     ly, llse = filled((lw.rows, lw.D), BF16), empty_f32((lw.rows,))
@@ -113,3 +113,36 @@ def test_launches_follow_the_current_stream():
             got = host(x)
             assert np.all(np.isfinite(got) | ~np.isfinite(want)), f"{name} output {i}: NaN left by the fill"
             assert np.array_equal(got, want, equal_nan=True), f"{name} output {i} differs from the default stream's"
+
+
+def test_concurrent_streams_share_no_state():
+    """Two independent sets of calls (different inputs) interleaved on two
+    side streams run concurrently and each gives bitwise the results of a
+    run on its own: no entry point keeps device state between calls (the
+    no-allocation backward, whose static scratch concurrent calls share by
+    design, is left out)."""
+    torch = need_gpu()
+    sets = [[c for c in _calls(torch, seed) if c[0] != "fa_bwd_noalloc"] for seed in (0, 100)]
+    refs = []
+    for calls in sets:
+        for _, outs, launch in calls:
+            launch()
+        torch.cuda.synchronize()
+        refs.append([[host(x).copy() for x in outs] for _, outs, _ in calls])
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for calls, st in zip(sets, streams):
+        with torch.cuda.stream(st):
+            for _, outs, _ in calls:
+                for x in outs:
+                    x.fill_(float("nan"))
+    for i in range(len(sets[0])):
+        for calls, st in zip(sets, streams):
+            with torch.cuda.stream(st):
+                calls[i][2]()
+    torch.cuda.synchronize()
+    for k, (calls, ref) in enumerate(zip(sets, refs)):
+        for (name, outs, _), r in zip(calls, ref):
+            for j, (x, want) in enumerate(zip(outs, r)):
+                assert np.array_equal(host(x), want, equal_nan=True), f"set {k} {name} output {j}"
+        log(f"concurrent set {k} ok")
